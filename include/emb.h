@@ -1,0 +1,215 @@
+/*
+ * emb.h -- C ABI of the MI355X pooled-embedding library (libemb.so).
+ *
+ * The operations are those of the embedding layer of a deep learning
+ * recommendation model, as the NVIDIA Merlin / HugeCTR / EMBark pages state
+ * the problem:
+ *   - "Merlin HugeCTR: GPU-accelerated recommender system training and
+ *     inference" (GTC 2022 deck), slide "COMMON EMBEDDING PRIMITIVES":
+ *     table lookup, pooling/reduction of multi-hot features, concatenation;
+ *     slide "HUGECTR EMBEDDING LAYER": lookup and in-register reduction and
+ *     concatenation fused into one kernel;
+ *     slide "CHALLENGES OF EMBEDDING LAYER": these primitives are memory
+ *     bound, tables are sharded across GPUs (one GPU's share is what this
+ *     library holds);
+ *     slide "WEIGHT CONVERSION FOR MIXED PRECISION TRAINING": the optimizer
+ *     computes in FP32.
+ *   - NVIDIA Merlin blog, HugeCTR section: the features of one slot are
+ *     each turned into an embedding vector and reduced to a single vector.
+ *   - EMBark (RecSys'24 news article, section on embedding clusters):
+ *     reduction-based and unique-based compression of embedding traffic,
+ *     applied here locally as key dedup + per-key gradient reduction.
+ *
+ * Conventions for every call
+ *   - All tensors are caller-owned device memory (allocated e.g. by
+ *     PyTorch). The library never frees caller memory and never allocates
+ *     more than a small per-context descriptor block (lazily, on first use).
+ *   - Every call that takes `hip_stream` is asynchronous on that stream
+ *     (a hipStream_t passed as void*; NULL = the null stream) and performs
+ *     no host synchronisation, except emb_check_device_error and
+ *     emb_kernel_times.
+ *   - Return value: EMB_OK (0) or a negative EMB_E_* code; then
+ *     emb_last_error() returns a message (per thread). No C++ exception
+ *     crosses this interface. Argument validation happens before any HIP
+ *     call, so an invalid call has no effect on the device.
+ *   - Layouts:
+ *       table t, slice s: row-major [rows][dim/col_slices] of the storage
+ *         type; element (r, c) lives in slice c / (dim/col_slices).
+ *       indices: [N] int32 or int64 row ids, each in [0, rows_t).
+ *       offsets: [T*B + 1], same integer type as indices, table-major: bag
+ *         (t, b) is indices[offsets[t*B+b] .. offsets[t*B+b+1]);
+ *         offsets[0] = 0, non-decreasing, offsets[T*B] = N.
+ *       pooled output / upstream gradient: [B][T*dim] fp32, sample-major,
+ *         the T pooled vectors of a sample concatenated in table order.
+ *       global key of a lookup: row_offset[t] + idx, row_offset[t] being the
+ *         sum of rows of tables 0..t-1 (creation order).
+ */
+#ifndef EMB_H_
+#define EMB_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------- */
+#define EMB_OK            0
+#define EMB_E_INVAL      (-1)  /* bad argument: null pointer, size, layout */
+#define EMB_E_DTYPE      (-2)  /* unknown dtype / index type / pool / optimizer */
+#define EMB_E_WORKSPACE  (-3)  /* workspace smaller than emb_backward_workspace_bytes */
+#define EMB_E_HIP        (-4)  /* a HIP runtime call or launch failed */
+#define EMB_E_BOUNDS     (-5)  /* a kernel saw an index outside [0, rows) */
+#define EMB_E_STATE      (-6)  /* call order: update without a matching backward */
+
+/* ---- enums ------------------------------------------------------------ */
+#define EMB_F32   0   /* storage types */
+#define EMB_BF16  1
+#define EMB_F16   2
+
+#define EMB_I32   0   /* index / offset integer type */
+#define EMB_I64   1
+
+#define EMB_POOL_SUM   0
+#define EMB_POOL_MEAN  1
+
+#define EMB_OPT_SGD      0
+#define EMB_OPT_ADAGRAD  1
+
+#define EMB_MAX_SLICES 4
+
+/* One table of this GPU's share.
+ *   rows        >= 1
+ *   dim         >= 1; dim % col_slices == 0; the bytes of one slice row
+ *               (dim/col_slices * sizeof(storage)) must be a multiple of 16;
+ *               dim <= 256 (fp32) or 512 (bf16/fp16).
+ *   col_slices  1..EMB_MAX_SLICES; slices are a layout of one logical table
+ *               (one key stream, one dedup, one pooled output block of dim),
+ *               as a column-wise shard of a table is.
+ *   dtype       EMB_F32 | EMB_BF16 | EMB_F16 (the only stored copy).
+ *   weights[s]  device pointer of slice s, 16-byte aligned.
+ *   state[s]    device fp32 Adagrad accumulator of slice s (same shape as
+ *               the weight slice), or NULL for all s if Adagrad is not used.
+ * All tables of one context must share dim, col_slices and dtype. */
+typedef struct emb_table_desc {
+  int64_t rows;
+  int32_t dim;
+  int32_t col_slices;
+  int32_t dtype;
+  int32_t reserved;             /* must be 0 */
+  void*   weights[EMB_MAX_SLICES];
+  float*  state[EMB_MAX_SLICES];
+} emb_table_desc;
+
+typedef struct emb_ctx emb_ctx;
+
+/* Register T tables (this GPU's share). Copies the descriptors; computes
+ * row_offset. Fails with EMB_E_INVAL if T < 1, if the tables disagree in
+ * dim/col_slices/dtype, if the sum of rows is >= 2^32 - 1, or on any layout
+ * rule above; EMB_E_DTYPE on an unknown dtype. Touches no device state:
+ * the small device descriptor block is uploaded on the first launch. */
+int emb_create_tables(const emb_table_desc* descs, int32_t num_tables, emb_ctx** out);
+
+/* Frees the context and its descriptor block (synchronises the device
+ * if the block was uploaded). NULL is a no-op. */
+void emb_destroy_tables(emb_ctx* ctx);
+
+/* Sum of rows of tables 0..t-1 for t = 0..T (T+1 values) into row_offset. */
+int emb_row_offsets(const emb_ctx* ctx, int64_t* row_offset);
+
+/* Synthetic table contents (set-up, not part of a step): every element
+ * (t, r, c) becomes w = fp32(v) * fp32(0.1f * 2^-24) with
+ * v = (splitmix64(seed ^ (t << 40) ^ (r*dim + c)) >> 40) - 2^23, i.e.
+ * U(-0.05, 0.05), rounded to the storage type with round-to-nearest-even;
+ * Adagrad state (if present) is set to 0. SplitMix64 as published by
+ * Steele, Lea & Flood (OOPSLA 2014). */
+int emb_init_uniform(emb_ctx* ctx, uint64_t seed, void* hip_stream);
+
+/* Pooled forward: out[b][t*dim + c] = sum over bag (t, b) of
+ * W_t[idx][c] (EMB_POOL_SUM) or that sum / bag length (EMB_POOL_MEAN),
+ * accumulated in fp32 whatever the storage type; an empty bag gives 0.
+ * N = number of lookups (= offsets[T*B]), B = batch size (samples).
+ * A lookup whose index is outside [0, rows_t) contributes nothing and
+ * raises the context's device error flag (see emb_check_device_error). */
+int emb_forward_pooled(emb_ctx* ctx, const void* indices, const void* offsets,
+                       int32_t itype, int64_t N, int32_t B, int32_t pool,
+                       float* out, void* hip_stream);
+
+/* Bytes of workspace emb_backward_unique_reduce needs for N lookups and
+ * batch B (0 on invalid arguments). */
+size_t emb_backward_workspace_bytes(const emb_ctx* ctx, int64_t N, int32_t B);
+
+/* Backward, dedup part (EMBark's unique/reduction-based step, locally):
+ *   global keys g_i = row_offset[t(i)] + idx_i are sorted stably (device
+ *   LSD radix sort over (key, position) pairs) and run-length encoded:
+ *   unique_keys[u]  (capacity N) distinct keys, strictly ascending;
+ *   counts[u]       (capacity N) multiplicity of unique_keys[u];
+ *   inverse[i]      ([N]) index u of lookup i's key;
+ *   *num_unique     (device int32) U, the number of distinct keys.
+ *   Entries beyond U are left unspecified. If reduced_grad is not NULL
+ *   (capacity N x dim fp32), reduced_grad[u] = sum over lookups of key u
+ *   of scale_i * dY[b(i)][t(i)*dim ...], scale_i = 1 (sum) or 1/L (mean),
+ *   accumulated in fp32 in a fixed (deterministic) order.
+ * dY is [B][T*dim] fp32. ws (device, >= emb_backward_workspace_bytes)
+ * carries the sorted segments to emb_sparse_update; it, offsets and dY
+ * must stay valid and unchanged until that call. A lookup with an
+ * out-of-range index gets the key sum(rows) (which sorts last and is never
+ * applied by the update) and raises the device error flag.
+ * N must be < 2^31. */
+int emb_backward_unique_reduce(emb_ctx* ctx, const void* indices, const void* offsets,
+                               int32_t itype, int64_t N, int32_t B, int32_t pool,
+                               const float* dY, void* ws, size_t ws_bytes,
+                               uint32_t* unique_keys, int32_t* counts, int32_t* inverse,
+                               int32_t* num_unique, float* reduced_grad, void* hip_stream);
+
+/* Sparse optimizer step on the rows the last backward (with this ws) found,
+ * in place, each unique row read and written exactly once:
+ *   SGD:     w <- w - (lr*g)
+ *   Adagrad: G <- G + g*g;  w <- w - (lr*g) / (sqrt(G) + eps)
+ * in fp32 with each operation rounded separately in this order, then w
+ * rounded to the storage type with round-to-nearest-even. g is
+ * reduced_grad[u] if reduced_grad is not NULL (the buffer the backward
+ * filled), else it is reduced from dY inside the update kernel (fused
+ * path, no materialised gradient). Rows no lookup touched are not read or
+ * written. EMB_E_STATE if ws is not the workspace of this context's last
+ * backward; EMB_E_INVAL for Adagrad on tables without state. */
+int emb_sparse_update(emb_ctx* ctx, int32_t opt, float lr, float eps,
+                      const void* ws, const float* dY, const float* reduced_grad,
+                      void* hip_stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* emb_last_error(void);
+
+/* Synchronises hip_stream, then returns EMB_E_BOUNDS if any kernel of this
+ * context saw an out-of-range index since the last check (and clears the
+ * flag), else EMB_OK. */
+int emb_check_device_error(emb_ctx* ctx, void* hip_stream);
+
+/* ---- measurement ------------------------------------------------------ */
+/* Kernel families timed by emb_kernel_times (index into its outputs). */
+#define EMB_K_INIT          0
+#define EMB_K_FORWARD       1
+#define EMB_K_KEYS          2
+#define EMB_K_SORT_HIST     3
+#define EMB_K_SORT_SCAN     4
+#define EMB_K_SORT_SCATTER  5
+#define EMB_K_RLE           6
+#define EMB_K_REDUCE        7   /* segmented reduce (+ fused update) */
+#define EMB_K_COMBINE       8   /* long-segment combine (+ update) */
+#define EMB_K_APPLY         9   /* update from a materialised gradient */
+#define EMB_K_COUNT        10
+
+/* enable != 0: from now on every kernel launch of this context is
+ * bracketed by HIP events recorded on the launch stream. */
+int emb_set_kernel_timing(emb_ctx* ctx, int32_t enable);
+
+/* Waits for the recorded events, adds up the elapsed time (ms) and the
+ * number of launches per kernel family into ms[EMB_K_COUNT] and
+ * launches[EMB_K_COUNT], and forgets them. */
+int emb_kernel_times(emb_ctx* ctx, double* ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EMB_H_ */

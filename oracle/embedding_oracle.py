@@ -1,0 +1,285 @@
+"""Plain, slow, obviously-correct CPU oracle of the pooled-embedding path.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and ``bench.py``'s ``cpu_baseline`` leg, never by the product library. It
+shares no code, header, table or constant with the HIP path; the only thing
+both sides consume in common is the seeded input generator
+(``dlrm_sparse_embedding_amd.workloads``), which holds none of this arithmetic.
+
+What is computed, and where the pages define it
+-----------------------------------------------
+* Pooled forward -- "Merlin HugeCTR: GPU-accelerated recommender system
+  training and inference" (GTC 2022 deck), slide "COMMON EMBEDDING PRIMITIVES":
+  (1) table lookup, (2) pooling/reduction of a multi-hot feature, (3)
+  concatenation of the pooled vectors; NVIDIA Merlin blog, HugeCTR section:
+  the features of one slot are each mapped to a vector, then reduced to one
+  vector. Written out as: for every bag (table t, sample b), the sum (or mean)
+  of the stored rows W_t[idx] over the bag's CSR range, placed at
+  Y[b, t*D:(t+1)*D]. Accumulated in float64, rounded once to fp32.
+* Key dedup -- EMBark (RecSys'24 article, section on embedding clusters):
+  reduction-based and unique-based compression. Read here, applied to one
+  GPU's share, as: form the global key g = row_offset[t] + idx for every
+  lookup, and take the sorted distinct keys, their multiplicities and each
+  lookup's index into them (``np.unique``).
+* Gradient -- the plain definition: the dense scatter-add of every lookup's
+  upstream gradient (times 1/L for mean pooling) into its row, in float64,
+  rounded once to fp32. Unique-then-reduce reaches the same value up to fp32
+  summation order.
+* Optimizer -- GTC 2022 deck, slide "WEIGHT CONVERSION FOR MIXED PRECISION
+  TRAINING": the optimizer computes in FP32. SGD: w - lr*g. Adagrad
+  (element-wise, accumulator starts at 0): G' = G + g*g,
+  w' = w - (lr*g) / (sqrt(G') + eps). Every operation is a separately rounded
+  fp32 operation, in exactly that order. The result is rounded to the storage
+  type with round-to-nearest-even (bf16/fp16); the stored low-precision value
+  is the only copy of the weight.
+* Untouched rows -- a dense step with g = 0 and G = 0 leaves w and G bit for
+  bit unchanged, so only touched rows are computed.
+* Table contents -- synthetic: each element is a counter hash of (seed, table,
+  row*D + col) through SplitMix64 (Steele, Lea & Flood, "Fast splittable
+  pseudorandom number generators", OOPSLA 2014), mapped to U(-0.05, 0.05) by
+  one fp32 multiply, then rounded to the storage type.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "splitmix64", "init_values", "bf16_bits_rne", "bf16_bits_to_f32", "f16_rne",
+    "to_storage", "TouchedRows", "pooled_forward", "global_keys", "dedup",
+    "bag_of_positions", "reduced_grad", "sgd_step", "adagrad_step",
+    "update_rows",
+]
+
+_U64 = np.uint64
+_MASK64 = (1 << 64) - 1
+
+
+# ---------------------------------------------------------------------------
+# Synthetic table contents
+# ---------------------------------------------------------------------------
+
+def splitmix64(x: np.ndarray) -> np.ndarray:
+    """SplitMix64 output for counter value(s) ``x`` (uint64): add the golden
+    gamma 0x9E3779B97F4A7C15, then the variant-13 mix (xor-shift 30, multiply
+    0xBF58476D1CE4E5B9, xor-shift 27, multiply 0x94D049BB133111EB, xor-shift
+    31). Arithmetic wraps modulo 2^64."""
+    z = np.asarray(x, dtype=_U64)
+    with np.errstate(over="ignore"):
+        z = z + _U64(0x9E3779B97F4A7C15)
+        z = (z ^ (z >> _U64(30))) * _U64(0xBF58476D1CE4E5B9)
+        z = (z ^ (z >> _U64(27))) * _U64(0x94D049BB133111EB)
+        z = z ^ (z >> _U64(31))
+    return z
+
+
+_INIT_SCALE = np.float32(np.float32(0.1) * np.float32(2.0 ** -24))
+
+
+def init_values(seed: int, t: int, rows: np.ndarray, D: int, cols: np.ndarray | None = None) -> np.ndarray:
+    """fp32 initial value of elements (t, row, col), before storage rounding.
+
+    counter = seed XOR (t << 40) XOR (row*D + col); h = splitmix64(counter);
+    v = (h >> 40) - 2^23 (an integer in [-2^23, 2^23), exact in fp32);
+    w = fp32(v) * fp32(0.1 * 2^-24)  -- one rounded multiply, |w| <= 0.05.
+    Returns [len(rows), D] (or [len(rows), len(cols)])."""
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1, 1)
+    cc = np.arange(D, dtype=np.int64) if cols is None else np.asarray(cols, dtype=np.int64)
+    lin = (rows * D + cc.reshape(1, -1)).astype(_U64)
+    ctr = _U64(seed) ^ (_U64(t) << _U64(40)) ^ lin
+    h = splitmix64(ctr)
+    v = (h >> _U64(40)).astype(np.int64) - (1 << 23)
+    return v.astype(np.float32) * _INIT_SCALE
+
+
+# ---------------------------------------------------------------------------
+# Storage rounding (round to nearest, ties to even)
+# ---------------------------------------------------------------------------
+
+def bf16_bits_rne(x: np.ndarray) -> np.ndarray:
+    """bfloat16 bit pattern of fp32 ``x`` rounded to nearest-even. NaN stays
+    NaN (quiet); overflow rounds to +-inf as RNE dictates."""
+    b = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    nan = np.isnan(np.asarray(x, dtype=np.float32))
+    lsb = (b >> np.uint64(16)) & np.uint64(1)
+    r = ((b + np.uint64(0x7FFF) + lsb) >> np.uint64(16)) & np.uint64(0xFFFF)
+    r = np.where(nan, (b >> np.uint64(16)) | np.uint64(0x0040), r)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def f16_rne(x: np.ndarray) -> np.ndarray:
+    """IEEE binary16 of fp32 ``x``, round to nearest-even (numpy's cast)."""
+    with np.errstate(over="ignore"):
+        return np.asarray(x, dtype=np.float32).astype(np.float16)
+
+
+def to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Value actually stored for fp32 ``x`` in storage type ``dtype``,
+    returned widened to fp32 (exactly representable)."""
+    x = np.asarray(x, dtype=np.float32)
+    if dtype == "f32":
+        return x.copy()
+    if dtype == "bf16":
+        return bf16_bits_to_f32(bf16_bits_rne(x))
+    if dtype == "f16":
+        return f16_rne(x).astype(np.float32)
+    raise ValueError(dtype)
+
+
+class TouchedRows:
+    """Stored contents of table t restricted to the rows a batch touches, so
+    that a 53 GB table never has to exist on the host. Indexing with row ids
+    returns their stored values (fp32) -- the same values a full table holds."""
+
+    def __init__(self, seed: int, t: int, D: int, dtype: str, rows: np.ndarray):
+        self.rows = np.unique(np.asarray(rows, dtype=np.int64))
+        self.values = to_storage(init_values(seed, t, self.rows, D), dtype)
+        self.D = D
+
+    def __getitem__(self, r):
+        r = np.asarray(r, dtype=np.int64)
+        pos = np.searchsorted(self.rows, r)
+        if r.size and (np.any(pos >= self.rows.size) or np.any(self.rows[np.minimum(pos, self.rows.size - 1)] != r)):
+            raise KeyError("row not in the touched set")
+        return self.values[pos]
+
+
+# ---------------------------------------------------------------------------
+# Forward: lookup, pooling, concatenation
+# ---------------------------------------------------------------------------
+
+def bag_of_positions(offsets: np.ndarray, T: int, B: int) -> np.ndarray:
+    """Flat bag id t*B + b of every CSR position (table-major bags)."""
+    offsets = np.asarray(offsets, dtype=np.int64)
+    lengths = np.diff(offsets)
+    return np.repeat(np.arange(T * B, dtype=np.int64), lengths)
+
+
+def pooled_forward(tables, indices, offsets, T: int, B: int, D: int, pool: str) -> np.ndarray:
+    """Y[b, t*D:(t+1)*D] = sum (or mean) over bag (t, b) of W_t[idx].
+
+    ``tables[t][rows]`` must return the stored rows (any float type). Sums are
+    taken in float64 and rounded once to fp32; a mean divides the float64 sum
+    by the bag length before that rounding; an empty bag gives zeros."""
+    indices = np.asarray(indices, dtype=np.int64)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    blocks = []
+    for t in range(T):
+        p0, p1 = int(offsets[t * B]), int(offsets[(t + 1) * B])
+        lengths = np.diff(offsets[t * B:(t + 1) * B + 1])
+        local_bag = np.repeat(np.arange(B, dtype=np.int64), lengths)
+        s = np.zeros((B, D), dtype=np.float64)
+        if p1 > p0:
+            rows = np.asarray(tables[t][indices[p0:p1]], dtype=np.float64).reshape(p1 - p0, D)
+            np.add.at(s, local_bag, rows)
+        if pool == "mean":
+            nz = lengths > 0
+            s[nz] /= lengths[nz].astype(np.float64)[:, None]
+        elif pool != "sum":
+            raise ValueError(pool)
+        blocks.append(s)
+    if not blocks:
+        return np.zeros((B, 0), dtype=np.float32)
+    return np.concatenate(blocks, axis=1).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Backward: global keys, dedup, reduced gradient
+# ---------------------------------------------------------------------------
+
+def global_keys(indices, offsets, row_offset, T: int, B: int) -> np.ndarray:
+    """g_i = row_offset[t(i)] + idx_i for every CSR position i (int64)."""
+    indices = np.asarray(indices, dtype=np.int64)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    row_offset = np.asarray(row_offset, dtype=np.int64)
+    t_of_pos = bag_of_positions(offsets, T, B) // B if B else np.zeros(0, np.int64)
+    return row_offset[t_of_pos] + indices
+
+
+def dedup(g: np.ndarray):
+    """(unique_keys ascending, counts, inverse) of the global keys."""
+    u, inv, cnt = np.unique(np.asarray(g, dtype=np.int64), return_inverse=True, return_counts=True)
+    return u, cnt.astype(np.int64), inv.reshape(-1).astype(np.int64)
+
+
+def reduced_grad(dY, offsets, T: int, B: int, D: int, pool: str, inverse, U: int,
+                 select: np.ndarray | None = None) -> np.ndarray:
+    """gU[u] = sum over lookups i with inverse[i] == u of scale_i * dY[b(i), t(i)*D:(t(i)+1)*D],
+    scale_i = 1 (sum) or 1/L(bag) (mean). float64 scatter-add, one fp32 rounding.
+
+    ``select`` (sorted unique ids) restricts the result to those rows, in that
+    order, for workloads too large to reduce whole."""
+    dY = np.asarray(dY, dtype=np.float32)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    inverse = np.asarray(inverse, dtype=np.int64)
+    lengths = np.diff(offsets)
+    if select is None:
+        out = np.zeros((U, D), dtype=np.float64)
+        target_of = None
+    else:
+        select = np.asarray(select, dtype=np.int64)
+        out = np.zeros((select.size, D), dtype=np.float64)
+        target_of = select
+    for t in range(T):
+        p0, p1 = int(offsets[t * B]), int(offsets[(t + 1) * B])
+        if p1 == p0:
+            continue
+        lb = np.repeat(np.arange(B, dtype=np.int64), lengths[t * B:(t + 1) * B])
+        inv = inverse[p0:p1]
+        if target_of is not None:
+            pos = np.searchsorted(target_of, inv)
+            keep = (pos < target_of.size) & (target_of[np.minimum(pos, target_of.size - 1)] == inv)
+            lb, dst = lb[keep], pos[keep]
+        else:
+            dst = inv
+        if dst.size == 0:
+            continue
+        contrib = dY[lb, t * D:(t + 1) * D].astype(np.float64)
+        if pool == "mean":
+            contrib /= lengths[t * B + lb].astype(np.float64)[:, None]
+        np.add.at(out, dst, contrib)
+    return out.astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Optimizer (fp32, each operation separately rounded, in this order)
+# ---------------------------------------------------------------------------
+
+def sgd_step(w: np.ndarray, g: np.ndarray, lr: float) -> np.ndarray:
+    """w' = w - (lr * g)."""
+    w = np.asarray(w, dtype=np.float32)
+    g = np.asarray(g, dtype=np.float32)
+    step = np.float32(lr) * g
+    return (w - step).astype(np.float32)
+
+
+def adagrad_step(w: np.ndarray, G: np.ndarray, g: np.ndarray, lr: float, eps: float):
+    """G' = G + g*g;  w' = w - (lr*g) / (sqrt(G') + eps)."""
+    w = np.asarray(w, dtype=np.float32)
+    G = np.asarray(G, dtype=np.float32)
+    g = np.asarray(g, dtype=np.float32)
+    gg = g * g
+    G1 = (G + gg).astype(np.float32)
+    den = (np.sqrt(G1) + np.float32(eps)).astype(np.float32)
+    num = np.float32(lr) * g
+    w1 = (w - (num / den).astype(np.float32)).astype(np.float32)
+    return w1, G1
+
+
+def update_rows(w_stored: np.ndarray, G: np.ndarray | None, g: np.ndarray, opt: str,
+                lr: float, eps: float, dtype: str):
+    """One optimizer step on touched rows: widen the stored value, update in
+    fp32, round back to the storage type (RNE). Returns (w_stored', G')."""
+    w32 = np.asarray(w_stored, dtype=np.float32)
+    if opt == "sgd":
+        w1, G1 = sgd_step(w32, g, lr), G
+    elif opt == "adagrad":
+        if G is None:
+            raise ValueError("adagrad needs its accumulator")
+        w1, G1 = adagrad_step(w32, G, g, lr, eps)
+    else:
+        raise ValueError(opt)
+    return to_storage(w1, dtype), G1

@@ -1,0 +1,476 @@
+"""Pins of the CPU oracle to things other than itself (no GPU).
+
+Each oracle function is checked against an independent route to the same
+value: a published test vector, an independent library (torch CPU
+embedding_bag / autograd / torch.optim, numpy), brute force on tiny inputs,
+closed forms, invariants. The ``*_catches_*`` tests plant a plausible mistake
+in a copy of the oracle and check that the pin fails, so the pins are known to
+be sensitive.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from dlrm_sparse_embedding_amd import workloads as W
+
+
+def _f32_scaled_close(a, b, scale, ulps=2):
+    """|a - b| <= ulps * ulp(scale): for results of a - c computed with and
+    without a fused multiply-add, the error scale is max(|a|, |c|), not |result|."""
+    sp = np.spacing(np.abs(np.asarray(scale, np.float32))).astype(np.float64)
+    return np.all(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64)) <= ulps * sp)
+
+
+def _f32_ulp_close(a, b, ulps=1):
+    a = np.asarray(a, np.float32)
+    b = np.asarray(b, np.float32)
+    sp = np.spacing(np.maximum(np.abs(a), np.abs(b)).astype(np.float32))
+    return np.all(np.abs(a.astype(np.float64) - b.astype(np.float64)) <= ulps * sp.astype(np.float64))
+
+
+# ---------------------------------------------------------------------------
+# SplitMix64 + init mapping
+# ---------------------------------------------------------------------------
+
+def _read_golden_splitmix(golden_dir):
+    vals = []
+    seed = None
+    for line in open(os.path.join(golden_dir, "splitmix64_seed1234567.txt")):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        if line.startswith("seed"):
+            seed = int(line.split()[1])
+        else:
+            vals.append(int(line))
+    return seed, vals
+
+
+def test_splitmix64_published_vector(golden_dir):
+    seed, expect = _read_golden_splitmix(golden_dir)
+    gamma = 0x9E3779B97F4A7C15
+    ctr = np.array([(seed + i * gamma) % (1 << 64) for i in range(len(expect))], dtype=np.uint64)
+    got = [int(v) for v in O.splitmix64(ctr)]
+    assert got == expect
+
+
+def test_init_values_quantised_uniform():
+    rows = np.arange(0, 20000, 7)
+    w = O.init_values(3, 5, rows, 128)
+    assert w.dtype == np.float32 and w.shape == (rows.size, 128)
+    scale = np.float32(np.float32(0.1) * np.float32(2.0 ** -24))
+    # every value is one rounded fp32 product fp32(v) * scale of an integer v
+    # in [-2^23, 2^23) (the product rounds, so recover v by rounding)
+    v = np.round(w.astype(np.float64) / float(scale))
+    assert np.array_equal(v.astype(np.float32) * scale, w)
+    assert v.min() >= -(1 << 23) and v.max() < (1 << 23)
+    assert np.all(np.abs(w) <= 0.05)
+    # U(-0.05, 0.05): mean 0, sd 0.1/sqrt(12)
+    assert abs(w.mean()) < 5e-4
+    assert abs(w.std() - 0.1 / np.sqrt(12)) < 5e-4
+    # different tables / seeds / columns give different streams
+    assert not np.array_equal(w, O.init_values(3, 6, rows, 128))
+    assert not np.array_equal(w, O.init_values(4, 5, rows, 128))
+    assert not np.array_equal(w[:, 0], w[:, 1])
+
+
+def test_init_values_counter_layout():
+    # element (t, r, c) depends on r*D + c only through the counter: a 64-wide
+    # table's row 1 column 0 is the 128-wide table's row 0 column 64.
+    a = O.init_values(9, 2, np.array([1]), 64)
+    b = O.init_values(9, 2, np.array([0]), 128)
+    assert np.array_equal(a[0, :], b[0, 64:])
+    # column subsets agree with full rows
+    c = O.init_values(9, 2, np.array([5, 3]), 128, cols=np.array([7, 100]))
+    full = O.init_values(9, 2, np.array([5, 3]), 128)
+    assert np.array_equal(c, full[:, [7, 100]])
+
+
+# ---------------------------------------------------------------------------
+# Storage rounding
+# ---------------------------------------------------------------------------
+
+def _golden_ties(golden_dir):
+    out = []
+    for line in open(os.path.join(golden_dir, "rne_ties.txt")):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        kind, xin, xout = line.split()[:3]
+        out.append((kind, int(xin, 16), int(xout, 16)))
+    return out
+
+
+def test_rne_golden_ties(golden_dir):
+    for kind, xin, xout in _golden_ties(golden_dir):
+        x = np.array([xin], dtype=np.uint32).view(np.float32)
+        if kind == "bf16":
+            assert int(O.bf16_bits_rne(x)[0]) == xout, hex(xin)
+        else:
+            assert int(O.f16_rne(x).view(np.uint16)[0]) == xout, hex(xin)
+
+
+def test_rne_vs_torch_random():
+    rng = np.random.default_rng(0)
+    bits = rng.integers(0, 1 << 32, 200000, dtype=np.uint64).astype(np.uint32)
+    x = bits.view(np.float32)
+    x = x[np.isfinite(x)]
+    got_bf = O.bf16_bits_rne(x)
+    ref_bf = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got_bf, ref_bf)
+    # fp16 on the magnitudes that matter (incl. subnormal and overflow range)
+    y = (rng.standard_normal(200000) * np.exp(rng.uniform(-20, 12, 200000))).astype(np.float32)
+    got_h = O.f16_rne(y).view(np.uint16)
+    ref_h = torch.from_numpy(y).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got_h, ref_h)
+
+
+def test_bf16_nan_stays_nan():
+    x = np.array([np.nan, -np.nan], dtype=np.float32)
+    assert np.all(np.isnan(O.bf16_bits_to_f32(O.bf16_bits_rne(x))))
+
+
+def test_to_storage_idempotent():
+    x = O.init_values(1, 0, np.arange(100), 32).ravel()
+    for dt in ("f32", "bf16", "f16"):
+        s = O.to_storage(x, dt)
+        assert np.array_equal(O.to_storage(s, dt), s)
+
+
+# ---------------------------------------------------------------------------
+# Forward
+# ---------------------------------------------------------------------------
+
+def _small_case(seed=0, T=3, B=7, rows=(11, 5, 23), D=8, max_len=5, empty_every=3):
+    rng = np.random.default_rng(seed)
+    tables = [rng.standard_normal((rows[t], D)).astype(np.float32) for t in range(T)]
+    lens, keys = [], []
+    for t in range(T):
+        L = rng.integers(0, max_len + 1, B)
+        L[::empty_every] = 0
+        lens.append(L)
+        keys.append(rng.integers(0, rows[t], int(L.sum())))
+    batch = W.make_batch_from_lengths(lens, keys, B, index_dtype=np.int64)
+    return tables, batch, D
+
+
+def _torch_forward(tables, batch, D, pool):
+    T, B = batch.T, batch.B
+    out = []
+    for t in range(T):
+        o0 = int(batch.offsets[t * B])
+        off = torch.from_numpy((batch.offsets[t * B:(t + 1) * B] - o0).astype(np.int64))
+        idx = torch.from_numpy(batch.indices[o0:int(batch.offsets[(t + 1) * B])].astype(np.int64))
+        wt = torch.from_numpy(tables[t].astype(np.float64))
+        out.append(torch.nn.functional.embedding_bag(idx, wt, off, mode=pool))
+    return torch.cat(out, dim=1).numpy()
+
+
+def _forward_pin_ok(fwd, tables, batch, D, pool):
+    got = fwd(tables, batch.indices, batch.offsets, batch.T, batch.B, D, pool)
+    ref = _torch_forward(tables, batch, D, pool).astype(np.float32)
+    return got.shape == ref.shape and _f32_ulp_close(got, ref, 1)
+
+
+@pytest.mark.parametrize("pool", ["sum", "mean"])
+def test_forward_vs_torch_embedding_bag(pool):
+    for seed in range(4):
+        tables, batch, D = _small_case(seed)
+        assert _forward_pin_ok(O.pooled_forward, tables, batch, D, pool)
+
+
+def test_forward_bruteforce_loops():
+    tables, batch, D = _small_case(7, T=2, B=5, rows=(6, 9), D=4)
+    got = O.pooled_forward(tables, batch.indices, batch.offsets, batch.T, batch.B, D, "mean")
+    for t in range(batch.T):
+        for b in range(batch.B):
+            lo, hi = int(batch.offsets[t * batch.B + b]), int(batch.offsets[t * batch.B + b + 1])
+            acc = [0.0] * D
+            for i in range(lo, hi):
+                for c in range(D):
+                    acc[c] += float(tables[t][batch.indices[i], c])
+            for c in range(D):
+                v = acc[c] / (hi - lo) if hi > lo else 0.0
+                assert got[b, t * D + c] == np.float32(v)
+
+
+def test_forward_onehot_is_row_copy():
+    cfg = W.make_config(2, batch=300, num_tables=5)
+    batch = W.make_batch(cfg)
+    tabs = [O.TouchedRows(cfg.init_seed, t, cfg.dim, "f32", batch.indices[t * cfg.batch:(t + 1) * cfg.batch])
+            for t in range(cfg.T)]
+    Y = O.pooled_forward(tabs, batch.indices, batch.offsets, cfg.T, cfg.batch, cfg.dim, "sum")
+    for t in range(cfg.T):
+        rows = batch.indices[t * cfg.batch:(t + 1) * cfg.batch]
+        assert np.array_equal(Y[:, t * cfg.dim:(t + 1) * cfg.dim], O.init_values(cfg.init_seed, t, rows, cfg.dim))
+
+
+def test_forward_empty_bags_zero():
+    tables, batch, D = _small_case(3, empty_every=1)   # every bag empty
+    for pool in ("sum", "mean"):
+        Y = O.pooled_forward(tables, batch.indices, batch.offsets, batch.T, batch.B, D, pool)
+        assert np.all(Y == 0)
+
+
+def test_forward_pin_catches_mistakes():
+    tables, batch, D = _small_case(1)
+
+    def swapped_concat(tabs, idx, off, T, B, D_, pool):      # sample/table order transposed
+        Y = O.pooled_forward(tabs, idx, off, T, B, D_, pool)
+        return Y.reshape(B, T, D_)[:, ::-1, :].reshape(B, T * D_).copy()
+
+    def dropped_last(tabs, idx, off, T, B, D_, pool):          # last lookup of each bag dropped
+        off2 = np.asarray(off).copy()
+        keep = np.ones(len(idx), bool)
+        ends = off2[1:][np.diff(off2) > 0] - 1
+        keep[ends] = False
+        lens = np.diff(off2) - (np.diff(off2) > 0)
+        off3 = np.concatenate([[0], np.cumsum(lens)])
+        return O.pooled_forward(tabs, np.asarray(idx)[keep], off3, T, B, D_, pool)
+
+    def sum_for_mean(tabs, idx, off, T, B, D_, pool):
+        return O.pooled_forward(tabs, idx, off, T, B, D_, "sum")
+
+    assert not _forward_pin_ok(swapped_concat, tables, batch, D, "sum")
+    assert not _forward_pin_ok(dropped_last, tables, batch, D, "sum")
+    assert not _forward_pin_ok(sum_for_mean, tables, batch, D, "mean")
+
+
+# ---------------------------------------------------------------------------
+# Keys and dedup
+# ---------------------------------------------------------------------------
+
+def test_global_keys_bruteforce():
+    tables, batch, D = _small_case(2)
+    ro = np.concatenate([[0], np.cumsum([t.shape[0] for t in tables])])
+    g = O.global_keys(batch.indices, batch.offsets, ro, batch.T, batch.B)
+    exp = []
+    for t in range(batch.T):
+        for b in range(batch.B):
+            for i in range(int(batch.offsets[t * batch.B + b]), int(batch.offsets[t * batch.B + b + 1])):
+                exp.append(int(ro[t]) + int(batch.indices[i]))
+    assert g.tolist() == exp
+
+
+def _dedup_pin_ok(dedup, g):
+    u, c, inv = dedup(g)
+    # brute force with a dict
+    cnt = {}
+    for k in g.tolist():
+        cnt[k] = cnt.get(k, 0) + 1
+    keys = sorted(cnt)
+    return (u.tolist() == keys and c.tolist() == [cnt[k] for k in keys]
+            and [keys[j] for j in inv.tolist()] == g.tolist())
+
+
+def test_dedup_bruteforce_and_invariants():
+    rng = np.random.default_rng(5)
+    for n in (0, 1, 2, 50, 1000):
+        g = rng.integers(0, 40, n)
+        assert _dedup_pin_ok(O.dedup, g)
+        u, c, inv = O.dedup(g)
+        assert np.all(np.diff(u) > 0)
+        assert int(c.sum()) == n
+        assert np.array_equal(u[inv], g)
+    u, c, inv = O.dedup(np.full(777, 12345))
+    assert u.tolist() == [12345] and c.tolist() == [777] and np.all(inv == 0)
+
+
+def test_dedup_pin_catches_mistakes():
+    g = np.random.default_rng(6).integers(0, 30, 200)
+
+    def unsorted_unique(x):
+        u, c, inv = O.dedup(x)
+        return u[::-1], c[::-1], (len(u) - 1 - inv)
+
+    def off_by_one_counts(x):
+        u, c, inv = O.dedup(x)
+        return u, c + 1, inv
+
+    assert not _dedup_pin_ok(unsorted_unique, g)
+    assert not _dedup_pin_ok(off_by_one_counts, g)
+
+
+# ---------------------------------------------------------------------------
+# Gradient: unique-reduced == dense autograd of the pooled forward
+# ---------------------------------------------------------------------------
+
+def _autograd_dense(tables, batch, D, pool, dY):
+    T, B = batch.T, batch.B
+    ws = [torch.tensor(t.astype(np.float64), requires_grad=True) for t in tables]
+    outs = []
+    for t in range(T):
+        o0 = int(batch.offsets[t * B])
+        off = torch.from_numpy((batch.offsets[t * B:(t + 1) * B] - o0).astype(np.int64))
+        idx = torch.from_numpy(batch.indices[o0:int(batch.offsets[(t + 1) * B])].astype(np.int64))
+        outs.append(torch.nn.functional.embedding_bag(idx, ws[t], off, mode=pool))
+    Y = torch.cat(outs, dim=1)
+    (Y * torch.from_numpy(dY.astype(np.float64))).sum().backward()
+    return [w.grad.numpy() for w in ws]
+
+
+def _grad_pin_ok(red, tables, batch, D, pool, dY):
+    ro = np.concatenate([[0], np.cumsum([t.shape[0] for t in tables])])
+    g = O.global_keys(batch.indices, batch.offsets, ro, batch.T, batch.B)
+    u, c, inv = O.dedup(g)
+    gU = red(dY, batch.offsets, batch.T, batch.B, D, pool, inv, len(u))
+    dense = _autograd_dense(tables, batch, D, pool, dY)
+    ok = True
+    touched = set(u.tolist())
+    for t in range(batch.T):
+        for r in range(tables[t].shape[0]):
+            key = int(ro[t]) + r
+            ref = dense[t][r].astype(np.float32)
+            if key in touched:
+                ok &= bool(_f32_ulp_close(gU[int(np.searchsorted(u, key))], ref, 1))
+            else:
+                ok &= bool(np.all(dense[t][r] == 0))
+    return ok
+
+
+@pytest.mark.parametrize("pool", ["sum", "mean"])
+def test_reduced_grad_vs_autograd(pool):
+    for seed in range(3):
+        tables, batch, D = _small_case(seed + 10)
+        dY = np.random.default_rng(seed).standard_normal((batch.B, batch.T * D)).astype(np.float32)
+        assert _grad_pin_ok(O.reduced_grad, tables, batch, D, pool, dY)
+
+
+def test_reduced_grad_select_subset():
+    tables, batch, D = _small_case(4)
+    dY = np.random.default_rng(1).standard_normal((batch.B, batch.T * D)).astype(np.float32)
+    ro = np.concatenate([[0], np.cumsum([t.shape[0] for t in tables])])
+    u, c, inv = O.dedup(O.global_keys(batch.indices, batch.offsets, ro, batch.T, batch.B))
+    full = O.reduced_grad(dY, batch.offsets, batch.T, batch.B, D, "mean", inv, len(u))
+    sel = np.array([0, 3, len(u) - 1])
+    part = O.reduced_grad(dY, batch.offsets, batch.T, batch.B, D, "mean", inv, len(u), select=sel)
+    assert np.array_equal(part, full[sel])
+
+
+def test_reduced_grad_integer_exact():
+    tables, batch, D = _small_case(8, max_len=9)
+    dY = np.random.default_rng(2).integers(-8, 9, (batch.B, batch.T * D)).astype(np.float32)
+    ro = np.concatenate([[0], np.cumsum([t.shape[0] for t in tables])])
+    u, c, inv = O.dedup(O.global_keys(batch.indices, batch.offsets, ro, batch.T, batch.B))
+    gU = O.reduced_grad(dY, batch.offsets, batch.T, batch.B, D, "sum", inv, len(u))
+    dense = _autograd_dense(tables, batch, D, "sum", dY)
+    for j, key in enumerate(u.tolist()):
+        t = int(np.searchsorted(ro, key, side="right") - 1)
+        assert np.array_equal(gU[j], dense[t][key - int(ro[t])].astype(np.float32))
+
+
+def test_grad_pin_catches_mistakes():
+    tables, batch, D = _small_case(12)
+    dY = np.random.default_rng(3).standard_normal((batch.B, batch.T * D)).astype(np.float32)
+
+    def no_mean_scale(dY_, off, T, B, D_, pool, inv, U, select=None):
+        return O.reduced_grad(dY_, off, T, B, D_, "sum", inv, U)
+
+    def wrong_sign(dY_, off, T, B, D_, pool, inv, U, select=None):
+        return -O.reduced_grad(dY_, off, T, B, D_, pool, inv, U)
+
+    def wrong_table_block(dY_, off, T, B, D_, pool, inv, U, select=None):
+        return O.reduced_grad(np.roll(dY_, D_, axis=1), off, T, B, D_, pool, inv, U)
+
+    assert not _grad_pin_ok(no_mean_scale, tables, batch, D, "mean", dY)
+    assert not _grad_pin_ok(wrong_sign, tables, batch, D, "sum", dY)
+    assert not _grad_pin_ok(wrong_table_block, tables, batch, D, "sum", dY)
+
+
+# ---------------------------------------------------------------------------
+# Optimizer: vs torch.optim on a dense copy, closed forms, untouched rows
+# ---------------------------------------------------------------------------
+
+def _dense_opt_case(seed=0, rows=50, D=16, touched=17):
+    rng = np.random.default_rng(seed)
+    w = O.init_values(seed, 0, np.arange(rows), D)
+    tr = np.sort(rng.choice(rows, touched, replace=False))
+    g = np.zeros((rows, D), np.float32)
+    g[tr] = rng.standard_normal((touched, D)).astype(np.float32)
+    return w, g, tr
+
+
+def _update_pin_ok(step, opt, seed=0):
+    w, g, tr = _dense_opt_case(seed)
+    lr, eps = 0.01, 1e-8
+    p = torch.nn.Parameter(torch.from_numpy(w.copy()))
+    if opt == "sgd":
+        o = torch.optim.SGD([p], lr=lr)
+    else:
+        o = torch.optim.Adagrad([p], lr=lr, eps=eps, initial_accumulator_value=0.0)
+    p.grad = torch.from_numpy(g.copy())
+    o.step()
+    ref = p.detach().numpy()
+    G0 = np.zeros((len(tr), w.shape[1]), np.float32)
+    got, G1 = step(w[tr], G0 if opt == "adagrad" else None, g[tr], opt, lr, eps, "f32")
+    untouched = np.setdiff1d(np.arange(w.shape[0]), tr)
+    # torch applies the step with a fused multiply-add; the oracle rounds lr*g
+    # first, so they agree to an ulp of the operands' magnitude
+    scale = np.maximum(np.abs(w[tr]), np.abs(ref[tr] - w[tr]))
+    ok = _f32_scaled_close(got, ref[tr], scale, 2) and np.array_equal(ref[untouched], w[untouched])
+    if opt == "adagrad":
+        ok = ok and np.array_equal(G1, o.state[p]["sum"].numpy()[tr])
+    return bool(ok)
+
+
+@pytest.mark.parametrize("opt", ["sgd", "adagrad"])
+def test_update_vs_torch_optim(opt):
+    for seed in range(3):
+        assert _update_pin_ok(O.update_rows, opt, seed)
+
+
+def test_dense_zero_grad_is_noop():
+    # a dense step with g = 0 and G = 0 leaves every bit unchanged, which is why
+    # the oracle (and the library) only touch rows that were looked up
+    w = O.init_values(2, 1, np.arange(64), 32)
+    z = np.zeros_like(w)
+    w1, G1 = O.adagrad_step(w, z, z, 0.01, 1e-8)
+    assert np.array_equal(w1.view(np.uint32), w.view(np.uint32)) and np.all(G1 == 0)
+    assert np.array_equal(O.sgd_step(w, z, 0.01).view(np.uint32), w.view(np.uint32))
+
+
+def test_adagrad_step1_closed_form():
+    rng = np.random.default_rng(9)
+    w = O.init_values(1, 0, np.arange(200), 16)
+    g = rng.standard_normal(w.shape).astype(np.float32)
+    w1, G1 = O.adagrad_step(w, np.zeros_like(w), g, 0.01, 1e-8)
+    assert np.array_equal(G1, g * g)     # G' = g^2, one rounding
+    exact = w.astype(np.float64) - 0.01 * g.astype(np.float64) / (np.abs(g.astype(np.float64)) + 1e-8)
+    scale = np.maximum(np.abs(w), np.abs(exact - w)).astype(np.float32)
+    assert _f32_scaled_close(w1, exact, scale, 3)
+
+
+def test_update_pin_catches_mistakes():
+    def eps_inside_sqrt(w, G, g, opt, lr, eps, dt):
+        w32 = np.asarray(w, np.float32)
+        G1 = G + g * g
+        return (w32 - np.float32(lr) * g / np.sqrt(G1 + np.float32(eps))).astype(np.float32), G1
+
+    def sign_flip(w, G, g, opt, lr, eps, dt):
+        return O.update_rows(w, G, -g, opt, lr, eps, dt)
+
+    def lr_twice(w, G, g, opt, lr, eps, dt):
+        return O.update_rows(w, G, g, opt, 2 * lr, eps, dt)
+
+    assert not _update_pin_ok(sign_flip, "sgd")
+    assert not _update_pin_ok(lr_twice, "sgd")
+    assert not _update_pin_ok(sign_flip, "adagrad")
+    # eps inside the sqrt only differs where |g| ~ sqrt(eps); make that happen
+    w, g, tr = _dense_opt_case(1)
+    g[tr[:3]] = 1e-5
+    a, _ = eps_inside_sqrt(w[tr], np.zeros((len(tr), 16), np.float32), g[tr], "adagrad", 0.01, 1e-8, "f32")
+    b, _ = O.update_rows(w[tr], np.zeros((len(tr), 16), np.float32), g[tr], "adagrad", 0.01, 1e-8, "f32")
+    assert not _f32_ulp_close(a, b, 2)
+
+
+def test_low_precision_update_rounds_rne():
+    w32 = O.init_values(4, 0, np.arange(300), 16)
+    for dt in ("bf16", "f16"):
+        w = O.to_storage(w32, dt)
+        g = np.random.default_rng(0).standard_normal(w.shape).astype(np.float32)
+        got, _ = O.update_rows(w, None, g, "sgd", 0.01, 0.0, dt)
+        ref = torch.from_numpy(O.sgd_step(w, g, 0.01)).to(torch.bfloat16 if dt == "bf16" else torch.float16).float().numpy()
+        assert np.array_equal(got, ref)
