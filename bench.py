@@ -1,0 +1,289 @@
+#!/usr/bin/env python3
+"""Benchmark of the pooled-embedding training step on one MI355X.
+
+A step is one pass of the whole path over one batch: pooled forward
+(emb_forward_pooled), key dedup + segmented reduction (emb_backward_unique_reduce)
+and the fused sparse Adagrad/SGD update (emb_sparse_update). Inputs (tables,
+indices, offsets, upstream gradient) are resident in HBM before timing starts.
+
+Default workload: 26 fp32 tables x 4,000,000 rows x 128 (53 GB of weights +
+53 GB of Adagrad state), batch 65536, one lookup per bag, Zipf(1.05) keys, sum
+pooling, Adagrad lr 0.01 eps 1e-8. Seeded synthetic data; 4 different batches
+are cycled so consecutive steps see different keys.
+
+Prints ONE JSON line. `value` is lookups/s of the whole step; the forward and
+backward+update phases are also reported with their algorithmic GB/s, the
+dominant kernel against the 8 TB/s HBM roofline (per-kernel HIP events on the
+launch stream, recorded by the library), and the CPU oracle on a bounded
+sample of the same batch.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "pooled lookups/sec + achieved HBM GB/s (fwd, bwd+update) on 1 MI355X"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, help="workload 1..5 (3 = the headline)")
+    ap.add_argument("--batches", type=int, default=4)
+    ap.add_argument("--cpu-sample", type=int, default=32768, help="samples of batch 0 the oracle runs on")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--uniform-keys", action="store_true", help="control run: uniform keys instead of Zipf")
+    return ap.parse_args()
+
+
+def kernel_source_sha(name: str) -> str:
+    p = os.path.join(ROOT, "dlrm_sparse_embedding_amd", "csrc", name)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload_tag: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None if there is none or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload_tag}_counters.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    m_s = re.search(r"source_sha256_16:\s*([0-9a-f]+)", txt)
+    m_f = re.search(r"source_file:\s*(\S+)", txt)
+    if not (m_b and m_s and m_f):
+        return None
+    if kernel_source_sha(m_f.group(1)) != m_s.group(1):
+        return None
+    return float(m_b.group(1))
+
+
+def main() -> int:
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: --gpus {args.gpus} requested, but this implementation is the single-GPU "
+              "embedding path (one GPU's share of the tables); it runs on exactly one GPU and has no "
+              "multi-GPU mode.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    from dataclasses import replace
+
+    from dlrm_sparse_embedding_amd import emb as E
+    from dlrm_sparse_embedding_amd import workloads as W
+
+    cfg = W.make_config(args.config)
+    if args.uniform_keys:
+        cfg = replace(cfg, zipf_s=None)
+    T, B, D = cfg.T, cfg.batch, cfg.dim
+    elt = W.DTYPE_BYTES[cfg.dtype]
+    rowbytes = D * elt
+
+    torch.cuda.set_device(0)
+    specs = [E.TableSpec(t.rows, t.dim, t.dtype, t.col_slices) for t in cfg.tables]
+    tabs = E.EmbeddingTables(specs, with_state=cfg.opt == "adagrad")
+    tabs.init_uniform(cfg.init_seed)
+    print(f"[bench] tables ready: {T} x {cfg.tables[0].rows} x {D} {cfg.dtype}", file=sys.stderr, flush=True)
+
+    host_batches = [W.make_batch(cfg, k=k) for k in range(args.batches)]
+    dev = []
+    for b in host_batches:
+        dev.append((torch.from_numpy(b.indices).cuda(), torch.from_numpy(b.offsets).cuda(), b.N))
+    dY_host = W.make_dy(cfg)
+    dy = torch.from_numpy(dY_host).cuda()
+    Y = torch.empty((B, T * D), dtype=torch.float32, device="cuda")
+    nmax = max(b.N for b in host_batches)
+    bufs = tabs.backward_buffers(nmax, B, with_grad=False)
+    torch.cuda.synchronize()
+    print(f"[bench] {len(dev)} batches on device, N = {[b.N for b in host_batches]}", file=sys.stderr, flush=True)
+
+    # unique keys per batch (for the byte counts), read outside any timed region
+    U_of = []
+    for idx, off, n in dev:
+        tabs.backward(idx, off, B, cfg.pool, dy, bufs)
+        torch.cuda.synchronize()
+        U_of.append(int(bufs["num_unique"].item()))
+
+    def step(i):
+        idx, off, n = dev[i % len(dev)]
+        tabs.forward(idx, off, B, cfg.pool, out=Y)
+        tabs.backward(idx, off, B, cfg.pool, dy, bufs)
+        tabs.update(cfg.opt, cfg.lr, cfg.eps, bufs, dY=dy)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    tabs.check_device_error()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(K):
+        idx, off, n = dev[i % len(dev)]
+        ev[i][0].record()
+        tabs.forward(idx, off, B, cfg.pool, out=Y)
+        ev[i][1].record()
+        tabs.backward(idx, off, B, cfg.pool, dy, bufs)
+        tabs.update(cfg.opt, cfg.lr, cfg.eps, bufs, dY=dy)
+        ev[i][2].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev)
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev)
+    print(f"[bench] timed {K} steps: {total_ms:.3f} ms (wall {wall * 1e3:.1f} ms)", file=sys.stderr, flush=True)
+
+    # algorithmic bytes per step (SURVEY-style formula, actual N and U)
+    ib = 4 if host_batches[0].indices.dtype == np.int32 else 8
+    state_b = D * 4 if cfg.opt == "adagrad" else 0
+    steps_N = [dev[i % len(dev)][2] for i in range(K)]
+    steps_U = [U_of[i % len(dev)] for i in range(K)]
+    fwd_bytes = sum(n * rowbytes + n * ib + (T * B + 1) * ib + B * T * D * 4 for n in steps_N)
+    bwd_bytes = sum(B * T * D * 4 + n * ib + (T * B + 1) * ib + u * (rowbytes + state_b) * 2 + u * 8 + n * 4
+                    for n, u in zip(steps_N, steps_U))
+    lookups = sum(steps_N)
+
+    # per-kernel times (HIP events around each launch, on the launch stream)
+    E.emb_set_kernel_timing(tabs.ctx, True)
+    for i in range(K):
+        step(i)
+    torch.cuda.synchronize()
+    ktimes = E.emb_kernel_times(tabs.ctx)
+    E.emb_set_kernel_timing(tabs.ctx, False)
+    kavg_us = {k: (ms / n * 1e3 if n else 0.0) for k, (ms, n) in ktimes.items()}
+    ktot = {k: ms for k, (ms, n) in ktimes.items()}
+    dominant = max((k for k in ktot if k != "init"), key=lambda k: ktot[k])
+
+    # algorithmic bytes of one launch of the dominant kernel
+    Navg = lookups / K
+    Uavg = sum(steps_U) / K
+    per_launch = {
+        "forward": Navg * rowbytes + Navg * ib + (T * B + 1) * ib + B * T * D * 4,
+        # fused reduce + update: every bag's dY row once, each unique row's
+        # weight (+ state) read and written once, the sorted bag ids
+        "reduce": B * T * D * 4 + Uavg * (rowbytes + state_b) * 2 + Navg * 4,
+        "sort_scatter": Navg * 8 * 2,
+        "sort_hist": Navg * 8,
+        "keys": Navg * ib * 2 + Navg * (8 + 4),
+    }
+    alg = per_launch.get(dominant)
+    roofline = None
+    if alg is not None and kavg_us[dominant] > 0:
+        achieved = alg / (kavg_us[dominant] * 1e-6) / 1e9
+        wtag = f"cfg{args.config}" + ("_uniform" if args.uniform_keys else "")
+        src = {"forward": "k_forward.hip", "reduce": "k_reduce.hip", "sort_scatter": "k_keys_sort.hip",
+               "sort_hist": "k_keys_sort.hip", "keys": "k_keys_sort.hip"}[dominant]
+        traffic = measured_traffic(dominant, wtag)
+        roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                    "traffic": traffic, "alg_bytes_per_launch": int(alg),
+                    "avg_launch_us": round(kavg_us[dominant], 2), "source": src}
+
+    # CPU oracle on a bounded sample of batch 0
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, host_batches[0], dY_host, args.cpu_sample)
+
+    ms_step = total_ms / K
+    out = {
+        "metric": METRIC,
+        "value": round(lookups / (total_ms * 1e-3), 1),
+        "unit": "lookups/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if cfg.dtype == "f32" else f"{cfg.dtype}-storage/f32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{T} {cfg.dtype} tables x {cfg.tables[0].rows} rows x {D}, batch {B}, "
+                         f"{'uniform' if cfg.zipf_s is None else f'Zipf({cfg.zipf_s})'} keys, "
+                         f"{cfg.pool} pooling, {cfg.opt}"),
+            "config_id": args.config,
+            "global_batch": B,
+            "lookups_per_step": int(round(Navg)),
+            "unique_per_step": int(round(Uavg)),
+            "batches_cycled": len(dev),
+        },
+        "fwd": {"ms": round(fwd_ms / K, 4), "lookups_per_s": round(lookups / (fwd_ms * 1e-3), 1),
+                "alg_GBps": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9, 1),
+                "alg_bytes_per_step": int(fwd_bytes / K)},
+        "bwd_update": {"ms": round(bwd_ms / K, 4), "lookups_per_s": round(lookups / (bwd_ms * 1e-3), 1),
+                       "alg_GBps": round(bwd_bytes / (bwd_ms * 1e-3) / 1e9, 1),
+                       "alg_bytes_per_step": int(bwd_bytes / K)},
+        "kernels_avg_us": {k: round(v, 2) for k, v in kavg_us.items() if v > 0},
+        "kernels_ms_per_step": {k: round(v / K, 4) for k, v in ktot.items() if v > 0},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    tabs.close()
+    return 0
+
+
+def cpu_baseline(cfg, batch, dY, n_samples):
+    """The oracle, as it stands, on the first n_samples samples of the batch
+    (every table): forward, dedup, reduced gradient, optimizer step."""
+    import numpy as np
+
+    import oracle as O
+    from dlrm_sparse_embedding_amd import workloads as W
+
+    B = cfg.batch
+    s = np.arange(min(n_samples, B))
+    lens, keys = [], []
+    for t in range(cfg.T):
+        a, b = int(batch.offsets[t * B]), int(batch.offsets[t * B + len(s)])
+        lens.append(np.diff(batch.offsets[t * B:t * B + len(s) + 1].astype(np.int64)))
+        keys.append(batch.indices[a:b])
+    sub = W.make_batch_from_lengths(lens, keys, len(s))
+    dYs = np.ascontiguousarray(dY[s])
+    # untimed preparation: the stored contents of the touched rows
+    otabs = [O.TouchedRows(cfg.init_seed, t, cfg.dim, cfg.dtype,
+                           sub.indices[int(sub.offsets[t * len(s)]):int(sub.offsets[(t + 1) * len(s)])])
+             for t in range(cfg.T)]
+    ro = cfg.row_offset()
+    t0 = time.perf_counter()
+    O.pooled_forward(otabs, sub.indices, sub.offsets, cfg.T, len(s), cfg.dim, cfg.pool)
+    g = O.global_keys(sub.indices, sub.offsets, ro, cfg.T, len(s))
+    u, c, inv = O.dedup(g)
+    gU = O.reduced_grad(dYs, sub.offsets, cfg.T, len(s), cfg.dim, cfg.pool, inv, len(u))
+    t_of = np.searchsorted(ro, u, side="right") - 1
+    w_old = np.concatenate([otabs[t][u[t_of == t] - ro[t]] for t in range(cfg.T)])
+    G_old = np.zeros_like(w_old) if cfg.opt == "adagrad" else None
+    O.update_rows(w_old, G_old, gU, cfg.opt, cfg.lr, cfg.eps, cfg.dtype)
+    el = time.perf_counter() - t0
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except Exception:
+        avail = os.cpu_count()
+    return {"value": round(sub.N / el, 1), "unit": "lookups/s", "cores": 1, "kind": "oracle",
+            "sample": (f"first {len(s)} samples of the batch, all {cfg.T} tables ({sub.N} lookups, "
+                       f"{len(u)} unique keys): forward + dedup + reduce + optimizer, {el:.2f} s, "
+                       f"single-threaded numpy; {avail} host cores available")}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,501 @@
+// C-ABI host layer of libemb.so: argument validation, context / descriptor
+// management, workspace carve-up, kernel sequencing on the caller's stream,
+// optional per-kernel HIP-event timing. No C++ exception crosses the ABI.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "emb.h"
+#include "emb_internal.h"
+
+using namespace emb;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return EMB_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(EMB_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+struct TimedLaunch {
+  int kid;
+  hipEvent_t e0, e1;
+};
+
+}  // namespace
+
+struct emb_ctx {
+  std::vector<emb_table_desc> desc;
+  std::vector<int64_t> row_off;  // T+1
+  Geom g{};
+  bool has_state = false;
+  // device block (lazily uploaded)
+  int device = -1;
+  void* dev_block = nullptr;
+  DevCtx dc{};
+  // last backward, consumed by emb_sparse_update
+  struct {
+    const void* ws = nullptr;
+    const void* offsets = nullptr;
+    int itype = 0;
+    long long N = 0;
+    int B = 0;
+    int pool = 0;
+    const uint32_t* unique_keys = nullptr;
+    const int32_t* num_unique = nullptr;
+    bool valid = false;
+  } last;
+  // timing
+  bool timing = false;
+  std::vector<TimedLaunch> pending;
+  std::vector<hipEvent_t> free_events;
+};
+
+namespace {
+
+int ensure_device(emb_ctx* c) {
+  if (c->dev_block) return EMB_OK;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  const int T = c->g.T;
+  const size_t tab_bytes = sizeof(DevTable) * (size_t)T;
+  const size_t ro_off = (tab_bytes + 255) & ~size_t(255);
+  const size_t ro_bytes = sizeof(uint32_t) * (size_t)(T + 1);
+  const size_t err_off = (ro_off + ro_bytes + 255) & ~size_t(255);
+  const size_t total = err_off + 256;
+  std::vector<char> host(total, 0);
+  DevTable* ht = reinterpret_cast<DevTable*>(host.data());
+  for (int t = 0; t < T; ++t) {
+    for (int s = 0; s < EMB_MAX_SLICES; ++s) {
+      ht[t].w[s] = c->desc[t].weights[s];
+      ht[t].g[s] = c->desc[t].state[s];
+    }
+  }
+  uint32_t* hro = reinterpret_cast<uint32_t*>(host.data() + ro_off);
+  for (int t = 0; t <= T; ++t) hro[t] = (uint32_t)c->row_off[t];
+  void* p = nullptr;
+  e = hipMalloc(&p, total);
+  if (e != hipSuccess) return hip_fail(e, "hipMalloc(descriptor block)");
+  e = hipMemcpy(p, host.data(), total, hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(p);
+    return hip_fail(e, "hipMemcpy(descriptor block)");
+  }
+  c->dev_block = p;
+  c->device = dev;
+  c->dc.tables = reinterpret_cast<const DevTable*>(p);
+  c->dc.row_off = reinterpret_cast<const uint32_t*>(static_cast<char*>(p) + ro_off);
+  c->dc.err_flag = reinterpret_cast<int*>(static_cast<char*>(p) + err_off);
+  return EMB_OK;
+}
+
+hipEvent_t take_event(emb_ctx* c) {
+  if (!c->free_events.empty()) {
+    hipEvent_t e = c->free_events.back();
+    c->free_events.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Brackets one kernel launch with events when timing is on.
+struct KScope {
+  emb_ctx* c;
+  int kid;
+  hipStream_t st;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  KScope(emb_ctx* c_, int kid_, hipStream_t st_) : c(c_), kid(kid_), st(st_) {
+    if (c->timing) {
+      e0 = take_event(c);
+      e1 = take_event(c);
+      if (e0) (void)hipEventRecord(e0, st);
+    }
+  }
+  ~KScope() {
+    if (c->timing && e0 && e1) {
+      (void)hipEventRecord(e1, st);
+      c->pending.push_back({kid, e0, e1});
+    }
+  }
+};
+
+int dtype_bytes(int dt) { return dt == EMB_F32 ? 4 : 2; }
+
+int check_itype(int itype) {
+  if (itype != EMB_I32 && itype != EMB_I64) return fail(EMB_E_DTYPE, "itype %d is not EMB_I32/EMB_I64", itype);
+  return EMB_OK;
+}
+
+int check_pool(int pool) {
+  if (pool != EMB_POOL_SUM && pool != EMB_POOL_MEAN) return fail(EMB_E_DTYPE, "pool %d is not SUM/MEAN", pool);
+  return EMB_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+}  // namespace
+
+namespace emb {
+
+WsLayout ws_layout(const Geom& g, long long N, int B) {
+  WsLayout L{};
+  const long long TB = (long long)g.T * B;
+  L.ntiles = (int)((N + kChunk - 1) / kChunk);
+  L.nblk_sort = (int)((N + kSortTile - 1) / kSortTile);
+  L.nblk_rle = L.nblk_sort;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = (off + bytes + 255) & ~size_t(255);
+    return o;
+  };
+  L.keys_a = take(8ull * N);
+  L.keys_b = take(8ull * N);
+  L.bag_of_pos = take(4ull * N);
+  L.sorted_bag = take(4ull * N);
+  L.inv_len = take(4ull * (TB > 0 ? TB : 1));
+  L.seg_off = take(4ull * (N + 1));
+  L.chunk_off = take(4ull * (N + L.ntiles + 1));
+  L.chunk_seg = take(4ull * (N + L.ntiles));
+  L.tile_last_seg = take(4ull * (L.ntiles > 0 ? L.ntiles : 1));
+  L.partial = take(4ull * 2 * (L.ntiles > 0 ? L.ntiles : 1) * g.D);
+  L.ghist = take(4ull * kRadix * (L.nblk_sort > 0 ? L.nblk_sort : 1));
+  L.digit_tot = take(4ull * kRadix);
+  L.rle_blk = take(8ull * (L.nblk_rle > 0 ? L.nblk_rle : 1));
+  L.scalars = take(64);
+  L.total = off;
+  return L;
+}
+
+}  // namespace emb
+
+extern "C" {
+
+const char* emb_last_error(void) { return g_last_error.c_str(); }
+
+int emb_create_tables(const emb_table_desc* descs, int32_t num_tables, emb_ctx** out) {
+  try {
+    if (!out) return fail(EMB_E_INVAL, "out is NULL");
+    *out = nullptr;
+    if (!descs) return fail(EMB_E_INVAL, "descs is NULL");
+    if (num_tables < 1) return fail(EMB_E_INVAL, "num_tables must be >= 1 (got %d)", num_tables);
+    if (num_tables > kMaxTables) return fail(EMB_E_INVAL, "num_tables must be <= %d", kMaxTables);
+    const emb_table_desc& d0 = descs[0];
+    if (d0.dtype != EMB_F32 && d0.dtype != EMB_BF16 && d0.dtype != EMB_F16)
+      return fail(EMB_E_DTYPE, "table 0: unknown dtype %d", d0.dtype);
+    if (d0.col_slices < 1 || d0.col_slices > EMB_MAX_SLICES)
+      return fail(EMB_E_INVAL, "table 0: col_slices must be in 1..%d", EMB_MAX_SLICES);
+    if (d0.dim < 1 || d0.dim % d0.col_slices != 0)
+      return fail(EMB_E_INVAL, "table 0: dim %d not a positive multiple of col_slices %d", d0.dim, d0.col_slices);
+    const int eb = dtype_bytes(d0.dtype);
+    const int Dsl = d0.dim / d0.col_slices;
+    if ((Dsl * eb) % 16 != 0)
+      return fail(EMB_E_INVAL, "slice row of %d bytes is not a multiple of 16", Dsl * eb);
+    if (d0.dim * eb > 64 * 16)
+      return fail(EMB_E_INVAL, "dim %d too wide (row bytes must be <= 1024)", d0.dim);
+    const bool state0 = d0.state[0] != nullptr;
+    int64_t sum = 0;
+    for (int t = 0; t < num_tables; ++t) {
+      const emb_table_desc& d = descs[t];
+      if (d.dtype != EMB_F32 && d.dtype != EMB_BF16 && d.dtype != EMB_F16)
+        return fail(EMB_E_DTYPE, "table %d: unknown dtype %d", t, d.dtype);
+      if (d.dim != d0.dim || d.col_slices != d0.col_slices || d.dtype != d0.dtype)
+        return fail(EMB_E_INVAL, "table %d: dim/col_slices/dtype differ from table 0", t);
+      if (d.reserved != 0) return fail(EMB_E_INVAL, "table %d: reserved must be 0", t);
+      if (d.rows < 1) return fail(EMB_E_INVAL, "table %d: rows must be >= 1", t);
+      for (int s = 0; s < EMB_MAX_SLICES; ++s) {
+        const bool used = s < d.col_slices;
+        if (used && !d.weights[s]) return fail(EMB_E_INVAL, "table %d: weights[%d] is NULL", t, s);
+        if (used && !aligned(d.weights[s], 16)) return fail(EMB_E_INVAL, "table %d: weights[%d] not 16-byte aligned", t, s);
+        if (used && ((d.state[s] != nullptr) != state0))
+          return fail(EMB_E_INVAL, "table %d: state must be given for all slices of all tables or none", t);
+        if (used && d.state[s] && !aligned(d.state[s], 16))
+          return fail(EMB_E_INVAL, "table %d: state[%d] not 16-byte aligned", t, s);
+      }
+      sum += d.rows;
+      if (sum >= (int64_t)0xFFFFFFFFll) return fail(EMB_E_INVAL, "sum of rows must be < 2^32 - 1");
+    }
+    emb_ctx* c = new (std::nothrow) emb_ctx();
+    if (!c) return fail(EMB_E_INVAL, "out of host memory");
+    c->desc.assign(descs, descs + num_tables);
+    c->row_off.resize(num_tables + 1);
+    c->row_off[0] = 0;
+    for (int t = 0; t < num_tables; ++t) c->row_off[t + 1] = c->row_off[t] + descs[t].rows;
+    c->g.T = num_tables;
+    c->g.D = d0.dim;
+    c->g.Dsl = Dsl;
+    c->g.nslices = d0.col_slices;
+    c->g.dtype = d0.dtype;
+    c->g.total_rows = (uint32_t)sum;
+    int bits = 1;
+    while (bits < 32 && (1ull << bits) <= (uint64_t)sum) ++bits;
+    c->g.key_bits = bits;  // keys 0..sum (sum = invalid-index sentinel)
+    c->has_state = state0;
+    *out = c;
+    return ok();
+  } catch (...) {
+    return fail(EMB_E_INVAL, "internal error in emb_create_tables");
+  }
+}
+
+void emb_destroy_tables(emb_ctx* ctx) {
+  if (!ctx) return;
+  if (ctx->dev_block) {
+    (void)hipDeviceSynchronize();
+    (void)hipFree(ctx->dev_block);
+  }
+  for (auto& p : ctx->pending) {
+    (void)hipEventDestroy(p.e0);
+    (void)hipEventDestroy(p.e1);
+  }
+  for (auto e : ctx->free_events) (void)hipEventDestroy(e);
+  delete ctx;
+}
+
+int emb_row_offsets(const emb_ctx* ctx, int64_t* row_offset) {
+  if (!ctx || !row_offset) return fail(EMB_E_INVAL, "NULL argument");
+  for (int t = 0; t <= ctx->g.T; ++t) row_offset[t] = ctx->row_off[t];
+  return ok();
+}
+
+int emb_init_uniform(emb_ctx* ctx, uint64_t seed, void* hip_stream) {
+  if (!ctx) return fail(EMB_E_INVAL, "ctx is NULL");
+  int rc = ensure_device(ctx);
+  if (rc != EMB_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  for (int t = 0; t < ctx->g.T; ++t) {
+    for (int s = 0; s < ctx->g.nslices; ++s) {
+      KScope ks(ctx, EMB_K_INIT, st);
+      hipError_t e = launch_init_slice(ctx->g, ctx->dc, t, s, ctx->desc[t].rows, ctx->desc[t].weights[s],
+                                       ctx->desc[t].state[s], seed, st);
+      if (e != hipSuccess) return hip_fail(e, "init kernel");
+    }
+  }
+  return ok();
+}
+
+int emb_forward_pooled(emb_ctx* ctx, const void* indices, const void* offsets, int32_t itype, int64_t N,
+                       int32_t B, int32_t pool, float* out, void* hip_stream) {
+  if (!ctx) return fail(EMB_E_INVAL, "ctx is NULL");
+  int rc = check_itype(itype);
+  if (rc) return rc;
+  if ((rc = check_pool(pool))) return rc;
+  if (B < 0 || N < 0) return fail(EMB_E_INVAL, "negative B or N");
+  if (N >= (1ll << 31)) return fail(EMB_E_INVAL, "N must be < 2^31");
+  if (B == 0) return N == 0 ? ok() : fail(EMB_E_INVAL, "B == 0 with N > 0");
+  if (!offsets || !out) return fail(EMB_E_INVAL, "offsets/out is NULL");
+  if (N > 0 && !indices) return fail(EMB_E_INVAL, "indices is NULL");
+  if (!aligned(out, 16)) return fail(EMB_E_INVAL, "out must be 16-byte aligned");
+  if ((rc = ensure_device(ctx))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  KScope ks(ctx, EMB_K_FORWARD, st);
+  hipError_t e = launch_forward(ctx->g, ctx->dc, indices, offsets, itype, N, B, pool, out, st);
+  if (e != hipSuccess) return hip_fail(e, "forward kernel");
+  return ok();
+}
+
+size_t emb_backward_workspace_bytes(const emb_ctx* ctx, int64_t N, int32_t B) {
+  if (!ctx || N < 0 || B < 0 || N >= (1ll << 31)) return 0;
+  return ws_layout(ctx->g, N, B).total;
+}
+
+int emb_backward_unique_reduce(emb_ctx* ctx, const void* indices, const void* offsets, int32_t itype,
+                               int64_t N, int32_t B, int32_t pool, const float* dY, void* ws,
+                               size_t ws_bytes, uint32_t* unique_keys, int32_t* counts, int32_t* inverse,
+                               int32_t* num_unique, float* reduced_grad, void* hip_stream) {
+  if (!ctx) return fail(EMB_E_INVAL, "ctx is NULL");
+  int rc = check_itype(itype);
+  if (rc) return rc;
+  if ((rc = check_pool(pool))) return rc;
+  if (B < 0 || N < 0) return fail(EMB_E_INVAL, "negative B or N");
+  if (N >= (1ll << 31)) return fail(EMB_E_INVAL, "N must be < 2^31");
+  if (B == 0 && N > 0) return fail(EMB_E_INVAL, "B == 0 with N > 0");
+  if (!ws || !num_unique) return fail(EMB_E_INVAL, "ws/num_unique is NULL");
+  if (N > 0 && (!indices || !offsets || !dY || !unique_keys || !counts || !inverse))
+    return fail(EMB_E_INVAL, "NULL buffer");
+  if (!aligned(ws, 256)) return fail(EMB_E_INVAL, "ws must be 256-byte aligned");
+  if (dY && !aligned(dY, 16)) return fail(EMB_E_INVAL, "dY must be 16-byte aligned");
+  if (reduced_grad && !aligned(reduced_grad, 16)) return fail(EMB_E_INVAL, "reduced_grad must be 16-byte aligned");
+  const WsLayout L = ws_layout(ctx->g, N, B);
+  if (ws_bytes < L.total)
+    return fail(EMB_E_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, L.total);
+  if ((rc = ensure_device(ctx))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  char* w = static_cast<char*>(ws);
+  ctx->last.valid = false;
+  hipError_t e;
+  if (N == 0) {
+    KScope ks(ctx, EMB_K_RLE, st);
+    e = launch_set_empty(L, w, num_unique, st);
+    if (e != hipSuccess) return hip_fail(e, "empty backward");
+  } else {
+    {
+      KScope ks(ctx, EMB_K_KEYS, st);
+      e = launch_keys(ctx->g, ctx->dc, indices, offsets, itype, N, B, pool, L, w, st);
+      if (e != hipSuccess) return hip_fail(e, "keys kernel");
+    }
+    uint64_t* a = reinterpret_cast<uint64_t*>(w + L.keys_a);
+    uint64_t* b = reinterpret_cast<uint64_t*>(w + L.keys_b);
+    uint32_t* ghist = reinterpret_cast<uint32_t*>(w + L.ghist);
+    uint32_t* dtot = reinterpret_cast<uint32_t*>(w + L.digit_tot);
+    for (int shift = 0; shift < ctx->g.key_bits; shift += kRadixBits) {
+      {
+        KScope ks(ctx, EMB_K_SORT_HIST, st);
+        if ((e = launch_sort_hist(a, (int)N, shift, ghist, L.nblk_sort, st)) != hipSuccess)
+          return hip_fail(e, "sort histogram");
+      }
+      {
+        KScope ks(ctx, EMB_K_SORT_SCAN, st);
+        if ((e = launch_sort_scan(ghist, L.nblk_sort, dtot, st)) != hipSuccess) return hip_fail(e, "sort scan");
+      }
+      {
+        KScope ks(ctx, EMB_K_SORT_SCATTER, st);
+        if ((e = launch_sort_scatter(a, b, (int)N, shift, ghist, dtot, L.nblk_sort, st)) != hipSuccess)
+          return hip_fail(e, "sort scatter");
+      }
+      uint64_t* tmp = a;
+      a = b;
+      b = tmp;
+    }
+    {
+      KScope ks(ctx, EMB_K_RLE, st);
+      RleOut o{unique_keys, counts, inverse, num_unique};
+      if ((e = launch_rle(a, (int)N, L, w, o, st)) != hipSuccess) return hip_fail(e, "run-length encode");
+    }
+    if (reduced_grad) {
+      {
+        KScope ks(ctx, EMB_K_REDUCE, st);
+        if ((e = launch_reduce(ctx->g, ctx->dc, 0, (int)N, B, pool, dY, L, w, unique_keys, num_unique,
+                               reduced_grad, 0.f, 0.f, st)) != hipSuccess)
+          return hip_fail(e, "segment reduce");
+      }
+      {
+        KScope ks(ctx, EMB_K_COMBINE, st);
+        if ((e = launch_combine(ctx->g, ctx->dc, 0, (int)N, L, w, unique_keys, reduced_grad, 0.f, 0.f, st)) !=
+            hipSuccess)
+          return hip_fail(e, "segment combine");
+      }
+    }
+  }
+  ctx->last.ws = ws;
+  ctx->last.offsets = offsets;
+  ctx->last.itype = itype;
+  ctx->last.N = N;
+  ctx->last.B = B;
+  ctx->last.pool = pool;
+  ctx->last.unique_keys = unique_keys;
+  ctx->last.num_unique = num_unique;
+  ctx->last.valid = true;
+  return ok();
+}
+
+int emb_sparse_update(emb_ctx* ctx, int32_t opt, float lr, float eps, const void* ws, const float* dY,
+                      const float* reduced_grad, void* hip_stream) {
+  if (!ctx) return fail(EMB_E_INVAL, "ctx is NULL");
+  if (opt != EMB_OPT_SGD && opt != EMB_OPT_ADAGRAD) return fail(EMB_E_DTYPE, "opt %d is not SGD/ADAGRAD", opt);
+  if (opt == EMB_OPT_ADAGRAD && !ctx->has_state) return fail(EMB_E_INVAL, "Adagrad requested but the tables have no state");
+  if (!ctx->last.valid || ws != ctx->last.ws)
+    return fail(EMB_E_STATE, "ws is not the workspace of this context's last backward");
+  const long long N = ctx->last.N;
+  if (N > 0 && !reduced_grad && !dY) return fail(EMB_E_INVAL, "dY is NULL (needed by the fused path)");
+  if (dY && !aligned(dY, 16)) return fail(EMB_E_INVAL, "dY must be 16-byte aligned");
+  if (N == 0) return ok();
+  int rc;
+  if ((rc = ensure_device(ctx))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const WsLayout L = ws_layout(ctx->g, N, ctx->last.B);
+  const char* w = static_cast<const char*>(ws);
+  const int mode = opt == EMB_OPT_SGD ? 1 : 2;
+  hipError_t e;
+  if (reduced_grad) {
+    KScope ks(ctx, EMB_K_APPLY, st);
+    if ((e = launch_apply(ctx->g, ctx->dc, mode, (int)N, ctx->last.unique_keys, ctx->last.num_unique, reduced_grad,
+                          lr, eps, st)) != hipSuccess)
+      return hip_fail(e, "apply update");
+  } else {
+    {
+      KScope ks(ctx, EMB_K_REDUCE, st);
+      if ((e = launch_reduce(ctx->g, ctx->dc, mode, (int)N, ctx->last.B, ctx->last.pool, dY, L, w,
+                             ctx->last.unique_keys, ctx->last.num_unique, nullptr, lr, eps, st)) != hipSuccess)
+        return hip_fail(e, "fused reduce + update");
+    }
+    {
+      KScope ks(ctx, EMB_K_COMBINE, st);
+      if ((e = launch_combine(ctx->g, ctx->dc, mode, (int)N, L, w, ctx->last.unique_keys, nullptr, lr, eps, st)) !=
+          hipSuccess)
+        return hip_fail(e, "fused combine + update");
+    }
+  }
+  return ok();
+}
+
+int emb_check_device_error(emb_ctx* ctx, void* hip_stream) {
+  if (!ctx) return fail(EMB_E_INVAL, "ctx is NULL");
+  if (!ctx->dev_block) return ok();
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  hipError_t e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  int flag = 0;
+  e = hipMemcpy(&flag, ctx->dc.err_flag, sizeof(int), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy(err flag)");
+  if (flag) {
+    const int zero = 0;
+    e = hipMemcpy(ctx->dc.err_flag, &zero, sizeof(int), hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpy(clear err flag)");
+    return fail(EMB_E_BOUNDS, "a kernel saw an index outside [0, rows)");
+  }
+  return ok();
+}
+
+int emb_set_kernel_timing(emb_ctx* ctx, int32_t enable) {
+  if (!ctx) return fail(EMB_E_INVAL, "ctx is NULL");
+  ctx->timing = enable != 0;
+  return ok();
+}
+
+int emb_kernel_times(emb_ctx* ctx, double* ms, int64_t* launches) {
+  if (!ctx || !ms || !launches) return fail(EMB_E_INVAL, "NULL argument");
+  for (int k = 0; k < EMB_K_COUNT; ++k) {
+    ms[k] = 0.0;
+    launches[k] = 0;
+  }
+  for (auto& p : ctx->pending) {
+    hipError_t e = hipEventSynchronize(p.e1);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    float t = 0.f;
+    e = hipEventElapsedTime(&t, p.e0, p.e1);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    ms[p.kid] += t;
+    launches[p.kid] += 1;
+    ctx->free_events.push_back(p.e0);
+    ctx->free_events.push_back(p.e1);
+  }
+  ctx->pending.clear();
+  return ok();
+}
+
+}  // extern "C"

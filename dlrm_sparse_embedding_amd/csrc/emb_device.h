@@ -1,0 +1,162 @@
+// Device helpers for the gfx950 kernels: storage conversions, vector
+// loads/stores, wave-level primitives, XCD-aware block mapping.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "emb_internal.h"
+
+namespace emb {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+
+// ---- storage types ------------------------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h16) { return __uint_as_float(h16 << 16); }
+
+// fp32 -> bfloat16, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
+  uint32_t b = __float_as_uint(x);
+  if ((b & 0x7fffffffu) > 0x7f800000u) return ((b >> 16) | 0x40u) & 0xffffu;
+  b += 0x7fffu + ((b >> 16) & 1u);
+  return b >> 16;
+}
+
+__device__ __forceinline__ float f16_to_f32(uint32_t h16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h16);
+}
+
+// fp32 -> binary16 (v_cvt_f16_f32, round to nearest even in the default mode).
+__device__ __forceinline__ uint32_t f32_to_f16_rne(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+template <int DT>
+struct Stor;
+template <>
+struct Stor<EMB_F32> {
+  static constexpr int kBytes = 4;
+};
+template <>
+struct Stor<EMB_BF16> {
+  static constexpr int kBytes = 2;
+};
+template <>
+struct Stor<EMB_F16> {
+  static constexpr int kBytes = 2;
+};
+
+template <int DT>
+__device__ __forceinline__ float half_to_f32(uint32_t h) {
+  if constexpr (DT == EMB_BF16) return bf16_to_f32(h);
+  else return f16_to_f32(h);
+}
+template <int DT>
+__device__ __forceinline__ uint32_t f32_to_half(float x) {
+  if constexpr (DT == EMB_BF16) return f32_to_bf16_rne(x);
+  else return f32_to_f16_rne(x);
+}
+
+// 16 bytes of storage -> 16/sizeof(S) floats.
+template <int DT>
+__device__ __forceinline__ void widen16(const u4 v, float* out) {
+  if constexpr (DT == EMB_F32) {
+    out[0] = __uint_as_float(v.x);
+    out[1] = __uint_as_float(v.y);
+    out[2] = __uint_as_float(v.z);
+    out[3] = __uint_as_float(v.w);
+  } else {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = half_to_f32<DT>(w[i] & 0xffffu);
+      out[2 * i + 1] = half_to_f32<DT>(w[i] >> 16);
+    }
+  }
+}
+
+// Four consecutive elements of a row (16 bytes fp32 or 8 bytes 16-bit).
+template <int DT>
+__device__ __forceinline__ void load4(const void* p, float* out) {
+  if constexpr (DT == EMB_F32) {
+    const f4 v = *reinterpret_cast<const f4*>(p);
+    out[0] = v.x;
+    out[1] = v.y;
+    out[2] = v.z;
+    out[3] = v.w;
+  } else {
+    const u2 v = *reinterpret_cast<const u2*>(p);
+    out[0] = half_to_f32<DT>(v.x & 0xffffu);
+    out[1] = half_to_f32<DT>(v.x >> 16);
+    out[2] = half_to_f32<DT>(v.y & 0xffffu);
+    out[3] = half_to_f32<DT>(v.y >> 16);
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void store4(void* p, const float* in) {
+  if constexpr (DT == EMB_F32) {
+    f4 v;
+    v.x = in[0];
+    v.y = in[1];
+    v.z = in[2];
+    v.w = in[3];
+    *reinterpret_cast<f4*>(p) = v;
+  } else {
+    u2 v;
+    v.x = f32_to_half<DT>(in[0]) | (f32_to_half<DT>(in[1]) << 16);
+    v.y = f32_to_half<DT>(in[2]) | (f32_to_half<DT>(in[3]) << 16);
+    *reinterpret_cast<u2*>(p) = v;
+  }
+}
+
+// ---- index types ----------------------------------------------------------
+
+template <typename IDX>
+__device__ __forceinline__ long long ld_idx(const void* base, long long i) {
+  return (long long)reinterpret_cast<const IDX*>(base)[i];
+}
+
+// ---- wave helpers -----------------------------------------------------------
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+__device__ __forceinline__ uint64_t lanemask_lt() { return (1ull << __lane_id()) - 1ull; }
+
+// Blocks are handed to the 8 XCDs round-robin by block id; remap so that XCD
+// x works on the contiguous range [x*n/8, (x+1)*n/8) of logical blocks and
+// its private L2 sees one contiguous slice of the work. nblk_padded % 8 == 0.
+__device__ __forceinline__ int xcd_remap(int bid, int nblk_padded) {
+  const int per = nblk_padded >> 3;
+  return (bid & 7) * per + (bid >> 3);
+}
+
+// Exclusive scan of one value per thread over a 256-thread block.
+// `lds` needs 8 uint32 (4 waves). Returns the exclusive prefix; *total gets
+// the block sum. Contains __syncthreads.
+__device__ __forceinline__ uint32_t block_excl_scan_256(uint32_t v, uint32_t* lds, uint32_t* total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) lds[wave] = x;
+  __syncthreads();
+  uint32_t wpre = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t c = lds[w];
+    if (w < wave) wpre += c;
+    tot += c;
+  }
+  __syncthreads();
+  *total = tot;
+  return wpre + x - v;
+}
+
+}  // namespace emb

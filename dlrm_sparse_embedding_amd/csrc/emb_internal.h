@@ -1,0 +1,124 @@
+// Internal declarations shared by the HIP kernels and the C-ABI host layer.
+// Not part of the public interface (that is include/emb.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "emb.h"
+
+namespace emb {
+
+// Per-table device descriptor (weights / Adagrad state per column slice).
+struct DevTable {
+  void* w[EMB_MAX_SLICES];
+  float* g[EMB_MAX_SLICES];
+};
+
+// Upper bound on tables per context: the row-offset array is staged in LDS
+// by the update kernels (4 bytes per entry).
+constexpr int kMaxTables = 4096;
+
+// Segment chunking of the sorted lookups (see the reduce kernels): every
+// segment is cut at multiples of kChunk sorted positions.
+constexpr int kChunk = 128;
+
+// Radix sort / run-length tiles.
+constexpr int kSortThreads = 256;
+constexpr int kSortIPT = 8;
+constexpr int kSortTile = kSortThreads * kSortIPT;  // 2048 items
+constexpr int kRadixBits = 8;
+constexpr int kRadix = 1 << kRadixBits;
+
+inline int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+inline int next_pow2(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+inline int round_up8(int x) { return (x + 7) & ~7; }
+
+// Geometry common to every table of a context.
+struct Geom {
+  int T;
+  int D;          // logical row width
+  int Dsl;        // width of one column slice
+  int nslices;
+  int dtype;      // EMB_F32 / EMB_BF16 / EMB_F16
+  uint32_t total_rows;
+  int key_bits;   // bits needed for keys 0..total_rows (total_rows = invalid-index sentinel)
+};
+
+// Device-side context block.
+struct DevCtx {
+  const DevTable* tables;     // [T]
+  const uint32_t* row_off;    // [T+1]
+  int* err_flag;              // set to 1 by kernels that see an out-of-range index
+};
+
+// Workspace carve-up for the backward / update pair.
+struct WsLayout {
+  size_t keys_a, keys_b;        // uint64 [N] (key << 32 | position), ping-pong
+  size_t bag_of_pos;            // int32 [N]
+  size_t sorted_bag;            // int32 [N] bag of each sorted lookup
+  size_t inv_len;               // fp32 [T*B] 1/L per bag (mean pooling)
+  size_t seg_off;               // int32 [N+1]
+  size_t chunk_off;             // int32 [N + ntiles + 1]
+  size_t chunk_seg;             // int32 [N + ntiles]
+  size_t tile_last_seg;         // int32 [ntiles]
+  size_t partial;               // fp32 [2*ntiles][D]
+  size_t ghist;                 // uint32 [kRadix][nblk_sort]
+  size_t digit_tot;             // uint32 [kRadix]
+  size_t rle_blk;               // uint32x2 [nblk_rle]
+  size_t scalars;               // int32 [16]: [0] num_chunks
+  size_t total;
+  int ntiles, nblk_sort, nblk_rle;
+};
+WsLayout ws_layout(const Geom& g, long long N, int B);
+
+// ---- launchers (defined in the .hip files) -------------------------------
+// Each returns hipSuccess or the launch error. `kid` callbacks for timing are
+// handled by the host layer around these calls.
+
+hipError_t launch_init_slice(const Geom& g, const DevCtx& dc, int t, int s, int64_t rows, void* w,
+                             float* state, uint64_t seed, hipStream_t st);
+
+hipError_t launch_forward(const Geom& g, const DevCtx& dc, const void* indices, const void* offsets,
+                          int itype, long long N, int B, int pool, float* out, hipStream_t st);
+
+hipError_t launch_keys(const Geom& g, const DevCtx& dc, const void* indices, const void* offsets,
+                       int itype, long long N, int B, int pool, const WsLayout& L, char* ws,
+                       hipStream_t st);
+
+hipError_t launch_sort_hist(const uint64_t* keys, int N, int shift, uint32_t* ghist, int nblk,
+                            hipStream_t st);
+hipError_t launch_sort_scan(uint32_t* ghist, int nblk, uint32_t* digit_tot, hipStream_t st);
+hipError_t launch_sort_scatter(const uint64_t* in, uint64_t* out, int N, int shift,
+                               const uint32_t* ghist, const uint32_t* digit_tot, int nblk,
+                               hipStream_t st);
+
+struct RleOut {
+  uint32_t* unique_keys;
+  int32_t* counts;
+  int32_t* inverse;
+  int32_t* num_unique;
+};
+hipError_t launch_rle(const uint64_t* sorted, int N, const WsLayout& L, char* ws, const RleOut& o,
+                      hipStream_t st);
+hipError_t launch_set_empty(const WsLayout& L, char* ws, int32_t* num_unique, hipStream_t st);
+
+// mode: 0 = write reduced gradient, 1 = fused SGD, 2 = fused Adagrad
+hipError_t launch_reduce(const Geom& g, const DevCtx& dc, int mode, int N, int B, int pool,
+                         const float* dY, const WsLayout& L, const char* ws,
+                         const uint32_t* unique_keys, const int32_t* num_unique, float* grad_out,
+                         float lr, float eps, hipStream_t st);
+hipError_t launch_combine(const Geom& g, const DevCtx& dc, int mode, int N, const WsLayout& L,
+                          const char* ws, const uint32_t* unique_keys, float* grad_out, float lr,
+                          float eps, hipStream_t st);
+// opt: 1 = SGD, 2 = Adagrad; reads grad_in[u] for u < *num_unique
+hipError_t launch_apply(const Geom& g, const DevCtx& dc, int opt, int N,
+                        const uint32_t* unique_keys, const int32_t* num_unique,
+                        const float* grad_in, float lr, float eps, hipStream_t st);
+
+}  // namespace emb

@@ -1,0 +1,216 @@
+// Pooled forward: multi-table, multi-hot lookup + sum/mean pooling +
+// per-sample concatenation, in one kernel.
+//
+// What is computed follows "Merlin HugeCTR: GPU-accelerated recommender
+// system training and inference" (GTC 2022 deck), slide "COMMON EMBEDDING
+// PRIMITIVES" (table lookup, pooling/reduction of a multi-hot feature,
+// concatenation) and slide "HUGECTR EMBEDDING LAYER" (lookup and in-register
+// reduction + concatenation fused into one kernel): for bag (t, b),
+//   out[b][t*D + c] = sum_{i in bag} W_t[idx_i][c]   (or / L for mean),
+// accumulated in fp32 registers whatever the storage type.
+//
+// gfx950 mapping. A subgroup of LPR lanes owns one row: every lane loads 16
+// bytes (4 fp32 or 8 bf16/fp16 columns), so a row is one coalesced
+// LPR*16-byte access and a wave64 holds 64/LPR rows per load instruction.
+// Each subgroup walks a run of `bps` consecutive bags of one table as one
+// flat stream of lookups, issuing U = 8 row loads before consuming them, so
+// one-hot bags (one row per bag) still keep 8 rows per subgroup in flight.
+// The run's bag boundaries (bps+1 offsets) sit one per lane and are read by
+// lane shuffles (ds_bpermute), not by dependent global loads. Pooled rows
+// are written with non-temporal stores so the L2 keeps Zipf-hot table rows.
+// Blocks are remapped so each XCD works on a contiguous slice of the bags.
+#include "emb_device.h"
+
+namespace emb {
+
+struct FwdArgs {
+  const void* indices;
+  const void* offsets;
+  const DevTable* tables;
+  const uint32_t* row_off;
+  float* out;
+  int* err;
+  long long N;
+  int T, B, D, Dsl;
+  int bps;           // bags per subgroup (<= LPR - 1)
+  int sg_per_table;  // ceil(B / bps)
+  long long total_sg;
+  int nblk;
+  int mean;
+};
+
+__device__ __forceinline__ long long shfl64(long long v, int src, int width) {
+  const int lo = __shfl((int)(v & 0xffffffffll), src, width);
+  const int hi = __shfl((int)(v >> 32), src, width);
+  return ((long long)hi << 32) | (unsigned int)lo;
+}
+
+template <int DT, typename IDX, int LPR>
+__global__ __launch_bounds__(256) void k_forward(FwdArgs a) {
+  constexpr int CPL = 16 / Stor<DT>::kBytes;  // columns per lane
+  constexpr int SGW = 256 / LPR;              // subgroups per block
+  constexpr int U = 8;                        // rows in flight per subgroup
+  const int blk = xcd_remap(blockIdx.x, gridDim.x);
+  if (blk >= a.nblk) return;
+  const int lsg = threadIdx.x & (LPR - 1);
+  const long long sg = (long long)blk * SGW + threadIdx.x / LPR;
+  if (sg >= a.total_sg) return;
+
+  const int t = (int)(sg / a.sg_per_table);
+  const int b0 = (int)(sg - (long long)t * a.sg_per_table) * a.bps;
+  const int nb = min(a.bps, a.B - b0);
+  const long long bag0 = (long long)t * a.B + b0;
+
+  // offsets are clamped into [0, N] so that malformed input can never index
+  // outside `indices`
+  long long my_off = 0;
+  if (lsg <= nb) my_off = min(max(ld_idx<IDX>(a.offsets, bag0 + lsg), 0ll), a.N);
+  const long long P0 = shfl64(my_off, 0, LPR);
+  const long long P1 = shfl64(my_off, nb, LPR);
+
+  const long long ro = a.row_off[t];
+  const long long rows_t = (long long)a.row_off[t + 1] - ro;
+  const int c0 = lsg * CPL;
+  const bool act = c0 < a.D;
+  const int s = act ? c0 / a.Dsl : 0;
+  const int cs = c0 - s * a.Dsl;
+  const char* wbase =
+      reinterpret_cast<const char*>(a.tables[t].w[s]) + (size_t)cs * Stor<DT>::kBytes;
+  const size_t rstride = (size_t)a.Dsl * Stor<DT>::kBytes;
+  const size_t ostride = (size_t)a.T * a.D;
+  float* obase = a.out + (size_t)b0 * ostride + (size_t)t * a.D + c0;
+
+  float acc[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+
+  int cur = 0;
+  long long cur_start = P0;
+  long long cur_end = shfl64(my_off, nb > 0 ? 1 : 0, LPR);
+  int bad = 0;
+
+  auto flush = [&](long long L) {
+    float* o = obase + (size_t)cur * ostride;
+    if (act) {
+      if (a.mean && L > 0) {
+        const float fl = (float)L;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc[c] = __fdiv_rn(acc[c], fl);
+      }
+#pragma unroll
+      for (int c = 0; c < CPL; c += 4) {
+        f4 v = {acc[c], acc[c + 1], acc[c + 2], acc[c + 3]};
+        __builtin_nontemporal_store(v, reinterpret_cast<f4*>(o + c));
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+  };
+
+  for (long long p = P0; p < P1; p += U) {
+    u4 v[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      v[k] = u4{0u, 0u, 0u, 0u};
+      if (p + k < P1) {
+        const long long r = ld_idx<IDX>(a.indices, p + k);
+        if (r >= 0 && r < rows_t) {
+          if (act) v[k] = *reinterpret_cast<const u4*>(wbase + (size_t)r * rstride);
+        } else {
+          bad = 1;
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      if (p + k < P1) {
+        while (p + k >= cur_end && cur + 1 < nb) {
+          flush(cur_end - cur_start);
+          ++cur;
+          cur_start = cur_end;
+          cur_end = shfl64(my_off, cur + 1, LPR);
+        }
+        float f[CPL];
+        widen16<DT>(v[k], f);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc[c] += f[c];
+      }
+    }
+  }
+  // the bag in progress, then any empty bags that close the run
+  while (cur < nb) {
+    flush(cur_end - cur_start);
+    ++cur;
+    cur_start = cur_end;
+    cur_end = shfl64(my_off, min(cur + 1, nb), LPR);
+  }
+  if (bad && lsg == 0) atomicOr(a.err, 1);
+}
+
+#define FWD_LAUNCH(DT, IDX, LPR)                                                        \
+  hipLaunchKernelGGL((k_forward<DT, IDX, LPR>), dim3(grid), dim3(256), 0, st, args); \
+  break;
+
+#define FWD_LPR_SWITCH(DT, IDX)                \
+  switch (lpr) {                               \
+    case 2: FWD_LAUNCH(DT, IDX, 2)             \
+    case 4: FWD_LAUNCH(DT, IDX, 4)             \
+    case 8: FWD_LAUNCH(DT, IDX, 8)             \
+    case 16: FWD_LAUNCH(DT, IDX, 16)           \
+    case 32: FWD_LAUNCH(DT, IDX, 32)           \
+    default: FWD_LAUNCH(DT, IDX, 64)           \
+  }
+
+#define FWD_IDX_SWITCH(DT)                                   \
+  if (itype == EMB_I32) {                                    \
+    FWD_LPR_SWITCH(DT, int32_t)                              \
+  } else {                                                   \
+    FWD_LPR_SWITCH(DT, int64_t)                              \
+  }
+
+hipError_t launch_forward(const Geom& g, const DevCtx& dc, const void* indices, const void* offsets,
+                          int itype, long long N, int B, int pool, float* out, hipStream_t st) {
+  if (B == 0 || g.T == 0) return hipSuccess;
+  const int cpl = 16 / (g.dtype == EMB_F32 ? 4 : 2);
+  int lpr = next_pow2((g.D + cpl - 1) / cpl);
+  if (lpr < 2) lpr = 2;
+  // about 16 lookups per subgroup run, at most lpr-1 bags (one offset per lane)
+  const double avg = (double)N / ((double)g.T * (double)B);
+  int bps = avg > 0 ? (int)(16.0 / avg + 0.5) : lpr - 1;
+  if (bps < 1) bps = 1;
+  if (bps > lpr - 1) bps = lpr - 1;
+  if (bps > B) bps = B;
+  FwdArgs args;
+  args.indices = indices;
+  args.offsets = offsets;
+  args.tables = dc.tables;
+  args.row_off = dc.row_off;
+  args.out = out;
+  args.err = dc.err_flag;
+  args.N = N;
+  args.T = g.T;
+  args.B = B;
+  args.D = g.D;
+  args.Dsl = g.Dsl;
+  args.bps = bps;
+  args.sg_per_table = ceil_div(B, bps);
+  args.total_sg = (long long)g.T * args.sg_per_table;
+  const int sgw = 256 / lpr;
+  args.nblk = (int)((args.total_sg + sgw - 1) / sgw);
+  args.mean = pool == EMB_POOL_MEAN;
+  const int grid = round_up8(args.nblk);
+  switch (g.dtype) {
+    case EMB_F32:
+      FWD_IDX_SWITCH(EMB_F32)
+      break;
+    case EMB_BF16:
+      FWD_IDX_SWITCH(EMB_BF16)
+      break;
+    default:
+      FWD_IDX_SWITCH(EMB_F16)
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace emb

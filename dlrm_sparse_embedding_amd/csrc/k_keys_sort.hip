@@ -1,0 +1,249 @@
+// Backward, first half: global keys and a stable device LSD radix sort of
+// (key, position) pairs.
+//
+// The dedup is EMBark's unique-based / reduction-based compression (RecSys'24
+// article, section on embedding clusters) applied to one GPU's share: before
+// any gradient is reduced or a row is written, the step's lookups are grouped
+// by global key g = row_offset[t] + idx. Here the grouping is a sort: each
+// lookup i becomes the 64-bit word (g << 32 | i), and an LSD radix sort over
+// the low key_bits bits of g (8 bits per pass) orders the words by key, with
+// positions ascending inside a key because every pass is stable.
+//
+// Sort pass = three kernels:
+//   hist    per 2048-item tile, count digits in LDS -> ghist[digit][tile]
+//   scan    one block per digit: exclusive scan of its row over tiles
+//   scatter per tile: rank every item among equal digits (wave ballots give
+//           the lanes holding the same digit; per-wave LDS counters carry the
+//           rank across the tile's items in order), stage the tile in LDS in
+//           digit order, then write runs of equal digits contiguously.
+// The tile is striped per wave (item k of lane l of wave w sits at
+// w*512 + k*64 + l), which is the order the ranking visits, so ranks are
+// stable.
+#include "emb_device.h"
+
+namespace emb {
+
+// ---------------------------------------------------------------------------
+// keys
+// ---------------------------------------------------------------------------
+
+struct KeysArgs {
+  const void* indices;
+  const void* offsets;
+  const uint32_t* row_off;
+  uint64_t* keys;
+  int32_t* bag_of_pos;
+  float* inv_len;  // null unless mean pooling
+  int* err;
+  long long N;
+  int T, B;
+  uint32_t total_rows;
+};
+
+template <typename IDX>
+__global__ __launch_bounds__(256) void k_keys(KeysArgs a) {
+  const long long bag = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (bag >= (long long)a.T * a.B) return;
+  const int t = (int)(bag / a.B);
+  // clamped into [0, N]: malformed offsets cannot index outside the buffers
+  const long long s = min(max(ld_idx<IDX>(a.offsets, bag), 0ll), a.N);
+  const long long e = min(max(ld_idx<IDX>(a.offsets, bag + 1), s), a.N);
+  const uint32_t ro = a.row_off[t];
+  const long long rows_t = (long long)a.row_off[t + 1] - ro;
+  if (a.inv_len) a.inv_len[bag] = e > s ? __fdiv_rn(1.0f, (float)(e - s)) : 0.f;
+  bool bad = false;
+  for (long long p = s; p < e; ++p) {
+    const long long r = ld_idx<IDX>(a.indices, p);
+    uint32_t key;
+    if (r >= 0 && r < rows_t) {
+      key = ro + (uint32_t)r;
+    } else {
+      key = a.total_rows;  // sentinel: sorts last, never applied
+      bad = true;
+    }
+    a.keys[p] = ((uint64_t)key << 32) | (uint32_t)p;
+    a.bag_of_pos[p] = (int32_t)bag;
+  }
+  if (bad) atomicOr(a.err, 1);
+}
+
+hipError_t launch_keys(const Geom& g, const DevCtx& dc, const void* indices, const void* offsets,
+                       int itype, long long N, int B, int pool, const WsLayout& L, char* ws,
+                       hipStream_t st) {
+  KeysArgs a;
+  a.indices = indices;
+  a.offsets = offsets;
+  a.row_off = dc.row_off;
+  a.keys = reinterpret_cast<uint64_t*>(ws + L.keys_a);
+  a.bag_of_pos = reinterpret_cast<int32_t*>(ws + L.bag_of_pos);
+  a.inv_len = pool == EMB_POOL_MEAN ? reinterpret_cast<float*>(ws + L.inv_len) : nullptr;
+  a.err = dc.err_flag;
+  a.N = N;
+  a.T = g.T;
+  a.B = B;
+  a.total_rows = g.total_rows;
+  const long long bags = (long long)g.T * B;
+  const int grid = ceil_div(bags, 256);
+  if (grid == 0) return hipSuccess;
+  if (itype == EMB_I32)
+    hipLaunchKernelGGL(k_keys<int32_t>, dim3(grid), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_keys<int64_t>, dim3(grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// radix sort
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint32_t digit_of(uint64_t x, int shift) {
+  return (uint32_t)(x >> (32 + shift)) & (kRadix - 1);
+}
+
+__global__ __launch_bounds__(256) void k_sort_hist(const uint64_t* __restrict__ keys, int N,
+                                                   int shift, uint32_t* __restrict__ ghist,
+                                                   int nblk) {
+  __shared__ uint32_t h[kRadix];
+  h[threadIdx.x] = 0;
+  __syncthreads();
+  const long long base = (long long)blockIdx.x * kSortTile;
+#pragma unroll
+  for (int k = 0; k < kSortIPT; ++k) {
+    const long long i = base + k * 256 + threadIdx.x;
+    if (i < N) atomicAdd(&h[digit_of(keys[i], shift)], 1u);
+  }
+  __syncthreads();
+  ghist[(size_t)threadIdx.x * nblk + blockIdx.x] = h[threadIdx.x];
+}
+
+__global__ __launch_bounds__(256) void k_sort_scan(uint32_t* __restrict__ ghist, int nblk,
+                                                   uint32_t* __restrict__ digit_tot) {
+  __shared__ uint32_t lds[8];
+  uint32_t* row = ghist + (size_t)blockIdx.x * nblk;
+  uint32_t running = 0;
+  for (int base = 0; base < nblk; base += 256 * 4) {
+    uint32_t v[4];
+    uint32_t sum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = base + threadIdx.x * 4 + j;
+      v[j] = i < nblk ? row[i] : 0u;
+      sum += v[j];
+    }
+    uint32_t tot;
+    uint32_t run = running + block_excl_scan_256(sum, lds, &tot);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = base + threadIdx.x * 4 + j;
+      if (i < nblk) row[i] = run;
+      run += v[j];
+    }
+    running += tot;
+  }
+  if (threadIdx.x == 0) digit_tot[blockIdx.x] = running;
+}
+
+__global__ __launch_bounds__(256) void k_sort_scatter(const uint64_t* __restrict__ in,
+                                                      uint64_t* __restrict__ out, int N, int shift,
+                                                      const uint32_t* __restrict__ ghist,
+                                                      const uint32_t* __restrict__ digit_tot,
+                                                      int nblk) {
+  __shared__ uint32_t s_gbase[kRadix];   // global start of this tile's digit-d run
+  __shared__ uint32_t s_wcnt[4][kRadix]; // per-wave digit counters, then per-wave offsets
+  __shared__ uint32_t s_bexcl[kRadix];   // tile-local start of digit d
+  __shared__ uint64_t s_stage[kSortTile];
+  __shared__ uint32_t s_scan[8];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int blk = blockIdx.x;
+
+  {
+    uint32_t tot;
+    const uint32_t pre = block_excl_scan_256(digit_tot[tid], s_scan, &tot);
+    s_gbase[tid] = pre + ghist[(size_t)tid * nblk + blk];
+  }
+#pragma unroll
+  for (int w = 0; w < 4; ++w) s_wcnt[w][tid] = 0;
+  __syncthreads();
+
+  const long long base = (long long)blk * kSortTile + wave * (64 * kSortIPT);
+  uint64_t item[kSortIPT];
+  uint32_t rank[kSortIPT];
+#pragma unroll
+  for (int k = 0; k < kSortIPT; ++k) {
+    const long long i = base + k * 64 + lane;
+    item[k] = i < N ? in[i] : 0ull;
+  }
+  const uint64_t lt = lanemask_lt();
+#pragma unroll
+  for (int k = 0; k < kSortIPT; ++k) {
+    const bool valid = base + k * 64 + lane < N;
+    const uint32_t d = digit_of(item[k], shift);
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < kRadixBits; ++b) {
+      const bool bit = (d >> b) & 1u;
+      const uint64_t bb = __ballot(bit);
+      peers &= bit ? bb : ~bb;
+    }
+    const uint32_t before = (uint32_t)__popcll(peers & lt);
+    uint32_t basev = 0;
+    if (valid) basev = s_wcnt[wave][d];
+    rank[k] = basev + before;
+    // every lane has read the counter (LDS ops of one wave complete in
+    // order); the group's first lane now advances it
+    __builtin_amdgcn_wave_barrier();
+    if (valid && before == 0) s_wcnt[wave][d] = basev + (uint32_t)__popcll(peers);
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+  {
+    const uint32_t c0 = s_wcnt[0][tid], c1 = s_wcnt[1][tid], c2 = s_wcnt[2][tid], c3 = s_wcnt[3][tid];
+    s_wcnt[0][tid] = 0;
+    s_wcnt[1][tid] = c0;
+    s_wcnt[2][tid] = c0 + c1;
+    s_wcnt[3][tid] = c0 + c1 + c2;
+    uint32_t tot;
+    s_bexcl[tid] = block_excl_scan_256(c0 + c1 + c2 + c3, s_scan, &tot);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kSortIPT; ++k) {
+    const bool valid = base + k * 64 + lane < N;
+    if (valid) {
+      const uint32_t d = digit_of(item[k], shift);
+      s_stage[s_bexcl[d] + s_wcnt[wave][d] + rank[k]] = item[k];
+    }
+  }
+  __syncthreads();
+  const long long rem = (long long)N - (long long)blk * kSortTile;
+  const int cnt = rem < kSortTile ? (int)rem : kSortTile;
+  for (int j = tid; j < cnt; j += 256) {
+    const uint64_t x = s_stage[j];
+    const uint32_t d = digit_of(x, shift);
+    const size_t dst = (size_t)s_gbase[d] + (uint32_t)(j - (int)s_bexcl[d]);
+    if (dst < (size_t)N) out[dst] = x;
+  }
+}
+
+hipError_t launch_sort_hist(const uint64_t* keys, int N, int shift, uint32_t* ghist, int nblk,
+                            hipStream_t st) {
+  hipLaunchKernelGGL(k_sort_hist, dim3(nblk), dim3(256), 0, st, keys, N, shift, ghist, nblk);
+  return hipGetLastError();
+}
+
+hipError_t launch_sort_scan(uint32_t* ghist, int nblk, uint32_t* digit_tot, hipStream_t st) {
+  hipLaunchKernelGGL(k_sort_scan, dim3(kRadix), dim3(256), 0, st, ghist, nblk, digit_tot);
+  return hipGetLastError();
+}
+
+hipError_t launch_sort_scatter(const uint64_t* in, uint64_t* out, int N, int shift,
+                               const uint32_t* ghist, const uint32_t* digit_tot, int nblk,
+                               hipStream_t st) {
+  hipLaunchKernelGGL(k_sort_scatter, dim3(nblk), dim3(256), 0, st, in, out, N, shift, ghist,
+                     digit_tot, nblk);
+  return hipGetLastError();
+}
+
+}  // namespace emb

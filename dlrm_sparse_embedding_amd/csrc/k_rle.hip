@@ -1,0 +1,199 @@
+// Backward, second half of the dedup: run-length encoding of the sorted
+// (key, position) words into the unique keys, their counts, each lookup's
+// segment id (inverse) and the chunking of every segment used by the
+// gradient reduction.
+//
+// A segment starts where the key changes. A chunk starts at every segment
+// start and at every multiple of kChunk sorted positions, so every chunk lies
+// in one segment and in one kChunk-tile; a segment longer than a tile (a
+// Zipf-hot key) is thereby split into pieces that can be reduced in parallel
+// and combined in a fixed order. Both counters are scanned in one pass
+// (count per tile, scan of tile counts, write).
+#include "emb_device.h"
+
+namespace emb {
+
+__device__ __forceinline__ uint32_t key_of(uint64_t x) { return (uint32_t)(x >> 32); }
+
+__global__ __launch_bounds__(256) void k_rle_count(const uint64_t* __restrict__ sorted, int N,
+                                                   u2* __restrict__ blk_out) {
+  __shared__ uint32_t lds[8];
+  const long long base = (long long)blockIdx.x * kSortTile;
+  uint32_t cs = 0, cc = 0;
+#pragma unroll
+  for (int k = 0; k < kSortIPT; ++k) {
+    const long long i = base + k * 256 + threadIdx.x;
+    if (i < N) {
+      const bool fs = i == 0 || key_of(sorted[i]) != key_of(sorted[i - 1]);
+      const bool fc = fs || (i % kChunk) == 0;
+      cs += fs;
+      cc += fc;
+    }
+  }
+  uint32_t ts, tc;
+  block_excl_scan_256(cs, lds, &ts);
+  block_excl_scan_256(cc, lds, &tc);
+  if (threadIdx.x == 0) blk_out[blockIdx.x] = u2{ts, tc};
+}
+
+// One block: exclusive scan of the per-tile (segments, chunks) counts in
+// place; totals to *num_unique and num_chunks.
+__global__ __launch_bounds__(256) void k_rle_scan(u2* __restrict__ blk, int nblk,
+                                                  int32_t* __restrict__ num_unique,
+                                                  int32_t* __restrict__ num_chunks) {
+  __shared__ uint32_t lds[8];
+  const int per = (nblk + 255) / 256;
+  const int b0 = threadIdx.x * per;
+  uint32_t ss = 0, sc = 0;
+  for (int i = 0; i < per; ++i) {
+    if (b0 + i < nblk) {
+      const u2 v = blk[b0 + i];
+      ss += v.x;
+      sc += v.y;
+    }
+  }
+  uint32_t ts, tc;
+  uint32_t ps = block_excl_scan_256(ss, lds, &ts);
+  uint32_t pc = block_excl_scan_256(sc, lds, &tc);
+  for (int i = 0; i < per; ++i) {
+    if (b0 + i < nblk) {
+      const u2 v = blk[b0 + i];
+      blk[b0 + i] = u2{ps, pc};
+      ps += v.x;
+      pc += v.y;
+    }
+  }
+  if (threadIdx.x == 0) {
+    *num_unique = (int32_t)ts;
+    *num_chunks = (int32_t)tc;
+  }
+}
+
+struct RleArgs {
+  const uint64_t* sorted;
+  const u2* blk;
+  const int32_t* bag_of_pos;
+  uint32_t* unique_keys;
+  int32_t* inverse;
+  int32_t* seg_off;
+  int32_t* chunk_off;
+  int32_t* chunk_seg;
+  int32_t* tile_last_seg;
+  int32_t* sorted_bag;
+  int N;
+};
+
+__global__ __launch_bounds__(256) void k_rle_write(RleArgs a) {
+  __shared__ uint32_t s_ws[4], s_wc[4];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const long long base = (long long)blockIdx.x * kSortTile + wave * (64 * kSortIPT);
+  const uint64_t le = lanemask_lt() | (1ull << lane);
+  uint64_t item[kSortIPT];
+  uint32_t is[kSortIPT], ic[kSortIPT];
+  uint32_t fl = 0;  // bit k: segment start, bit 16+k: chunk start
+  uint32_t run_s = 0, run_c = 0;
+#pragma unroll
+  for (int k = 0; k < kSortIPT; ++k) {
+    const long long i = base + k * 64 + lane;
+    bool fs = false, fc = false;
+    item[k] = 0;
+    if (i < a.N) {
+      item[k] = a.sorted[i];
+      fs = i == 0 || key_of(item[k]) != key_of(a.sorted[i - 1]);
+      fc = fs || (i % kChunk) == 0;
+    }
+    const uint64_t bs = __ballot(fs);
+    const uint64_t bc = __ballot(fc);
+    is[k] = run_s + (uint32_t)__popcll(bs & le);
+    ic[k] = run_c + (uint32_t)__popcll(bc & le);
+    run_s += (uint32_t)__popcll(bs);
+    run_c += (uint32_t)__popcll(bc);
+    fl |= (fs ? 1u << k : 0u) | (fc ? 1u << (16 + k) : 0u);
+  }
+  if (lane == 0) {
+    s_ws[wave] = run_s;
+    s_wc[wave] = run_c;
+  }
+  __syncthreads();
+  const u2 bp = a.blk[blockIdx.x];
+  uint32_t ps = bp.x, pc = bp.y;
+  for (int w = 0; w < wave; ++w) {
+    ps += s_ws[w];
+    pc += s_wc[w];
+  }
+#pragma unroll
+  for (int k = 0; k < kSortIPT; ++k) {
+    const long long i = base + k * 64 + lane;
+    if (i >= a.N) continue;
+    const int32_t seg = (int32_t)(ps + is[k] - 1);
+    const int32_t chk = (int32_t)(pc + ic[k] - 1);
+    const uint32_t pos = (uint32_t)item[k];
+    if (pos < (uint32_t)a.N) {
+      a.inverse[pos] = seg;
+      a.sorted_bag[i] = a.bag_of_pos[pos];
+    }
+    if (fl & (1u << k)) {
+      a.unique_keys[seg] = key_of(item[k]);
+      a.seg_off[seg] = (int32_t)i;
+    }
+    if (fl & (1u << (16 + k))) {
+      a.chunk_off[chk] = (int32_t)i;
+      a.chunk_seg[chk] = seg;
+    }
+    if ((i % kChunk) == kChunk - 1 || i == a.N - 1) a.tile_last_seg[i / kChunk] = seg;
+    if (i == a.N - 1) {
+      a.seg_off[seg + 1] = a.N;
+      a.chunk_off[chk + 1] = a.N;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_counts(const int32_t* __restrict__ seg_off,
+                                                const int32_t* __restrict__ num_unique,
+                                                int32_t* __restrict__ counts, int N) {
+  const int U = min(*num_unique, N);
+  for (int u = blockIdx.x * 256 + threadIdx.x; u < U; u += gridDim.x * 256)
+    counts[u] = seg_off[u + 1] - seg_off[u];
+}
+
+__global__ void k_set_empty(int32_t* num_unique, int32_t* num_chunks) {
+  if (threadIdx.x == 0) {
+    *num_unique = 0;
+    *num_chunks = 0;
+  }
+}
+
+hipError_t launch_rle(const uint64_t* sorted, int N, const WsLayout& L, char* ws, const RleOut& o,
+                      hipStream_t st) {
+  u2* blk = reinterpret_cast<u2*>(ws + L.rle_blk);
+  int32_t* num_chunks = reinterpret_cast<int32_t*>(ws + L.scalars);
+  const int nblk = L.nblk_rle;
+  hipLaunchKernelGGL(k_rle_count, dim3(nblk), dim3(256), 0, st, sorted, N, blk);
+  hipLaunchKernelGGL(k_rle_scan, dim3(1), dim3(256), 0, st, blk, nblk, o.num_unique, num_chunks);
+  RleArgs a;
+  a.sorted = sorted;
+  a.blk = blk;
+  a.bag_of_pos = reinterpret_cast<const int32_t*>(ws + L.bag_of_pos);
+  a.unique_keys = o.unique_keys;
+  a.inverse = o.inverse;
+  a.seg_off = reinterpret_cast<int32_t*>(ws + L.seg_off);
+  a.chunk_off = reinterpret_cast<int32_t*>(ws + L.chunk_off);
+  a.chunk_seg = reinterpret_cast<int32_t*>(ws + L.chunk_seg);
+  a.tile_last_seg = reinterpret_cast<int32_t*>(ws + L.tile_last_seg);
+  a.sorted_bag = reinterpret_cast<int32_t*>(ws + L.sorted_bag);
+  a.N = N;
+  hipLaunchKernelGGL(k_rle_write, dim3(nblk), dim3(256), 0, st, a);
+  const int cgrid = ceil_div(N, 256) < 8192 ? ceil_div(N, 256) : 8192;
+  hipLaunchKernelGGL(k_counts, dim3(cgrid), dim3(256), 0, st,
+                     reinterpret_cast<const int32_t*>(ws + L.seg_off), o.num_unique, o.counts, N);
+  return hipGetLastError();
+}
+
+hipError_t launch_set_empty(const WsLayout& L, char* ws, int32_t* num_unique, hipStream_t st) {
+  hipLaunchKernelGGL(k_set_empty, dim3(1), dim3(64), 0, st, num_unique,
+                     reinterpret_cast<int32_t*>(ws + L.scalars));
+  return hipGetLastError();
+}
+
+}  // namespace emb

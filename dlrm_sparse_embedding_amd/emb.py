@@ -1,0 +1,301 @@
+"""Thin ctypes binding of libemb.so (C ABI declared in include/emb.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels. PyTorch supplies device memory and the current HIP stream. The
+functions carry the C names; ``EmbeddingTables`` bundles a context with the
+tensors that back it.
+
+``torch`` is imported before the library is loaded so that the library's
+``libamdhip64.so.7`` resolves to the HIP runtime torch already holds (one
+runtime per process). If ``libemb.so`` has not been built, loading raises --
+there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libemb.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "emb.h")
+
+EMB_OK = 0
+EMB_E_INVAL = -1
+EMB_E_DTYPE = -2
+EMB_E_WORKSPACE = -3
+EMB_E_HIP = -4
+EMB_E_BOUNDS = -5
+EMB_E_STATE = -6
+
+EMB_F32, EMB_BF16, EMB_F16 = 0, 1, 2
+EMB_I32, EMB_I64 = 0, 1
+EMB_POOL_SUM, EMB_POOL_MEAN = 0, 1
+EMB_OPT_SGD, EMB_OPT_ADAGRAD = 0, 1
+EMB_MAX_SLICES = 4
+
+KERNELS = ["init", "forward", "keys", "sort_hist", "sort_scan", "sort_scatter", "rle", "reduce",
+           "combine", "apply"]
+
+DTYPE_CODE = {"f32": EMB_F32, "bf16": EMB_BF16, "f16": EMB_F16}
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+POOL_CODE = {"sum": EMB_POOL_SUM, "mean": EMB_POOL_MEAN}
+OPT_CODE = {"sgd": EMB_OPT_SGD, "adagrad": EMB_OPT_ADAGRAD}
+
+
+class EmbError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"emb error {code}: {msg}")
+        self.code = code
+
+
+class emb_table_desc(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("dim", ctypes.c_int32), ("col_slices", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("weights", ctypes.c_void_p * EMB_MAX_SLICES),
+                ("state", ctypes.c_void_p * EMB_MAX_SLICES)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libemb.so once (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m dlrm_sparse_embedding_amd.build` (no CPU fallback exists)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    L.emb_create_tables.argtypes = [ctypes.POINTER(emb_table_desc), i32, ctypes.POINTER(vp)]
+    L.emb_create_tables.restype = ctypes.c_int
+    L.emb_destroy_tables.argtypes = [vp]
+    L.emb_destroy_tables.restype = None
+    L.emb_row_offsets.argtypes = [vp, ctypes.POINTER(i64)]
+    L.emb_row_offsets.restype = ctypes.c_int
+    L.emb_init_uniform.argtypes = [vp, ctypes.c_uint64, vp]
+    L.emb_init_uniform.restype = ctypes.c_int
+    L.emb_forward_pooled.argtypes = [vp, vp, vp, i32, i64, i32, i32, vp, vp]
+    L.emb_forward_pooled.restype = ctypes.c_int
+    L.emb_backward_workspace_bytes.argtypes = [vp, i64, i32]
+    L.emb_backward_workspace_bytes.restype = sz
+    L.emb_backward_unique_reduce.argtypes = [vp, vp, vp, i32, i64, i32, i32, vp, vp, sz, vp, vp, vp,
+                                             vp, vp, vp]
+    L.emb_backward_unique_reduce.restype = ctypes.c_int
+    L.emb_sparse_update.argtypes = [vp, i32, ctypes.c_float, ctypes.c_float, vp, vp, vp, vp]
+    L.emb_sparse_update.restype = ctypes.c_int
+    L.emb_last_error.argtypes = []
+    L.emb_last_error.restype = ctypes.c_char_p
+    L.emb_check_device_error.argtypes = [vp, vp]
+    L.emb_check_device_error.restype = ctypes.c_int
+    L.emb_set_kernel_timing.argtypes = [vp, i32]
+    L.emb_set_kernel_timing.restype = ctypes.c_int
+    L.emb_kernel_times.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
+    L.emb_kernel_times.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(rc: int) -> None:
+    if rc != EMB_OK:
+        raise EmbError(rc, lib().emb_last_error().decode())
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        return int(t)
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _itype(t: torch.Tensor) -> int:
+    if t.dtype == torch.int32:
+        return EMB_I32
+    if t.dtype == torch.int64:
+        return EMB_I64
+    raise ValueError(f"indices/offsets must be int32 or int64, not {t.dtype}")
+
+
+# ---- C entry points, same names --------------------------------------------
+
+def emb_create_tables(descs) -> int:
+    """descs: sequence of emb_table_desc. Returns the context handle."""
+    arr = (emb_table_desc * len(descs))(*descs)
+    out = ctypes.c_void_p()
+    _check(lib().emb_create_tables(arr, len(descs), ctypes.byref(out)))
+    return out.value
+
+
+def emb_destroy_tables(ctx: int) -> None:
+    lib().emb_destroy_tables(ctx)
+
+
+def emb_row_offsets(ctx: int, T: int) -> list:
+    buf = (ctypes.c_int64 * (T + 1))()
+    _check(lib().emb_row_offsets(ctx, buf))
+    return list(buf)
+
+
+def emb_init_uniform(ctx: int, seed: int, stream=None) -> None:
+    _check(lib().emb_init_uniform(ctx, int(seed), _stream(stream)))
+
+
+def emb_forward_pooled(ctx: int, indices: torch.Tensor, offsets: torch.Tensor, B: int, pool: str,
+                       out: torch.Tensor, stream=None) -> None:
+    if offsets.dtype != indices.dtype:
+        raise ValueError("indices and offsets must share one integer type")
+    if out.dtype != torch.float32:
+        raise ValueError("out must be fp32")
+    _check(lib().emb_forward_pooled(ctx, _ptr(indices), _ptr(offsets), _itype(indices),
+                                    int(indices.numel()), int(B), POOL_CODE[pool], _ptr(out),
+                                    _stream(stream)))
+
+
+def emb_backward_workspace_bytes(ctx: int, N: int, B: int) -> int:
+    return int(lib().emb_backward_workspace_bytes(ctx, int(N), int(B)))
+
+
+def emb_backward_unique_reduce(ctx: int, indices, offsets, B: int, pool: str, dY, ws, unique_keys,
+                               counts, inverse, num_unique, reduced_grad=None, stream=None) -> None:
+    if offsets.dtype != indices.dtype:
+        raise ValueError("indices and offsets must share one integer type")
+    _check(lib().emb_backward_unique_reduce(
+        ctx, _ptr(indices), _ptr(offsets), _itype(indices), int(indices.numel()), int(B),
+        POOL_CODE[pool], _ptr(dY), _ptr(ws), int(ws.numel() * ws.element_size()), _ptr(unique_keys),
+        _ptr(counts), _ptr(inverse), _ptr(num_unique), _ptr(reduced_grad), _stream(stream)))
+
+
+def emb_sparse_update(ctx: int, opt: str, lr: float, eps: float, ws, dY=None, reduced_grad=None,
+                      stream=None) -> None:
+    _check(lib().emb_sparse_update(ctx, OPT_CODE[opt], float(lr), float(eps), _ptr(ws), _ptr(dY),
+                                   _ptr(reduced_grad), _stream(stream)))
+
+
+def emb_check_device_error(ctx: int, stream=None) -> None:
+    _check(lib().emb_check_device_error(ctx, _stream(stream)))
+
+
+def emb_set_kernel_timing(ctx: int, enable: bool) -> None:
+    _check(lib().emb_set_kernel_timing(ctx, 1 if enable else 0))
+
+
+def emb_kernel_times(ctx: int) -> dict:
+    ms = (ctypes.c_double * len(KERNELS))()
+    n = (ctypes.c_int64 * len(KERNELS))()
+    _check(lib().emb_kernel_times(ctx, ms, n))
+    return {k: (ms[i], int(n[i])) for i, k in enumerate(KERNELS)}
+
+
+# ---- convenience: a context with the tensors behind it ---------------------
+
+@dataclass
+class TableSpec:
+    rows: int
+    dim: int
+    dtype: str = "f32"
+    col_slices: int = 1
+
+
+class EmbeddingTables:
+    """Allocates this GPU's tables (and Adagrad state) as torch tensors,
+    registers them with emb_create_tables and forwards the calls."""
+
+    def __init__(self, specs, with_state: bool, device="cuda"):
+        specs = list(specs)
+        self.specs = specs
+        self.T = len(specs)
+        self.dim = specs[0].dim
+        self.dtype = specs[0].dtype
+        self.col_slices = specs[0].col_slices
+        self.weights = []   # [t][s] tensors [rows, dim/col_slices]
+        self.state = []     # [t][s] fp32 tensors or None
+        descs = []
+        for sp in specs:
+            dsl = sp.dim // sp.col_slices
+            ws = [torch.empty((sp.rows, dsl), dtype=TORCH_DTYPE[sp.dtype], device=device)
+                  for _ in range(sp.col_slices)]
+            ss = ([torch.empty((sp.rows, dsl), dtype=torch.float32, device=device)
+                   for _ in range(sp.col_slices)] if with_state else None)
+            self.weights.append(ws)
+            self.state.append(ss)
+            d = emb_table_desc()
+            d.rows, d.dim, d.col_slices, d.dtype, d.reserved = sp.rows, sp.dim, sp.col_slices, DTYPE_CODE[sp.dtype], 0
+            for s in range(sp.col_slices):
+                d.weights[s] = ws[s].data_ptr()
+                d.state[s] = ss[s].data_ptr() if ss else None
+            descs.append(d)
+        self.ctx = emb_create_tables(descs)
+        self.row_offset = emb_row_offsets(self.ctx, self.T)
+
+    def close(self) -> None:
+        if self.ctx:
+            emb_destroy_tables(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def init_uniform(self, seed: int, stream=None) -> None:
+        emb_init_uniform(self.ctx, seed, stream)
+
+    def forward(self, indices, offsets, B: int, pool: str, out=None, stream=None):
+        if out is None:
+            out = torch.empty((B, self.T * self.dim), dtype=torch.float32, device=indices.device)
+        emb_forward_pooled(self.ctx, indices, offsets, B, pool, out, stream)
+        return out
+
+    def workspace(self, N: int, B: int, device="cuda"):
+        nbytes = emb_backward_workspace_bytes(self.ctx, N, B)
+        return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+    def backward_buffers(self, N: int, B: int, with_grad: bool, device="cuda"):
+        """Device outputs of emb_backward_unique_reduce sized by N."""
+        cap = max(N, 1)
+        return dict(
+            ws=self.workspace(N, B, device),
+            unique_keys=torch.empty(cap, dtype=torch.int32, device=device),  # uint32 bits
+            counts=torch.empty(cap, dtype=torch.int32, device=device),
+            inverse=torch.empty(cap, dtype=torch.int32, device=device),
+            num_unique=torch.empty(1, dtype=torch.int32, device=device),
+            reduced_grad=(torch.empty((cap, self.dim), dtype=torch.float32, device=device)
+                          if with_grad else None),
+        )
+
+    def backward(self, indices, offsets, B: int, pool: str, dY, bufs, stream=None) -> None:
+        emb_backward_unique_reduce(self.ctx, indices, offsets, B, pool, dY, bufs["ws"],
+                                   bufs["unique_keys"], bufs["counts"], bufs["inverse"],
+                                   bufs["num_unique"], bufs["reduced_grad"], stream)
+
+    def update(self, opt: str, lr: float, eps: float, bufs, dY=None, stream=None) -> None:
+        emb_sparse_update(self.ctx, opt, lr, eps, bufs["ws"], dY, bufs["reduced_grad"], stream)
+
+    def check_device_error(self, stream=None) -> None:
+        emb_check_device_error(self.ctx, stream)
+
+    def logical_rows(self, t: int, rows) -> torch.Tensor:
+        """Rows of table t gathered from its column slices, [len(rows), dim]
+        in the storage dtype (a read-back helper for checks)."""
+        r = torch.as_tensor(rows, dtype=torch.int64, device=self.weights[t][0].device)
+        return torch.cat([w.index_select(0, r) for w in self.weights[t]], dim=1)
+
+    def logical_state(self, t: int, rows) -> torch.Tensor:
+        r = torch.as_tensor(rows, dtype=torch.int64, device=self.weights[t][0].device)
+        return torch.cat([s.index_select(0, r) for s in self.state[t]], dim=1)

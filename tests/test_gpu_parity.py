@@ -1,0 +1,247 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Run on an MI355X:  python -u -m pytest tests -m gpu -x -v --timeout 300
+Every case prints its name, seed and shape before it touches the GPU.
+"""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from dlrm_sparse_embedding_amd import emb as E
+from dlrm_sparse_embedding_amd import workloads as W
+
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _free_gpu():
+    yield
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# table contents: device counter hash == oracle counter hash, bit for bit
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,dim,slices", [("f32", 16, 1), ("f32", 128, 1), ("bf16", 128, 1),
+                                              ("f16", 128, 4), ("f16", 64, 2), ("bf16", 8, 1)])
+def test_init_bit_exact(dtype, dim, slices):
+    _say("init", dtype, dim, slices)
+    specs = [E.TableSpec(1000, dim, dtype, slices), E.TableSpec(37, dim, dtype, slices)]
+    tabs = E.EmbeddingTables(specs, with_state=True)
+    tabs.init_uniform(12345)
+    torch.cuda.synchronize()
+    for t, sp in enumerate(specs):
+        rows = np.arange(sp.rows)
+        got = tabs.logical_rows(t, rows).float().cpu().numpy()
+        ref = O.to_storage(O.init_values(12345, t, rows, dim), dtype)
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+        assert torch.all(tabs.logical_state(t, rows) == 0)
+    tabs.close()
+
+
+# ---------------------------------------------------------------------------
+# the five configurations, oracle-sized: every element checked
+# ---------------------------------------------------------------------------
+
+REDUCED = {1: dict(), 2: dict(batch=2048), 3: dict(batch=1024), 4: dict(batch=48), 5: dict(batch=1024)}
+
+
+@pytest.mark.parametrize("path", ["fused", "materialized"])
+@pytest.mark.parametrize("cfg_id", [1, 2, 3, 4, 5])
+def test_config_reduced(cfg_id, path):
+    cfg = W.make_config(cfg_id, **REDUCED[cfg_id])
+    batch = W.make_batch(cfg)
+    dY = W.make_dy(cfg)
+    _say(f"cfg{cfg_id} reduced B={cfg.batch} N={batch.N} path={path}")
+    r = P.run_step(cfg, batch, dY, path=path)
+    assert r["U"] > 0
+
+
+# ---------------------------------------------------------------------------
+# full sizes, launch configuration of the benchmark, sampled outputs
+# ---------------------------------------------------------------------------
+
+@pytest.mark.slow
+@pytest.mark.parametrize("cfg_id", [2, 3, 4, 5])
+def test_config_full_sampled(cfg_id):
+    cfg = W.make_config(cfg_id)
+    batch = W.make_batch(cfg)
+    dY = W.make_dy(cfg)
+    _say(f"cfg{cfg_id} full B={cfg.batch} N={batch.N}")
+    P.run_step(cfg, batch, dY, path="fused", sample_bags=512, sample_keys=3000)
+
+
+# ---------------------------------------------------------------------------
+# exactness: integer upstream gradients make every fp32 sum exact, so the
+# fused sparse update must equal the oracle bit for bit
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg_id,opt", [(1, "sgd"), (1, "adagrad"), (2, "adagrad"), (2, "sgd")])
+def test_integer_grad_bit_exact(cfg_id, opt):
+    from dataclasses import replace
+    cfg = replace(W.make_config(cfg_id, **REDUCED[cfg_id]), opt=opt, eps=1e-8)
+    batch = W.make_batch(cfg)
+    dY = W.make_int_dy(cfg)
+    _say(f"int-grad cfg{cfg_id} {opt} N={batch.N}")
+    r = P.run_step(cfg, batch, dY, path="fused")
+    u, c, inv = P.oracle_dedup(cfg, batch)
+    g = O.reduced_grad(dY, batch.offsets, cfg.T, cfg.batch, cfg.dim, cfg.pool, inv, len(u))
+    w_old = P.stored_init(cfg, u)
+    G_old = np.zeros_like(w_old) if opt == "adagrad" else None
+    w_ref, G_ref = O.update_rows(w_old, G_old, g, opt, cfg.lr, cfg.eps, cfg.dtype)
+    assert np.array_equal(r["w_new"].view(np.uint32), w_ref.view(np.uint32))
+    if opt == "adagrad":
+        assert np.array_equal(r["G_new"].view(np.uint32), G_ref.view(np.uint32))
+
+
+def test_fused_equals_materialized_and_reruns_bit_identical():
+    cfg = W.make_config(2, batch=4096)
+    batch = W.make_batch(cfg, k=3)
+    dY = W.make_dy(cfg, k=3)
+    _say("determinism cfg2 B=4096")
+    res = []
+    for path in ("fused", "materialized", "fused"):
+        res.append(P.run_step(cfg, batch, dY, path=path, sample_untouched=0))
+    for r in res[1:]:
+        assert np.array_equal(r["w_new"].view(np.uint32), res[0]["w_new"].view(np.uint32))
+        assert np.array_equal(r["G_new"].view(np.uint32), res[0]["G_new"].view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------
+
+def _custom_cfg(rows, dim=16, dtype="f32", slices=1, B=8, pool="sum", opt="adagrad"):
+    tabs = tuple(W.TableSpec(r, dim, dtype, slices) for r in rows)
+    return W.Config(99, "custom", tabs, B, pool, opt, 0.05, 1e-8, tuple(1 for _ in rows), None, init_seed=99)
+
+
+@pytest.mark.parametrize("pool", ["sum", "mean"])
+@pytest.mark.parametrize("itype", [np.int32, np.int64])
+def test_empty_and_ragged_bags(pool, itype):
+    rng = np.random.default_rng(11)
+    cfg = _custom_cfg([1, 7, 300, 5000], dim=32, B=333, pool=pool)
+    lens = [rng.integers(0, 6, cfg.batch) * (rng.random(cfg.batch) < 0.7) for _ in range(cfg.T)]
+    lens[1][:] = 0                                   # a table with only empty bags
+    keys = [rng.integers(0, cfg.tables[t].rows, int(lens[t].sum())) for t in range(cfg.T)]
+    batch = W.make_batch_from_lengths(lens, keys, cfg.batch, index_dtype=itype)
+    dY = np.random.default_rng(1).standard_normal((cfg.batch, cfg.T * cfg.dim)).astype(np.float32)
+    _say("ragged", pool, itype.__name__, batch.N)
+    P.run_step(cfg, batch, dY, path="materialized")
+    P.run_step(cfg, batch, dY, path="fused")
+
+
+def test_all_empty_batch():
+    cfg = _custom_cfg([10, 20], B=17)
+    batch = W.make_batch_from_lengths([np.zeros(17, int)] * 2, [np.zeros(0, int)] * 2, 17)
+    _say("all-empty")
+    tabs = P.make_tables(cfg)
+    idx, off, dy = P.to_dev(batch, np.ones((17, 32), np.float32))
+    Y = tabs.forward(idx, off, 17, "mean")
+    bufs = tabs.backward_buffers(0, 17, with_grad=True)
+    tabs.backward(idx, off, 17, "mean", dy, bufs)
+    tabs.update("adagrad", 0.1, 1e-8, bufs, dY=dy)
+    torch.cuda.synchronize()
+    assert torch.all(Y == 0) and int(bufs["num_unique"].item()) == 0
+    tabs.close()
+
+
+@pytest.mark.parametrize("n,dim,dtype", [(50000, 128, "f32"), (20000, 64, "bf16"), (1000, 128, "f16")])
+def test_single_hot_key_long_segment(n, dim, dtype):
+    # one key looked up n times (one segment of length n, split over many
+    # chunks and combined), next to a few keys of other lengths
+    rng = np.random.default_rng(5)
+    cfg = _custom_cfg([100, 1000], dim=dim, dtype=dtype, B=n)
+    k0 = np.full(n, 42)
+    k1 = rng.integers(0, 1000, n)
+    k1[: n // 2] = 7                                   # second long segment, in table 1
+    batch = W.make_batch_from_lengths([np.ones(n, int), np.ones(n, int)], [k0, k1], n)
+    dY = rng.standard_normal((n, 2 * dim)).astype(np.float32)
+    _say("hot-key", n, dim, dtype)
+    for path in ("materialized", "fused"):
+        P.run_step(cfg, batch, dY, path=path)
+
+
+def test_segments_on_chunk_boundaries():
+    # segment lengths straddling the 128-position chunk grid exactly
+    lens_seq = [128, 128, 1, 127, 129, 256, 255, 257, 1, 1, 384, 2]
+    keys = np.concatenate([np.full(L, i * 3) for i, L in enumerate(lens_seq)])
+    rng = np.random.default_rng(2)
+    rng.shuffle(keys)
+    n = len(keys)
+    cfg = _custom_cfg([64], dim=16, B=n, opt="sgd")
+    batch = W.make_batch_from_lengths([np.ones(n, int)], [keys], n)
+    dY = rng.standard_normal((n, 16)).astype(np.float32)
+    _say("chunk-boundaries", n)
+    for path in ("materialized", "fused"):
+        P.run_step(cfg, batch, dY, path=path)
+
+
+def test_out_of_range_index_flagged_not_applied():
+    cfg = _custom_cfg([50, 60], B=4, opt="sgd")
+    keys = [np.array([1, 2, 50, 3]), np.array([-1, 5, 59, 60])]   # 50, -1, 60 out of range
+    batch = W.make_batch_from_lengths([np.ones(4, int)] * 2, keys, 4, index_dtype=np.int64)
+    _say("out-of-range")
+    tabs = P.make_tables(cfg)
+    idx, off, dy = P.to_dev(batch, np.ones((4, 32), np.float32))
+    Y = tabs.forward(idx, off, 4, "sum")
+    with pytest.raises(E.EmbError) as ei:
+        tabs.check_device_error()
+    assert ei.value.code == E.EMB_E_BOUNDS
+    y = Y.cpu().numpy()
+    assert np.all(y[2, :16] == 0) and np.all(y[0, 16:] == 0) and np.all(y[3, 16:] == 0)
+    bufs = tabs.backward_buffers(8, 4, with_grad=False)
+    tabs.backward(idx, off, 4, "sum", dy, bufs)
+    tabs.update("sgd", 0.5, 0.0, bufs, dY=dy)
+    with pytest.raises(E.EmbError):
+        tabs.check_device_error()
+    U = int(bufs["num_unique"].item())
+    uk = bufs["unique_keys"][:U].cpu().numpy().view(np.uint32)
+    assert uk[-1] == cfg.total_rows          # the sentinel segment sorts last
+    tabs.check_device_error()                # flag was cleared
+    # valid rows were updated, the rest of both tables is untouched
+    w, _ = P.read_rows(tabs, cfg, np.arange(cfg.total_rows))
+    init = P.stored_init(cfg, np.arange(cfg.total_rows))
+    touched = np.array([1, 2, 3, 50 + 5, 50 + 59])
+    changed = np.nonzero(np.any(w != init, axis=1))[0]
+    assert np.array_equal(changed, touched)
+    tabs.close()
+
+
+def test_two_adagrad_steps():
+    cfg = W.make_config(2, batch=3000)
+    b1, b2 = W.make_batch(cfg, k=0), W.make_batch(cfg, k=1)
+    d1, d2 = W.make_dy(cfg, k=0), W.make_dy(cfg, k=1)
+    _say("two-steps cfg2")
+    tabs = P.make_tables(cfg)
+    state = {}   # key -> (w, G) oracle state of touched rows
+    for batch, dY in ((b1, d1), (b2, d2)):
+        idx, off, dy = P.to_dev(batch, dY)
+        bufs = tabs.backward_buffers(batch.N, cfg.batch, with_grad=False)
+        tabs.backward(idx, off, cfg.batch, cfg.pool, dy, bufs)
+        tabs.update(cfg.opt, cfg.lr, cfg.eps, bufs, dY=dy)
+        torch.cuda.synchronize()
+        u, c, inv = P.oracle_dedup(cfg, batch)
+        g, m = P.grad_bounds(cfg, batch, dY, inv, len(u))
+        w_old = P.stored_init(cfg, u)
+        G_old = np.zeros_like(w_old)
+        for j, k in enumerate(u.tolist()):
+            if k in state:
+                w_old[j], G_old[j] = state[k]
+        w_new, G_new = P.read_rows(tabs, cfg, u)
+        P.check_update(cfg, w_new, G_new, w_old, G_old, g, m)
+        for j, k in enumerate(u.tolist()):
+            state[k] = (w_new[j].copy(), G_new[j].copy())
+    tabs.close()
