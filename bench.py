@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=32768, help="samples of batch 0 the oracle runs on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--uniform-keys", action="store_true", help="control run: uniform keys instead of Zipf")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (5 times) and exit: the reference "
+                         "point for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
     return ap.parse_args()
 
 
@@ -82,6 +85,16 @@ def main() -> int:
     import numpy as np
     import torch
     from dataclasses import replace
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n * 4, "launches": 5}), flush=True)
+        return 0
 
     from dlrm_sparse_embedding_amd import emb as E
     from dlrm_sparse_embedding_amd import workloads as W

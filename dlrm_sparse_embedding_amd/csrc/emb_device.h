@@ -25,13 +25,42 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
   return b >> 16;
 }
 
+// binary16 -> fp32, exact, written on the bit fields so that no hardware
+// denormal mode can flush a subnormal half.
 __device__ __forceinline__ float f16_to_f32(uint32_t h16) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)h16);
+  const uint32_t sign = (h16 & 0x8000u) << 16;
+  const uint32_t e = (h16 >> 10) & 0x1fu;
+  const uint32_t m = h16 & 0x3ffu;
+  if (e == 0) {
+    const float v = __fmul_rn((float)m, 0x1p-24f);  // subnormal: m * 2^-24, exact
+    return __uint_as_float(__float_as_uint(v) | sign);
+  }
+  if (e == 31) return __uint_as_float(sign | 0x7f800000u | (m << 13));
+  return __uint_as_float(sign | ((e + 112u) << 23) | (m << 13));
 }
 
-// fp32 -> binary16 (v_cvt_f16_f32, round to nearest even in the default mode).
-__device__ __forceinline__ uint32_t f32_to_f16_rne(float x) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+// fp32 -> binary16, round to nearest, ties to even, on the bit fields
+// (subnormal halves included, whatever the hardware denormal mode).
+__device__ __forceinline__ uint32_t f32_to_f16_rne(float f) {
+  const uint32_t x = __float_as_uint(f);
+  const uint32_t sign = (x >> 16) & 0x8000u;
+  const uint32_t ax = x & 0x7fffffffu;
+  if (ax > 0x7f800000u) return sign | 0x7e00u | ((ax >> 13) & 0x3ffu);  // NaN stays NaN
+  if (ax >= 0x477ff000u) return sign | 0x7c00u;                        // >= 65520 -> inf
+  if (ax >= 0x38800000u) {                                             // normal half
+    uint32_t m = ax - 0x38000000u;                                     // rebias 127 -> 15
+    m += 0xfffu + ((m >> 13) & 1u);
+    return sign | (m >> 13);
+  }
+  if (ax <= 0x33000000u) return sign;                                  // <= 2^-25 -> 0
+  const uint32_t e = ax >> 23;                                         // 102..112
+  const uint32_t mant = (ax & 0x7fffffu) | 0x800000u;
+  const uint32_t sh = 126u - e;                                        // 14..24
+  uint32_t q = mant >> sh;
+  const uint32_t rem = mant & ((1u << sh) - 1u);
+  const uint32_t half = 1u << (sh - 1u);
+  if (rem > half || (rem == half && (q & 1u))) ++q;                    // may carry into 2^-14
+  return sign | q;
 }
 
 template <int DT>

@@ -46,7 +46,11 @@ def test_init_bit_exact(dtype, dim, slices):
         rows = np.arange(sp.rows)
         got = tabs.logical_rows(t, rows).float().cpu().numpy()
         ref = O.to_storage(O.init_values(12345, t, rows, dim), dtype)
-        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+        bad = got.view(np.uint32) != ref.view(np.uint32)
+        if bad.any():
+            r, c = np.nonzero(bad)
+            raise AssertionError(f"table {t}: {int(bad.sum())} of {bad.size} differ; first (row, col, got, ref): "
+                                 f"{[(int(a), int(b), float(got[a, b]), float(ref[a, b])) for a, b in zip(r[:6], c[:6])]}")
         assert torch.all(tabs.logical_state(t, rows) == 0)
     tabs.close()
 
