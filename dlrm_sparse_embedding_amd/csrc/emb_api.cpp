@@ -165,6 +165,7 @@ WsLayout ws_layout(const Geom& g, long long N, int B) {
   WsLayout L{};
   const long long TB = (long long)g.T * B;
   L.ntiles = (int)((N + kChunk - 1) / kChunk);
+  L.ntiles1 = (int)((N + kChunk1 - 1) / kChunk1);
   L.nblk_sort = (int)((N + kSortTile - 1) / kSortTile);
   L.nblk_rle = L.nblk_sort;
   size_t off = 0;
@@ -179,13 +180,14 @@ WsLayout ws_layout(const Geom& g, long long N, int B) {
   L.sorted_bag = take(4ull * N);
   L.inv_len = take(4ull * (TB > 0 ? TB : 1));
   L.seg_off = take(4ull * (N + 1));
-  L.chunk_off = take(4ull * (N + L.ntiles + 1));
-  L.chunk_seg = take(4ull * (N + L.ntiles));
+  L.desc = take(16ull * (N + L.ntiles + 1));
+  L.tile_first_seg = take(4ull * (L.ntiles > 0 ? L.ntiles : 1));
   L.tile_last_seg = take(4ull * (L.ntiles > 0 ? L.ntiles : 1));
-  L.partial = take(4ull * 2 * (L.ntiles > 0 ? L.ntiles : 1) * g.D);
+  L.partial0 = take(4ull * 2 * (L.ntiles > 0 ? L.ntiles : 1) * g.D);
+  L.partial1 = take(4ull * 2 * (L.ntiles1 > 0 ? L.ntiles1 : 1) * g.D);
   L.ghist = take(4ull * kRadix * (L.nblk_sort > 0 ? L.nblk_sort : 1));
   L.digit_tot = take(4ull * kRadix);
-  L.rle_blk = take(8ull * (L.nblk_rle > 0 ? L.nblk_rle : 1));
+  L.rle_blk = take(16ull * (L.nblk_rle > 0 ? L.nblk_rle : 1));
   L.scalars = take(64);
   L.total = off;
   return L;
@@ -340,6 +342,8 @@ int emb_backward_unique_reduce(emb_ctx* ctx, const void* indices, const void* of
   if (!aligned(ws, 256)) return fail(EMB_E_INVAL, "ws must be 256-byte aligned");
   if (dY && !aligned(dY, 16)) return fail(EMB_E_INVAL, "dY must be 16-byte aligned");
   if (reduced_grad && !aligned(reduced_grad, 16)) return fail(EMB_E_INVAL, "reduced_grad must be 16-byte aligned");
+  if ((long long)B * ctx->g.T * ctx->g.D >= (1ll << 32))
+    return fail(EMB_E_INVAL, "dY must hold fewer than 2^32 elements (B*T*dim)");
   const WsLayout L = ws_layout(ctx->g, N, B);
   if (ws_bytes < L.total)
     return fail(EMB_E_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, L.total);

@@ -21,8 +21,12 @@ struct DevTable {
 constexpr int kMaxTables = 4096;
 
 // Segment chunking of the sorted lookups (see the reduce kernels): every
-// segment is cut at multiples of kChunk sorted positions.
+// segment is cut at multiples of kChunk sorted positions (level-0 tiles);
+// partial sums of segments longer than a tile are combined per level-1 tile
+// of kChunk * kL1Tiles positions, then per segment.
 constexpr int kChunk = 128;
+constexpr int kL1Tiles = 32;
+constexpr int kChunk1 = kChunk * kL1Tiles;  // 4096 positions
 
 // Radix sort / run-length tiles.
 constexpr int kSortThreads = 256;
@@ -64,16 +68,17 @@ struct WsLayout {
   size_t sorted_bag;            // int32 [N] bag of each sorted lookup
   size_t inv_len;               // fp32 [T*B] 1/L per bag (mean pooling)
   size_t seg_off;               // int32 [N+1]
-  size_t chunk_off;             // int32 [N + ntiles + 1]
-  size_t chunk_seg;             // int32 [N + ntiles]
-  size_t tile_last_seg;         // int32 [ntiles]
-  size_t partial;               // fp32 [2*ntiles][D]
+  size_t desc;                  // int32x4 [N + ntiles] chunk descriptors
+  size_t tile_first_seg;        // int32 [ntiles] segment of a tile's first position
+  size_t tile_last_seg;         // int32 [ntiles] segment of a tile's last position
+  size_t partial0;              // fp32 [2*ntiles][D]
+  size_t partial1;              // fp32 [2*ntiles1][D]
   size_t ghist;                 // uint32 [kRadix][nblk_sort]
   size_t digit_tot;             // uint32 [kRadix]
-  size_t rle_blk;               // uint32x2 [nblk_rle]
+  size_t rle_blk;               // uint32x4 [nblk_rle]
   size_t scalars;               // int32 [16]: [0] num_chunks
   size_t total;
-  int ntiles, nblk_sort, nblk_rle;
+  int ntiles, ntiles1, nblk_sort, nblk_rle;
 };
 WsLayout ws_layout(const Geom& g, long long N, int B);
 

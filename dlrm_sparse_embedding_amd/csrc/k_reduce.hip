@@ -31,23 +31,24 @@ namespace emb {
 
 struct RedArgs {
   const int32_t* sorted_bag;
-  const float* inv_len;  // null for sum pooling
+  const float* inv_len;  // 1/L per bag, mean pooling only
   const float* dY;
   const uint32_t* ukeys;
   const int32_t* seg_off;
-  const int32_t* chunk_off;
-  const int32_t* chunk_seg;
+  const int4* desc;
   const int32_t* num_chunks;
   const int32_t* num_unique;
+  const int32_t* tile_first_seg;
   const int32_t* tile_last_seg;
-  float* partial;
+  float* partial0;
+  float* partial1;
   float* grad;  // reduced gradient out (mode 0) or in (apply)
   const DevTable* tables;
   const uint32_t* row_off;
   int T, B, D, Dsl;
   uint32_t total_rows;
   int N;
-  int ntiles;
+  int ntiles, ntiles1;
   float lr, eps;
 };
 
@@ -95,7 +96,34 @@ __device__ __forceinline__ void row_update(char* wp, float* gp, const float* wv,
   store4<DT>(wp, nw);
 }
 
-template <int DT, int LPR, int MODE>
+// Applies the finished gradient of unique key `key` (segment `seg`): mode 0
+// stores it, modes 1/2 run the optimizer on the row.
+template <int DT, int MODE>
+__device__ __forceinline__ void finish_row(const RedArgs& a, const uint32_t* s_ro, uint32_t key,
+                                           int seg, int c0, const float* g) {
+  if constexpr (MODE == 0) {
+    f4 o = {g[0], g[1], g[2], g[3]};
+    *reinterpret_cast<f4*>(a.grad + (size_t)seg * a.D + c0) = o;
+  } else {
+    const int t = table_of(s_ro, a.T, key);
+    char* wp;
+    float* gp;
+    row_ptrs<DT>(a, t, key - s_ro[t], c0, &wp, &gp);
+    float wv[4], Gv[4] = {0.f, 0.f, 0.f, 0.f};
+    load4<DT>(wp, wv);
+    if constexpr (MODE == 2) load4<EMB_F32>(gp, Gv);
+    row_update<DT, MODE>(wp, gp, wv, Gv, g, a.lr, a.eps);
+  }
+}
+
+// Level-0 slot of the partial sum of segment [so, eo) in tile j: the chunk of
+// the segment in tile j starts at the tile start (slot 2j) unless the
+// segment itself starts inside tile j (slot 2j+1). Same rule at level 1.
+__device__ __forceinline__ int slot_of(int so, int j, int tile) {
+  return (j == so / tile && so % tile != 0) ? 2 * j + 1 : 2 * j;
+}
+
+template <int DT, int LPR, int MODE, bool MEAN>
 __global__ __launch_bounds__(256) void k_chunks(RedArgs a) {
   extern __shared__ uint32_t s_ro[];
   for (int i = threadIdx.x; i <= a.T; i += 256) s_ro[i] = a.row_off[i];
@@ -111,65 +139,51 @@ __global__ __launch_bounds__(256) void k_chunks(RedArgs a) {
   for (long long q = (long long)blockIdx.x * SGW + threadIdx.x / LPR; q < nch; q += nsg) {
     // every index below is clamped into its buffer: a wrong count or offset
     // can give a wrong result, never an access outside the workspace
-    const int cb = max(a.chunk_off[q], 0);
-    const int ce = min(a.chunk_off[q + 1], a.N);
-    const int u = a.chunk_seg[q];
-    if (u < 0 || u >= a.N) continue;
-    const int so = a.seg_off[u];
-    const int eo = a.seg_off[u + 1];
-    const uint32_t key = a.ukeys[u];
-    if (key >= a.total_rows) continue;  // lookups with out-of-range indices
+    const int4 d = a.desc[q];
+    const int cb = max(d.x, 0);
+    const int ce = min(d.y & 0x7fffffff, a.N);
+    const bool whole = d.y < 0;
+    const uint32_t key = (uint32_t)d.z;
+    const int seg = d.w;
+    if (key >= a.total_rows || seg < 0 || seg >= a.N) continue;  // out-of-range lookups
     const int t = table_of(s_ro, a.T, key);
-    const uint32_t r = key - s_ro[t];
-    const bool whole = cb == so && ce == eo;
 
     char* wp = nullptr;
     float* gp = nullptr;
     float wv[4] = {0.f, 0.f, 0.f, 0.f}, Gv[4] = {0.f, 0.f, 0.f, 0.f};
     if constexpr (MODE != 0) {
-      if (whole && act) {
-        row_ptrs<DT>(a, t, r, c0, &wp, &gp);
+      if (whole && act) {  // prefetch the row so its latency overlaps the dY loads
+        row_ptrs<DT>(a, t, key - s_ro[t], c0, &wp, &gp);
         load4<DT>(wp, wv);
         if constexpr (MODE == 2) load4<EMB_F32>(gp, Gv);
       }
     }
 
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    const float* dyt = a.dY + (size_t)t * a.D + c0;
+    // dY element offsets fit in 32 bits (dY is smaller than 16 GiB), so the
+    // loads use the uniform base + a 32-bit per-lane offset
+    const uint32_t dyt = (uint32_t)(t * a.D + c0);
     const int bagt = t * a.B;
     for (int i = cb; i < ce; i += U) {
       int bg[U];
 #pragma unroll
       for (int k = 0; k < U; ++k) bg[k] = i + k < ce ? a.sorted_bag[i + k] : -1;
       f4 v[U];
-      float sc[U];
 #pragma unroll
       for (int k = 0; k < U; ++k) {
         v[k] = f4{0.f, 0.f, 0.f, 0.f};
-        sc[k] = 1.f;
-        if (bg[k] >= 0) {
-          const unsigned b = (unsigned)(bg[k] - bagt);
-          if (b < (unsigned)a.B) {
-            if (act) v[k] = *reinterpret_cast<const f4*>(dyt + (size_t)b * dys);
-            if (a.inv_len) sc[k] = a.inv_len[bg[k]];
-          }
+        const unsigned b = (unsigned)(bg[k] - bagt);
+        if (bg[k] >= 0 && b < (unsigned)a.B && act) {
+          v[k] = *reinterpret_cast<const f4*>(a.dY + (b * (uint32_t)dys + dyt));
+          if constexpr (MEAN) v[k] *= a.inv_len[bg[k]];
         }
       }
 #pragma unroll
       for (int k = 0; k < U; ++k) {
-        if (bg[k] >= 0) {
-          if (a.inv_len) {
-            acc[0] += sc[k] * v[k].x;
-            acc[1] += sc[k] * v[k].y;
-            acc[2] += sc[k] * v[k].z;
-            acc[3] += sc[k] * v[k].w;
-          } else {
-            acc[0] += v[k].x;
-            acc[1] += v[k].y;
-            acc[2] += v[k].z;
-            acc[3] += v[k].w;
-          }
-        }
+        acc[0] += v[k].x;
+        acc[1] += v[k].y;
+        acc[2] += v[k].z;
+        acc[3] += v[k].w;
       }
     }
 
@@ -177,7 +191,7 @@ __global__ __launch_bounds__(256) void k_chunks(RedArgs a) {
     if (whole) {
       if constexpr (MODE == 0) {
         f4 o = {acc[0], acc[1], acc[2], acc[3]};
-        *reinterpret_cast<f4*>(a.grad + (size_t)u * a.D + c0) = o;
+        *reinterpret_cast<f4*>(a.grad + (size_t)seg * a.D + c0) = o;
       } else {
         row_update<DT, MODE>(wp, gp, wv, Gv, acc, a.lr, a.eps);
       }
@@ -185,106 +199,101 @@ __global__ __launch_bounds__(256) void k_chunks(RedArgs a) {
       const int j = cb / kChunk;
       const int slot = 2 * j + (cb == j * kChunk ? 0 : 1);
       f4 o = {acc[0], acc[1], acc[2], acc[3]};
-      *reinterpret_cast<f4*>(a.partial + (size_t)slot * a.D + c0) = o;
+      *reinterpret_cast<f4*>(a.partial0 + (size_t)slot * a.D + c0) = o;
     }
   }
 }
 
-// Long segments: the block finds, among 256 tiles, the segments that start in
-// a tile and run past its end (one per tile at most: the tile's last
-// segment), then reduces each one's partials cooperatively.
+// Sums `n` partial rows partial[slot(k)], k = 0..n-1, in k order, 8 in flight.
+template <typename SlotFn>
+__device__ __forceinline__ void sum_partials(const float* partial, int D, int c0, bool act, int n,
+                                             SlotFn slot, float* g) {
+  constexpr int U = 8;
+  g[0] = g[1] = g[2] = g[3] = 0.f;
+  for (int k0 = 0; k0 < n; k0 += U) {
+    f4 v[U];
+#pragma unroll
+    for (int m = 0; m < U; ++m) {
+      v[m] = f4{0.f, 0.f, 0.f, 0.f};
+      if (k0 + m < n && act) v[m] = *reinterpret_cast<const f4*>(partial + (size_t)slot(k0 + m) * D + c0);
+    }
+#pragma unroll
+    for (int m = 0; m < U; ++m) {
+      g[0] += v[m].x;
+      g[1] += v[m].y;
+      g[2] += v[m].z;
+      g[3] += v[m].w;
+    }
+  }
+}
+
+// Level 1: one subgroup per 4096-position tile J. The segments that cross a
+// level-1 boundary and touch J can only be J's first and last segments; for
+// each, the level-0 partials inside J are added (tile order) into its
+// level-1 partial of J.
+template <int LPR>
+__global__ __launch_bounds__(256) void k_level1(RedArgs a) {
+  constexpr int SGW = 256 / LPR;
+  const int J = blockIdx.x * SGW + threadIdx.x / LPR;
+  if (J >= a.ntiles1) return;
+  const int c0 = (threadIdx.x & (LPR - 1)) * 4;
+  const bool act = c0 < a.D;
+  const int jf = J * kL1Tiles;
+  const int jl = min(jf + kL1Tiles - 1, a.ntiles - 1);
+  const int cand[2] = {a.tile_first_seg[jf], a.tile_last_seg[jl]};
+  for (int c = 0; c < 2; ++c) {
+    const int u = cand[c];
+    if (c == 1 && u == cand[0]) break;
+    if (u < 0 || u >= a.N || a.ukeys[u] >= a.total_rows) continue;
+    const int so = a.seg_off[u];
+    const int eo = a.seg_off[u + 1];
+    if (so / kChunk1 == (eo - 1) / kChunk1) continue;  // stays inside one level-1 tile
+    const int lo = max(so, J * kChunk1);
+    const int hi = min(eo, (J + 1) * kChunk1);
+    if (lo >= hi) continue;
+    const int j0 = lo / kChunk;
+    const int n = (hi - 1) / kChunk - j0 + 1;
+    float g[4];
+    sum_partials(a.partial0, a.D, c0, act, n, [&](int k) { return slot_of(so, j0 + k, kChunk); }, g);
+    const int slot1 = slot_of(so, J, kChunk1);
+    if (act) {
+      f4 o = {g[0], g[1], g[2], g[3]};
+      *reinterpret_cast<f4*>(a.partial1 + (size_t)slot1 * a.D + c0) = o;
+    }
+  }
+}
+
+// Final combine: one subgroup per level-0 tile j. It owns the segment that
+// starts in tile j and runs past its end (at most one: the tile's last
+// segment); it adds the segment's level-0 partials, or its level-1 partials if
+// it crosses a level-1 boundary, in order, and applies the update.
 template <int DT, int LPR, int MODE>
 __global__ __launch_bounds__(256) void k_combine(RedArgs a) {
   constexpr int SGW = 256 / LPR;
-  extern __shared__ uint32_t smem[];
-  uint32_t* s_ro = smem;
-  const int ro_words = (a.T + 1 + 3) & ~3;
-  float* s_part = reinterpret_cast<float*>(smem + ro_words);  // [SGW][4*LPR]
-  int* s_list = reinterpret_cast<int*>(s_part + SGW * 4 * LPR);  // [256]
-  __shared__ int s_n;
+  extern __shared__ uint32_t s_ro[];
   for (int i = threadIdx.x; i <= a.T; i += 256) s_ro[i] = a.row_off[i];
-  const int sg = threadIdx.x / LPR;
-  const int lsg = threadIdx.x & (LPR - 1);
-  const int c0 = lsg * 4;
+  __syncthreads();
+  const int j = blockIdx.x * SGW + threadIdx.x / LPR;
+  if (j >= a.ntiles) return;
+  const int c0 = (threadIdx.x & (LPR - 1)) * 4;
   const bool act = c0 < a.D;
-  for (long long tb = (long long)blockIdx.x * 256; tb < a.ntiles; tb += (long long)gridDim.x * 256) {
-    if (threadIdx.x == 0) s_n = 0;
-    __syncthreads();
-    const long long j = tb + threadIdx.x;
-    if (j < a.ntiles && (unsigned)a.tile_last_seg[j] < (unsigned)a.N) {
-      const int u = a.tile_last_seg[j];
-      const long long so = a.seg_off[u];
-      const long long eo = a.seg_off[u + 1];
-      if (so >= j * kChunk && eo > (j + 1) * kChunk && a.ukeys[u] < a.total_rows) {
-        const int p = atomicAdd(&s_n, 1);
-        s_list[p] = u;
-      }
-    }
-    __syncthreads();
-    const int n = s_n;
-    for (int e = 0; e < n; ++e) {
-      const int u = s_list[e];
-      const int so = a.seg_off[u];
-      const int eo = a.seg_off[u + 1];
-      const int j0 = so / kChunk;
-      const int np = (eo - 1) / kChunk - j0 + 1;
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
-      constexpr int U = 4;
-      for (int k0 = sg; k0 < np; k0 += SGW * U) {
-        f4 v[U];
-#pragma unroll
-        for (int m = 0; m < U; ++m) {
-          const int k = k0 + m * SGW;
-          v[m] = f4{0.f, 0.f, 0.f, 0.f};
-          if (k < np && act) {
-            const int slot = k == 0 ? (so == j0 * kChunk ? 2 * j0 : 2 * j0 + 1) : 2 * (j0 + k);
-            v[m] = *reinterpret_cast<const f4*>(a.partial + (size_t)slot * a.D + c0);
-          }
-        }
-#pragma unroll
-        for (int m = 0; m < U; ++m) {
-          acc[0] += v[m].x;
-          acc[1] += v[m].y;
-          acc[2] += v[m].z;
-          acc[3] += v[m].w;
-        }
-      }
-      if (act) {
-        float* sp = s_part + (size_t)sg * 4 * LPR + c0;
-        sp[0] = acc[0];
-        sp[1] = acc[1];
-        sp[2] = acc[2];
-        sp[3] = acc[3];
-      }
-      __syncthreads();
-      if (sg == 0 && act) {
-        float g[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int k = 0; k < SGW; ++k) {
-          const float* sp = s_part + (size_t)k * 4 * LPR + c0;
-          g[0] += sp[0];
-          g[1] += sp[1];
-          g[2] += sp[2];
-          g[3] += sp[3];
-        }
-        const uint32_t key = a.ukeys[u];
-        if constexpr (MODE == 0) {
-          f4 o = {g[0], g[1], g[2], g[3]};
-          *reinterpret_cast<f4*>(a.grad + (size_t)u * a.D + c0) = o;
-        } else {
-          const int t = table_of(s_ro, a.T, key);
-          char* wp;
-          float* gp;
-          row_ptrs<DT>(a, t, key - s_ro[t], c0, &wp, &gp);
-          float wv[4], Gv[4] = {0.f, 0.f, 0.f, 0.f};
-          load4<DT>(wp, wv);
-          if constexpr (MODE == 2) load4<EMB_F32>(gp, Gv);
-          row_update<DT, MODE>(wp, gp, wv, Gv, g, a.lr, a.eps);
-        }
-      }
-      __syncthreads();
-    }
-    __syncthreads();
+  const int u = a.tile_last_seg[j];
+  if (u < 0 || u >= a.N) return;
+  const int so = a.seg_off[u];
+  const int eo = a.seg_off[u + 1];
+  if (so < j * kChunk || eo <= (j + 1) * kChunk) return;  // not the owner
+  const uint32_t key = a.ukeys[u];
+  if (key >= a.total_rows) return;
+  float g[4];
+  if (so / kChunk1 == (eo - 1) / kChunk1) {
+    const int n = (eo - 1) / kChunk - j + 1;
+    sum_partials(a.partial0, a.D, c0, act, n, [&](int k) { return slot_of(so, j + k, kChunk); }, g);
+  } else {
+    const int J0 = so / kChunk1;
+    const int n = (eo - 1) / kChunk1 - J0 + 1;
+    sum_partials(a.partial1, a.D, c0, act, n, [&](int k) { return slot_of(so, J0 + k, kChunk1); }, g);
   }
+  if (act) finish_row<DT, MODE>(a, s_ro, key, u, c0, g);
 }
 
 // Update from a materialised reduced gradient (grad[u] for u < U).
@@ -302,15 +311,9 @@ __global__ __launch_bounds__(256) void k_apply(RedArgs a) {
        u += (long long)gridDim.x * SGW) {
     const uint32_t key = a.ukeys[u];
     if (key >= a.total_rows) continue;
-    const int t = table_of(s_ro, a.T, key);
-    char* wp;
-    float* gp;
-    row_ptrs<DT>(a, t, key - s_ro[t], c0, &wp, &gp);
-    float wv[4], Gv[4] = {0.f, 0.f, 0.f, 0.f}, g[4];
-    load4<DT>(wp, wv);
-    if constexpr (MODE == 2) load4<EMB_F32>(gp, Gv);
+    float g[4];
     load4<EMB_F32>(a.grad + (size_t)u * a.D + c0, g);
-    row_update<DT, MODE>(wp, gp, wv, Gv, g, a.lr, a.eps);
+    finish_row<DT, MODE>(a, s_ro, key, (int)u, c0, g);
   }
 }
 
@@ -326,12 +329,13 @@ static RedArgs make_args(const Geom& g, const DevCtx& dc, int N, const WsLayout&
   a.dY = nullptr;
   a.ukeys = ukeys;
   a.seg_off = reinterpret_cast<const int32_t*>(ws + L.seg_off);
-  a.chunk_off = reinterpret_cast<const int32_t*>(ws + L.chunk_off);
-  a.chunk_seg = reinterpret_cast<const int32_t*>(ws + L.chunk_seg);
+  a.desc = reinterpret_cast<const int4*>(ws + L.desc);
   a.num_chunks = reinterpret_cast<const int32_t*>(ws + L.scalars);
   a.num_unique = nullptr;
+  a.tile_first_seg = reinterpret_cast<const int32_t*>(ws + L.tile_first_seg);
   a.tile_last_seg = reinterpret_cast<const int32_t*>(ws + L.tile_last_seg);
-  a.partial = const_cast<float*>(reinterpret_cast<const float*>(ws + L.partial));
+  a.partial0 = const_cast<float*>(reinterpret_cast<const float*>(ws + L.partial0));
+  a.partial1 = const_cast<float*>(reinterpret_cast<const float*>(ws + L.partial1));
   a.grad = nullptr;
   a.tables = dc.tables;
   a.row_off = dc.row_off;
@@ -342,6 +346,7 @@ static RedArgs make_args(const Geom& g, const DevCtx& dc, int N, const WsLayout&
   a.total_rows = g.total_rows;
   a.N = N;
   a.ntiles = L.ntiles;
+  a.ntiles1 = L.ntiles1;
   a.lr = lr;
   a.eps = eps;
   return a;
@@ -352,31 +357,61 @@ static int lpr_b(const Geom& g) {
   return l < 2 ? 2 : l;
 }
 
-#define RED_KERNEL_SWITCH(KERNEL, DT, MODE, GRID, SMEM)                                 \
-  switch (lpr) {                                                                        \
-    case 2: hipLaunchKernelGGL((KERNEL<DT, 2, MODE>), GRID, dim3(256), SMEM, st, a); break;   \
-    case 4: hipLaunchKernelGGL((KERNEL<DT, 4, MODE>), GRID, dim3(256), SMEM, st, a); break;   \
-    case 8: hipLaunchKernelGGL((KERNEL<DT, 8, MODE>), GRID, dim3(256), SMEM, st, a); break;   \
-    case 16: hipLaunchKernelGGL((KERNEL<DT, 16, MODE>), GRID, dim3(256), SMEM, st, a); break; \
-    case 32: hipLaunchKernelGGL((KERNEL<DT, 32, MODE>), GRID, dim3(256), SMEM, st, a); break; \
-    default: hipLaunchKernelGGL((KERNEL<DT, 64, MODE>), GRID, dim3(256), SMEM, st, a); break; \
+#define LPR_SWITCH(LAUNCH)          \
+  switch (lpr) {                    \
+    case 2: LAUNCH(2) break;        \
+    case 4: LAUNCH(4) break;        \
+    case 8: LAUNCH(8) break;        \
+    case 16: LAUNCH(16) break;      \
+    case 32: LAUNCH(32) break;      \
+    default: LAUNCH(64) break;      \
   }
 
-#define RED_MODE_SWITCH(KERNEL, DT, GRID, SMEM)             \
-  if (mode == 0) {                                          \
-    RED_KERNEL_SWITCH(KERNEL, DT, 0, GRID, SMEM)            \
-  } else if (mode == 1) {                                   \
-    RED_KERNEL_SWITCH(KERNEL, DT, 1, GRID, SMEM)            \
-  } else {                                                  \
-    RED_KERNEL_SWITCH(KERNEL, DT, 2, GRID, SMEM)            \
+template <int DT, int MODE, bool MEAN>
+static void launch_chunks_t(int lpr, int grid, size_t smem, hipStream_t st, const RedArgs& a) {
+#define L_CH(P) hipLaunchKernelGGL((k_chunks<DT, P, MODE, MEAN>), dim3(grid), dim3(256), smem, st, a);
+  LPR_SWITCH(L_CH)
+#undef L_CH
+}
+
+template <int DT, int MODE>
+static void launch_combine_t(int lpr, int grid, size_t smem, hipStream_t st, const RedArgs& a) {
+#define L_CO(P) hipLaunchKernelGGL((k_combine<DT, P, MODE>), dim3(grid), dim3(256), smem, st, a);
+  LPR_SWITCH(L_CO)
+#undef L_CO
+}
+
+template <int DT, int MODE>
+static void launch_apply_t(int lpr, int grid, size_t smem, hipStream_t st, const RedArgs& a) {
+#define L_AP(P) hipLaunchKernelGGL((k_apply<DT, P, MODE>), dim3(grid), dim3(256), smem, st, a);
+  LPR_SWITCH(L_AP)
+#undef L_AP
+}
+
+#define DISPATCH_DT_MODE(FN, ...)                                   \
+  switch (g.dtype) {                                                \
+    case EMB_F32:                                                   \
+      if (mode == 0) FN<EMB_F32, 0>(__VA_ARGS__);                   \
+      else if (mode == 1) FN<EMB_F32, 1>(__VA_ARGS__);              \
+      else FN<EMB_F32, 2>(__VA_ARGS__);                             \
+      break;                                                        \
+    case EMB_BF16:                                                  \
+      if (mode == 0) FN<EMB_BF16, 0>(__VA_ARGS__);                  \
+      else if (mode == 1) FN<EMB_BF16, 1>(__VA_ARGS__);             \
+      else FN<EMB_BF16, 2>(__VA_ARGS__);                            \
+      break;                                                        \
+    default:                                                        \
+      if (mode == 0) FN<EMB_F16, 0>(__VA_ARGS__);                   \
+      else if (mode == 1) FN<EMB_F16, 1>(__VA_ARGS__);              \
+      else FN<EMB_F16, 2>(__VA_ARGS__);                             \
+      break;                                                        \
   }
 
-#define RED_DISPATCH(KERNEL, GRID, SMEM)                    \
-  switch (g.dtype) {                                        \
-    case EMB_F32: RED_MODE_SWITCH(KERNEL, EMB_F32, GRID, SMEM) break;   \
-    case EMB_BF16: RED_MODE_SWITCH(KERNEL, EMB_BF16, GRID, SMEM) break; \
-    default: RED_MODE_SWITCH(KERNEL, EMB_F16, GRID, SMEM) break;        \
-  }
+template <int DT, int MODE>
+static void launch_chunks_pool(bool mean, int lpr, int grid, size_t smem, hipStream_t st, const RedArgs& a) {
+  if (mean) launch_chunks_t<DT, MODE, true>(lpr, grid, smem, st, a);
+  else launch_chunks_t<DT, MODE, false>(lpr, grid, smem, st, a);
+}
 
 hipError_t launch_reduce(const Geom& g, const DevCtx& dc, int mode, int N, int B, int pool,
                          const float* dY, const WsLayout& L, const char* ws,
@@ -385,17 +420,18 @@ hipError_t launch_reduce(const Geom& g, const DevCtx& dc, int mode, int N, int B
   RedArgs a = make_args(g, dc, N, L, ws, unique_keys, lr, eps);
   a.B = B;
   a.dY = dY;
-  a.inv_len = pool == EMB_POOL_MEAN ? reinterpret_cast<const float*>(ws + L.inv_len) : nullptr;
+  const bool mean = pool == EMB_POOL_MEAN;
+  a.inv_len = mean ? reinterpret_cast<const float*>(ws + L.inv_len) : nullptr;
   a.num_unique = num_unique;
   a.grad = grad_out;
   const int lpr = lpr_b(g);
   const int sgw = 256 / lpr;
   // chunks <= N + ntiles; the loop is grid-strided over the device count
   const long long upper = (long long)N + L.ntiles;
-  long long want = (upper + sgw - 1) / sgw;
+  const long long want = (upper + sgw - 1) / sgw;
   const int grid = (int)(want < 16384 ? (want > 0 ? want : 1) : 16384);
   const size_t smem = (size_t)(g.T + 1) * 4;
-  RED_DISPATCH(k_chunks, dim3(grid), smem)
+  DISPATCH_DT_MODE(launch_chunks_pool, mean, lpr, grid, smem, st, a)
   return hipGetLastError();
 }
 
@@ -406,34 +442,34 @@ hipError_t launch_combine(const Geom& g, const DevCtx& dc, int mode, int N, cons
   a.grad = grad_out;
   const int lpr = lpr_b(g);
   const int sgw = 256 / lpr;
-  const int want = ceil_div(L.ntiles, 256);
-  const int grid = want < 4096 ? (want > 0 ? want : 1) : 4096;
-  const size_t smem = (size_t)((g.T + 1 + 3) & ~3) * 4 + (size_t)sgw * 4 * lpr * 4 + 256 * 4;
-  RED_DISPATCH(k_combine, dim3(grid), smem)
+  if (L.ntiles1 > 1) {
+    const int grid1 = ceil_div(L.ntiles1, sgw);
+#define L_L1(P) hipLaunchKernelGGL((k_level1<P>), dim3(grid1), dim3(256), 0, st, a);
+    LPR_SWITCH(L_L1)
+#undef L_L1
+  }
+  const int grid = ceil_div(L.ntiles, sgw);
+  const size_t smem = (size_t)(g.T + 1) * 4;
+  if (grid > 0) {
+    DISPATCH_DT_MODE(launch_combine_t, lpr, grid, smem, st, a)
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_apply(const Geom& g, const DevCtx& dc, int opt, int N,
                         const uint32_t* unique_keys, const int32_t* num_unique,
                         const float* grad_in, float lr, float eps, hipStream_t st) {
-  RedArgs a;
-  a.sorted_bag = nullptr;
-  a.inv_len = nullptr;
-  a.dY = nullptr;
+  RedArgs a{};
   a.ukeys = unique_keys;
-  a.seg_off = a.chunk_off = a.chunk_seg = a.num_chunks = a.tile_last_seg = nullptr;
   a.num_unique = num_unique;
-  a.partial = nullptr;
   a.grad = const_cast<float*>(grad_in);
   a.tables = dc.tables;
   a.row_off = dc.row_off;
   a.T = g.T;
-  a.B = 0;
   a.D = g.D;
   a.Dsl = g.Dsl;
   a.total_rows = g.total_rows;
   a.N = N;
-  a.ntiles = 0;
   a.lr = lr;
   a.eps = eps;
   const int lpr = lpr_b(g);
@@ -442,19 +478,7 @@ hipError_t launch_apply(const Geom& g, const DevCtx& dc, int opt, int N,
   const int grid = (int)(want < 16384 ? (want > 0 ? want : 1) : 16384);
   const size_t smem = (size_t)(g.T + 1) * 4;
   const int mode = opt;
-  if (mode == 1) {
-    switch (g.dtype) {
-      case EMB_F32: RED_KERNEL_SWITCH(k_apply, EMB_F32, 1, dim3(grid), smem) break;
-      case EMB_BF16: RED_KERNEL_SWITCH(k_apply, EMB_BF16, 1, dim3(grid), smem) break;
-      default: RED_KERNEL_SWITCH(k_apply, EMB_F16, 1, dim3(grid), smem) break;
-    }
-  } else {
-    switch (g.dtype) {
-      case EMB_F32: RED_KERNEL_SWITCH(k_apply, EMB_F32, 2, dim3(grid), smem) break;
-      case EMB_BF16: RED_KERNEL_SWITCH(k_apply, EMB_BF16, 2, dim3(grid), smem) break;
-      default: RED_KERNEL_SWITCH(k_apply, EMB_F16, 2, dim3(grid), smem) break;
-    }
-  }
+  DISPATCH_DT_MODE(launch_apply_t, lpr, grid, smem, st, a)
   return hipGetLastError();
 }
 

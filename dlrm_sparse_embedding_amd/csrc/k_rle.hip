@@ -7,19 +7,38 @@
 // start and at every multiple of kChunk sorted positions, so every chunk lies
 // in one segment and in one kChunk-tile; a segment longer than a tile (a
 // Zipf-hot key) is thereby split into pieces that can be reduced in parallel
-// and combined in a fixed order. Both counters are scanned in one pass
-// (count per tile, scan of tile counts, write).
+// and combined in a fixed order. Three running quantities are scanned in one
+// pass (count per tile, scan of tile counts, write): the number of segment
+// starts, the number of chunk starts, and the position of the latest segment
+// start (a max-scan). With them, the last position of every chunk writes the
+// chunk's whole descriptor -- start, end, key, segment, and whether it is the
+// entire segment -- so the reduce kernel needs a single 16-byte load per
+// chunk.
 #include "emb_device.h"
 
 namespace emb {
 
 __device__ __forceinline__ uint32_t key_of(uint64_t x) { return (uint32_t)(x >> 32); }
 
+// Inclusive max over the 64 lanes of a wave, lane order.
+__device__ __forceinline__ uint32_t wave_incl_max(uint32_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = __shfl_up(v, d, 64);
+    if (lane >= d) v = max(v, y);
+  }
+  return v;
+}
+
+// Per tile: segment starts, chunk starts, and 1 + the last segment start in
+// the tile (0 if none).
 __global__ __launch_bounds__(256) void k_rle_count(const uint64_t* __restrict__ sorted, int N,
-                                                   u2* __restrict__ blk_out) {
+                                                   u4* __restrict__ blk_out) {
   __shared__ uint32_t lds[8];
+  __shared__ uint32_t s_max[4];
   const long long base = (long long)blockIdx.x * kSortTile;
-  uint32_t cs = 0, cc = 0;
+  uint32_t cs = 0, cc = 0, ms = 0;
 #pragma unroll
   for (int k = 0; k < kSortIPT; ++k) {
     const long long i = base + k * 256 + threadIdx.x;
@@ -28,39 +47,56 @@ __global__ __launch_bounds__(256) void k_rle_count(const uint64_t* __restrict__ 
       const bool fc = fs || (i % kChunk) == 0;
       cs += fs;
       cc += fc;
+      if (fs) ms = max(ms, (uint32_t)i + 1u);
     }
   }
   uint32_t ts, tc;
   block_excl_scan_256(cs, lds, &ts);
   block_excl_scan_256(cc, lds, &tc);
-  if (threadIdx.x == 0) blk_out[blockIdx.x] = u2{ts, tc};
+  const uint32_t wm = wave_incl_max(ms);
+  if ((threadIdx.x & 63) == 63) s_max[threadIdx.x >> 6] = wm;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    blk_out[blockIdx.x] = u4{ts, tc, max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3])), 0u};
 }
 
-// One block: exclusive scan of the per-tile (segments, chunks) counts in
-// place; totals to *num_unique and num_chunks.
-__global__ __launch_bounds__(256) void k_rle_scan(u2* __restrict__ blk, int nblk,
+// One block: exclusive scans of the per-tile counts (sum) and of the last
+// segment start (max), in place; totals to *num_unique and num_chunks.
+__global__ __launch_bounds__(256) void k_rle_scan(u4* __restrict__ blk, int nblk,
                                                   int32_t* __restrict__ num_unique,
                                                   int32_t* __restrict__ num_chunks) {
   __shared__ uint32_t lds[8];
+  __shared__ uint32_t s_max[4];
   const int per = (nblk + 255) / 256;
   const int b0 = threadIdx.x * per;
-  uint32_t ss = 0, sc = 0;
+  uint32_t ss = 0, sc = 0, sm = 0;
   for (int i = 0; i < per; ++i) {
     if (b0 + i < nblk) {
-      const u2 v = blk[b0 + i];
+      const u4 v = blk[b0 + i];
       ss += v.x;
       sc += v.y;
+      sm = max(sm, v.z);
     }
   }
   uint32_t ts, tc;
   uint32_t ps = block_excl_scan_256(ss, lds, &ts);
   uint32_t pc = block_excl_scan_256(sc, lds, &tc);
+  // exclusive max over threads (thread order = tile order)
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const uint32_t incl = wave_incl_max(sm);
+  uint32_t pm = __shfl_up(incl, 1, 64);
+  if (lane == 0) pm = 0;
+  if (lane == 63) s_max[wave] = incl;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) pm = max(pm, s_max[w]);
   for (int i = 0; i < per; ++i) {
     if (b0 + i < nblk) {
-      const u2 v = blk[b0 + i];
-      blk[b0 + i] = u2{ps, pc};
+      const u4 v = blk[b0 + i];
+      blk[b0 + i] = u4{ps, pc, pm, 0u};
       ps += v.x;
       pc += v.y;
+      pm = max(pm, v.z);
     }
   }
   if (threadIdx.x == 0) {
@@ -71,37 +107,40 @@ __global__ __launch_bounds__(256) void k_rle_scan(u2* __restrict__ blk, int nblk
 
 struct RleArgs {
   const uint64_t* sorted;
-  const u2* blk;
+  const u4* blk;
   const int32_t* bag_of_pos;
   uint32_t* unique_keys;
   int32_t* inverse;
   int32_t* seg_off;
-  int32_t* chunk_off;
-  int32_t* chunk_seg;
+  int4* desc;
+  int32_t* tile_first_seg;
   int32_t* tile_last_seg;
   int32_t* sorted_bag;
   int N;
 };
 
 __global__ __launch_bounds__(256) void k_rle_write(RleArgs a) {
-  __shared__ uint32_t s_ws[4], s_wc[4];
+  __shared__ uint32_t s_ws[4], s_wc[4], s_wm[4];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const long long base = (long long)blockIdx.x * kSortTile + wave * (64 * kSortIPT);
   const uint64_t le = lanemask_lt() | (1ull << lane);
   uint64_t item[kSortIPT];
-  uint32_t is[kSortIPT], ic[kSortIPT];
-  uint32_t fl = 0;  // bit k: segment start, bit 16+k: chunk start
-  uint32_t run_s = 0, run_c = 0;
+  uint32_t is[kSortIPT], ic[kSortIPT], im[kSortIPT];
+  uint32_t fl = 0;  // bit k: segment start, 8+k: chunk start, 16+k: segment end, 24+k: chunk end
+  uint32_t run_s = 0, run_c = 0, run_m = 0;
 #pragma unroll
   for (int k = 0; k < kSortIPT; ++k) {
     const long long i = base + k * 64 + lane;
-    bool fs = false, fc = false;
+    bool fs = false, fc = false, se = false, ce = false;
     item[k] = 0;
     if (i < a.N) {
       item[k] = a.sorted[i];
-      fs = i == 0 || key_of(item[k]) != key_of(a.sorted[i - 1]);
+      const uint32_t key = key_of(item[k]);
+      fs = i == 0 || key != key_of(a.sorted[i - 1]);
       fc = fs || (i % kChunk) == 0;
+      se = i + 1 == a.N || key != key_of(a.sorted[i + 1]);
+      ce = se || ((i + 1) % kChunk) == 0;
     }
     const uint64_t bs = __ballot(fs);
     const uint64_t bc = __ballot(fc);
@@ -109,18 +148,24 @@ __global__ __launch_bounds__(256) void k_rle_write(RleArgs a) {
     ic[k] = run_c + (uint32_t)__popcll(bc & le);
     run_s += (uint32_t)__popcll(bs);
     run_c += (uint32_t)__popcll(bc);
-    fl |= (fs ? 1u << k : 0u) | (fc ? 1u << (16 + k) : 0u);
+    const uint32_t m = wave_incl_max(fs ? (uint32_t)i + 1u : 0u);
+    im[k] = max(run_m, m);
+    run_m = max(run_m, (uint32_t)__shfl(m, 63, 64));
+    fl |= (fs ? 1u << k : 0u) | (fc ? 1u << (8 + k) : 0u) | (se ? 1u << (16 + k) : 0u) |
+          (ce ? 1u << (24 + k) : 0u);
   }
   if (lane == 0) {
     s_ws[wave] = run_s;
     s_wc[wave] = run_c;
+    s_wm[wave] = run_m;
   }
   __syncthreads();
-  const u2 bp = a.blk[blockIdx.x];
-  uint32_t ps = bp.x, pc = bp.y;
+  const u4 bp = a.blk[blockIdx.x];
+  uint32_t ps = bp.x, pc = bp.y, pm = bp.z;
   for (int w = 0; w < wave; ++w) {
     ps += s_ws[w];
     pc += s_wc[w];
+    pm = max(pm, s_wm[w]);
   }
 #pragma unroll
   for (int k = 0; k < kSortIPT; ++k) {
@@ -128,23 +173,28 @@ __global__ __launch_bounds__(256) void k_rle_write(RleArgs a) {
     if (i >= a.N) continue;
     const int32_t seg = (int32_t)(ps + is[k] - 1);
     const int32_t chk = (int32_t)(pc + ic[k] - 1);
+    const int32_t seg_start = (int32_t)max(pm, im[k]) - 1;
+    const uint32_t key = key_of(item[k]);
     const uint32_t pos = (uint32_t)item[k];
     if (pos < (uint32_t)a.N) {
       a.inverse[pos] = seg;
       a.sorted_bag[i] = a.bag_of_pos[pos];
     }
     if (fl & (1u << k)) {
-      a.unique_keys[seg] = key_of(item[k]);
+      a.unique_keys[seg] = key;
       a.seg_off[seg] = (int32_t)i;
     }
-    if (fl & (1u << (16 + k))) {
-      a.chunk_off[chk] = (int32_t)i;
-      a.chunk_seg[chk] = seg;
-    }
+    if ((i % kChunk) == 0) a.tile_first_seg[i / kChunk] = seg;
     if ((i % kChunk) == kChunk - 1 || i == a.N - 1) a.tile_last_seg[i / kChunk] = seg;
-    if (i == a.N - 1) {
-      a.seg_off[seg + 1] = a.N;
-      a.chunk_off[chk + 1] = a.N;
+    if (i == a.N - 1) a.seg_off[seg + 1] = a.N;
+    if (fl & (1u << (24 + k))) {
+      // last position of chunk `chk`: it starts at the later of its segment's
+      // start and its tile's start; it is the whole segment when it starts at
+      // the segment start and ends at the segment end
+      const int32_t tile0 = (int32_t)((i / kChunk) * kChunk);
+      const int32_t cb = seg_start > tile0 ? seg_start : tile0;
+      const bool whole = cb == seg_start && (fl & (1u << (16 + k)));
+      a.desc[chk] = int4{cb, (int32_t)((uint32_t)(i + 1) | (whole ? 0x80000000u : 0u)), (int32_t)key, seg};
     }
   }
 }
@@ -166,7 +216,7 @@ __global__ void k_set_empty(int32_t* num_unique, int32_t* num_chunks) {
 
 hipError_t launch_rle(const uint64_t* sorted, int N, const WsLayout& L, char* ws, const RleOut& o,
                       hipStream_t st) {
-  u2* blk = reinterpret_cast<u2*>(ws + L.rle_blk);
+  u4* blk = reinterpret_cast<u4*>(ws + L.rle_blk);
   int32_t* num_chunks = reinterpret_cast<int32_t*>(ws + L.scalars);
   const int nblk = L.nblk_rle;
   hipLaunchKernelGGL(k_rle_count, dim3(nblk), dim3(256), 0, st, sorted, N, blk);
@@ -178,8 +228,8 @@ hipError_t launch_rle(const uint64_t* sorted, int N, const WsLayout& L, char* ws
   a.unique_keys = o.unique_keys;
   a.inverse = o.inverse;
   a.seg_off = reinterpret_cast<int32_t*>(ws + L.seg_off);
-  a.chunk_off = reinterpret_cast<int32_t*>(ws + L.chunk_off);
-  a.chunk_seg = reinterpret_cast<int32_t*>(ws + L.chunk_seg);
+  a.desc = reinterpret_cast<int4*>(ws + L.desc);
+  a.tile_first_seg = reinterpret_cast<int32_t*>(ws + L.tile_first_seg);
   a.tile_last_seg = reinterpret_cast<int32_t*>(ws + L.tile_last_seg);
   a.sorted_bag = reinterpret_cast<int32_t*>(ws + L.sorted_bag);
   a.N = N;

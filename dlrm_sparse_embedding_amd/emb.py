@@ -19,7 +19,8 @@ from dataclasses import dataclass
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libemb.so")
+# EMB_LIBRARY may name another build of the same library (e.g. a tuning variant)
+LIB_PATH = os.environ.get("EMB_LIBRARY") or os.path.join(_PKG, "libemb.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "emb.h")
 
 EMB_OK = 0
