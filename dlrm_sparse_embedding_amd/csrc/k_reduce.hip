@@ -36,6 +36,7 @@ struct RedArgs {
   const uint32_t* ukeys;
   const int32_t* seg_off;
   const int4* desc;
+  const int32_t* chunk_seg;
   const int32_t* num_chunks;
   const int32_t* num_unique;
   const int32_t* tile_first_seg;
@@ -124,7 +125,7 @@ __device__ __forceinline__ int slot_of(int so, int j, int tile) {
 }
 
 template <int DT, int LPR, int MODE, bool MEAN>
-__global__ __launch_bounds__(256) void k_chunks(RedArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_chunks(RedArgs a) {
   extern __shared__ uint32_t s_ro[];
   for (int i = threadIdx.x; i <= a.T; i += 256) s_ro[i] = a.row_off[i];
   __syncthreads();
@@ -133,19 +134,23 @@ __global__ __launch_bounds__(256) void k_chunks(RedArgs a) {
   const int lsg = threadIdx.x & (LPR - 1);
   const int c0 = lsg * 4;
   const bool act = c0 < a.D;
-  const size_t dys = (size_t)a.T * a.D;
-  const long long nsg = (long long)gridDim.x * SGW;
+  const uint32_t dys = (uint32_t)(a.T * a.D);
+  const int nsg = gridDim.x * SGW;
   const int nch = min(*a.num_chunks, a.N + a.ntiles);
-  for (long long q = (long long)blockIdx.x * SGW + threadIdx.x / LPR; q < nch; q += nsg) {
+  int q = blockIdx.x * SGW + threadIdx.x / LPR;
+  // the next descriptor is loaded while the current chunk is processed
+  int4 d = q < nch ? a.desc[q] : int4{0, 0, -1, -1};
+  for (; q < nch; q += nsg) {
+    const int4 dn = q + nsg < nch ? a.desc[q + nsg] : int4{0, 0, -1, -1};
     // every index below is clamped into its buffer: a wrong count or offset
     // can give a wrong result, never an access outside the workspace
-    const int4 d = a.desc[q];
     const int cb = max(d.x, 0);
     const int ce = min(d.y & 0x7fffffff, a.N);
     const bool whole = d.y < 0;
     const uint32_t key = (uint32_t)d.z;
-    const int seg = d.w;
-    if (key >= a.total_rows || seg < 0 || seg >= a.N) continue;  // out-of-range lookups
+    const int bag0 = d.w;
+    d = dn;
+    if (key >= a.total_rows) continue;  // lookups with out-of-range indices
     const int t = table_of(s_ro, a.T, key);
 
     char* wp = nullptr;
@@ -160,21 +165,21 @@ __global__ __launch_bounds__(256) void k_chunks(RedArgs a) {
     }
 
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    // dY element offsets fit in 32 bits (dY is smaller than 16 GiB), so the
+    // dY element offsets fit in 32 bits (fewer than 2^32 elements), so the
     // loads use the uniform base + a 32-bit per-lane offset
     const uint32_t dyt = (uint32_t)(t * a.D + c0);
     const int bagt = t * a.B;
     for (int i = cb; i < ce; i += U) {
       int bg[U];
 #pragma unroll
-      for (int k = 0; k < U; ++k) bg[k] = i + k < ce ? a.sorted_bag[i + k] : -1;
+      for (int k = 0; k < U; ++k) bg[k] = i + k < ce ? (i + k == cb ? bag0 : a.sorted_bag[i + k]) : -1;
       f4 v[U];
 #pragma unroll
       for (int k = 0; k < U; ++k) {
         v[k] = f4{0.f, 0.f, 0.f, 0.f};
         const unsigned b = (unsigned)(bg[k] - bagt);
         if (bg[k] >= 0 && b < (unsigned)a.B && act) {
-          v[k] = *reinterpret_cast<const f4*>(a.dY + (b * (uint32_t)dys + dyt));
+          v[k] = *reinterpret_cast<const f4*>(a.dY + (b * dys + dyt));
           if constexpr (MEAN) v[k] *= a.inv_len[bg[k]];
         }
       }
@@ -190,8 +195,11 @@ __global__ __launch_bounds__(256) void k_chunks(RedArgs a) {
     if (!act) continue;
     if (whole) {
       if constexpr (MODE == 0) {
-        f4 o = {acc[0], acc[1], acc[2], acc[3]};
-        *reinterpret_cast<f4*>(a.grad + (size_t)seg * a.D + c0) = o;
+        const int seg = a.chunk_seg[q];
+        if ((unsigned)seg < (unsigned)a.N) {
+          f4 o = {acc[0], acc[1], acc[2], acc[3]};
+          *reinterpret_cast<f4*>(a.grad + (size_t)seg * a.D + c0) = o;
+        }
       } else {
         row_update<DT, MODE>(wp, gp, wv, Gv, acc, a.lr, a.eps);
       }
@@ -330,6 +338,7 @@ static RedArgs make_args(const Geom& g, const DevCtx& dc, int N, const WsLayout&
   a.ukeys = ukeys;
   a.seg_off = reinterpret_cast<const int32_t*>(ws + L.seg_off);
   a.desc = reinterpret_cast<const int4*>(ws + L.desc);
+  a.chunk_seg = reinterpret_cast<const int32_t*>(ws + L.chunk_seg);
   a.num_chunks = reinterpret_cast<const int32_t*>(ws + L.scalars);
   a.num_unique = nullptr;
   a.tile_first_seg = reinterpret_cast<const int32_t*>(ws + L.tile_first_seg);

@@ -113,6 +113,7 @@ struct RleArgs {
   int32_t* inverse;
   int32_t* seg_off;
   int4* desc;
+  int32_t* chunk_seg;
   int32_t* tile_first_seg;
   int32_t* tile_last_seg;
   int32_t* sorted_bag;
@@ -167,6 +168,30 @@ __global__ __launch_bounds__(256) void k_rle_write(RleArgs a) {
     pc += s_wc[w];
     pm = max(pm, s_wm[w]);
   }
+  // gathers first (independent across items), stores after, so the loads
+  // of all items are in flight together
+  const int32_t* __restrict__ bag_of_pos = a.bag_of_pos;
+  const uint64_t* __restrict__ sorted = a.sorted;
+  int32_t bag[kSortIPT], cbv[kSortIPT], bag0[kSortIPT];
+#pragma unroll
+  for (int k = 0; k < kSortIPT; ++k) {
+    const long long i = base + k * 64 + lane;
+    const uint32_t pos = (uint32_t)item[k];
+    bag[k] = (i < a.N && pos < (uint32_t)a.N) ? bag_of_pos[pos] : -1;
+    // chunk start: the later of its segment's start and its tile's start
+    const int32_t seg_start = (int32_t)max(pm, im[k]) - 1;
+    const int32_t tile0 = (int32_t)((i / kChunk) * kChunk);
+    cbv[k] = seg_start > tile0 ? seg_start : tile0;
+  }
+#pragma unroll
+  for (int k = 0; k < kSortIPT; ++k) {
+    const long long i = base + k * 64 + lane;
+    bag0[k] = bag[k];
+    if (i < a.N && (fl & (1u << (24 + k))) && cbv[k] != (int32_t)i) {
+      const uint32_t p0 = (uint32_t)sorted[cbv[k]];
+      bag0[k] = p0 < (uint32_t)a.N ? bag_of_pos[p0] : -1;
+    }
+  }
 #pragma unroll
   for (int k = 0; k < kSortIPT; ++k) {
     const long long i = base + k * 64 + lane;
@@ -176,10 +201,8 @@ __global__ __launch_bounds__(256) void k_rle_write(RleArgs a) {
     const int32_t seg_start = (int32_t)max(pm, im[k]) - 1;
     const uint32_t key = key_of(item[k]);
     const uint32_t pos = (uint32_t)item[k];
-    if (pos < (uint32_t)a.N) {
-      a.inverse[pos] = seg;
-      a.sorted_bag[i] = a.bag_of_pos[pos];
-    }
+    if (pos < (uint32_t)a.N) a.inverse[pos] = seg;
+    a.sorted_bag[i] = bag[k];
     if (fl & (1u << k)) {
       a.unique_keys[seg] = key;
       a.seg_off[seg] = (int32_t)i;
@@ -188,13 +211,13 @@ __global__ __launch_bounds__(256) void k_rle_write(RleArgs a) {
     if ((i % kChunk) == kChunk - 1 || i == a.N - 1) a.tile_last_seg[i / kChunk] = seg;
     if (i == a.N - 1) a.seg_off[seg + 1] = a.N;
     if (fl & (1u << (24 + k))) {
-      // last position of chunk `chk`: it starts at the later of its segment's
-      // start and its tile's start; it is the whole segment when it starts at
-      // the segment start and ends at the segment end
-      const int32_t tile0 = (int32_t)((i / kChunk) * kChunk);
-      const int32_t cb = seg_start > tile0 ? seg_start : tile0;
-      const bool whole = cb == seg_start && (fl & (1u << (16 + k)));
-      a.desc[chk] = int4{cb, (int32_t)((uint32_t)(i + 1) | (whole ? 0x80000000u : 0u)), (int32_t)key, seg};
+      // last position of chunk `chk`; it is the whole segment when it starts
+      // at the segment start and ends at the segment end. The descriptor also
+      // carries the bag of the chunk's first lookup, so a one-lookup chunk
+      // needs no further index load in the reduce kernel.
+      const bool whole = cbv[k] == seg_start && (fl & (1u << (16 + k)));
+      a.desc[chk] = int4{cbv[k], (int32_t)((uint32_t)(i + 1) | (whole ? 0x80000000u : 0u)), (int32_t)key, bag0[k]};
+      a.chunk_seg[chk] = seg;
     }
   }
 }
@@ -229,6 +252,7 @@ hipError_t launch_rle(const uint64_t* sorted, int N, const WsLayout& L, char* ws
   a.inverse = o.inverse;
   a.seg_off = reinterpret_cast<int32_t*>(ws + L.seg_off);
   a.desc = reinterpret_cast<int4*>(ws + L.desc);
+  a.chunk_seg = reinterpret_cast<int32_t*>(ws + L.chunk_seg);
   a.tile_first_seg = reinterpret_cast<int32_t*>(ws + L.tile_first_seg);
   a.tile_last_seg = reinterpret_cast<int32_t*>(ws + L.tile_last_seg);
   a.sorted_bag = reinterpret_cast<int32_t*>(ws + L.sorted_bag);
