@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=32768, help="samples of batch 0 the oracle runs on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--uniform-keys", action="store_true", help="control run: uniform keys instead of Zipf")
+    ap.add_argument("--schedule", choices=["overlap", "serial"], default="overlap",
+                    help="overlap: the key dedup (emb_backward_dedup) runs on a second stream "
+                         "concurrently with the forward; serial: one stream, dedup inside the backward")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times) and exit: the reference "
                          "point for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -131,39 +134,61 @@ def main() -> int:
         torch.cuda.synchronize()
         U_of.append(int(bufs["num_unique"].item()))
 
-    def step(i):
-        idx, off, n = dev[i % len(dev)]
-        tabs.forward(idx, off, B, cfg.pool, out=Y)
-        tabs.backward(idx, off, B, cfg.pool, dy, bufs)
-        tabs.update(cfg.opt, cfg.lr, cfg.eps, bufs, dY=dy)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()          # default priority
+    ev_free = torch.cuda.Event()        # ws / dedup outputs free again (previous update done)
+    ev_dd = torch.cuda.Event()          # dedup done
+    ev_free.record(main)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    tabs.check_device_error()
+    def step(i, sched, evs=None):
+        """One training step; evs = three timing events (start, after forward
+        [+ dedup], end) recorded on the main stream."""
+        idx, off, n = dev[i % len(dev)]
+        if evs:
+            evs[0].record(main)
+        if sched == "overlap":
+            side.wait_event(ev_free)
+            with torch.cuda.stream(side):
+                tabs.dedup(idx, off, B, cfg.pool, bufs)
+            ev_dd.record(side)
+            tabs.forward(idx, off, B, cfg.pool, out=Y)
+            main.wait_event(ev_dd)
+        else:
+            tabs.forward(idx, off, B, cfg.pool, out=Y)
+        if evs:
+            evs[1].record(main)
+        tabs.backward(idx, off, B, cfg.pool, dy, bufs)   # skips the dedup done ahead
+        tabs.update(cfg.opt, cfg.lr, cfg.eps, bufs, dY=dy)
+        ev_free.record(main)
+        if evs:
+            evs[2].record(main)
+
+    def timed(sched, K):
+        for i in range(args.warmup):
+            step(i, sched)
+        torch.cuda.synchronize()
+        tabs.check_device_error()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        t0.record(main)
+        for i in range(K):
+            step(i, sched, ev[i])
+        t1.record(main)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        total = t0.elapsed_time(t1)
+        fwd = sum(e[0].elapsed_time(e[1]) for e in ev)
+        bwd = sum(e[1].elapsed_time(e[2]) for e in ev)
+        print(f"[bench] {sched}: {K} steps {total:.3f} ms (wall {wall * 1e3:.1f} ms)", file=sys.stderr, flush=True)
+        return total, fwd, bwd
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record()
-    for i in range(K):
-        idx, off, n = dev[i % len(dev)]
-        ev[i][0].record()
-        tabs.forward(idx, off, B, cfg.pool, out=Y)
-        ev[i][1].record()
-        tabs.backward(idx, off, B, cfg.pool, dy, bufs)
-        tabs.update(cfg.opt, cfg.lr, cfg.eps, bufs, dY=dy)
-        ev[i][2].record()
-    t_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_end)
-    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev)
-    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev)
-    print(f"[bench] timed {K} steps: {total_ms:.3f} ms (wall {wall * 1e3:.1f} ms)", file=sys.stderr, flush=True)
+    other = "serial" if args.schedule == "overlap" else "overlap"
+    total_ms, fwd_ms, bwd_ms = timed(args.schedule, K)
+    other_ms, _, _ = timed(other, K)
 
     # algorithmic bytes per step (SURVEY-style formula, actual N and U)
     ib = 4 if host_batches[0].indices.dtype == np.int32 else 8
@@ -174,11 +199,17 @@ def main() -> int:
     bwd_bytes = sum(B * T * D * 4 + n * ib + (T * B + 1) * ib + u * (rowbytes + state_b) * 2 + u * 8 + n * 4
                     for n, u in zip(steps_N, steps_U))
     lookups = sum(steps_N)
+    if args.schedule == "overlap":
+        # the dedup's own I/O (indices, offsets, unique keys + counts, inverse)
+        # runs in the forward phase under this schedule
+        dd = sum(n * ib + (T * B + 1) * ib + u * 8 + n * 4 for n, u in zip(steps_N, steps_U))
+        fwd_bytes += dd
+        bwd_bytes -= dd
 
     # per-kernel times (HIP events around each launch, on the launch stream)
     E.emb_set_kernel_timing(tabs.ctx, True)
     for i in range(K):
-        step(i)
+        step(i, args.schedule)
     torch.cuda.synchronize()
     ktimes = E.emb_kernel_times(tabs.ctx)
     E.emb_set_kernel_timing(tabs.ctx, False)
@@ -225,6 +256,8 @@ def main() -> int:
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "schedule": args.schedule,
+        f"ms_per_step_{other}": round(other_ms / K, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -240,6 +273,9 @@ def main() -> int:
             "unique_per_step": int(round(Uavg)),
             "batches_cycled": len(dev),
         },
+        "phases": ("fwd = forward with the dedup on a second stream alongside it; bwd_update = segmented "
+                   "reduce + fused optimizer" if args.schedule == "overlap" else
+                   "fwd = forward; bwd_update = dedup + segmented reduce + fused optimizer"),
         "fwd": {"ms": round(fwd_ms / K, 4), "lookups_per_s": round(lookups / (fwd_ms * 1e-3), 1),
                 "alg_GBps": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9, 1),
                 "alg_bytes_per_step": int(fwd_bytes / K)},

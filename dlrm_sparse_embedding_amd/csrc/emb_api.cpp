@@ -66,6 +66,21 @@ struct emb_ctx {
     const int32_t* num_unique = nullptr;
     bool valid = false;
   } last;
+  // a dedup done ahead by emb_backward_dedup, consumed by the next backward
+  struct {
+    const void* indices = nullptr;
+    const void* offsets = nullptr;
+    int itype = 0;
+    long long N = 0;
+    int B = 0;
+    int pool = 0;
+    const void* ws = nullptr;
+    const uint32_t* unique_keys = nullptr;
+    const int32_t* counts = nullptr;
+    const int32_t* inverse = nullptr;
+    const int32_t* num_unique = nullptr;
+    bool valid = false;
+  } dedup;
   // timing
   bool timing = false;
   std::vector<TimedLaunch> pending;
@@ -186,8 +201,8 @@ WsLayout ws_layout(const Geom& g, long long N, int B) {
   L.tile_last_seg = take(4ull * (L.ntiles > 0 ? L.ntiles : 1));
   L.partial0 = take(4ull * 2 * (L.ntiles > 0 ? L.ntiles : 1) * g.D);
   L.partial1 = take(4ull * 2 * (L.ntiles1 > 0 ? L.ntiles1 : 1) * g.D);
-  L.ghist = take(4ull * kRadix * (L.nblk_sort > 0 ? L.nblk_sort : 1));
-  L.digit_tot = take(4ull * kRadix);
+  L.ghist = take(4ull * kRadixMax * (L.nblk_sort > 0 ? L.nblk_sort : 1));
+  L.digit_tot = take(4ull * kRadixMax);
   L.rle_blk = take(16ull * (L.nblk_rle > 0 ? L.nblk_rle : 1));
   L.scalars = take(64);
   L.total = off;
@@ -326,10 +341,14 @@ size_t emb_backward_workspace_bytes(const emb_ctx* ctx, int64_t N, int32_t B) {
   return ws_layout(ctx->g, N, B).total;
 }
 
-int emb_backward_unique_reduce(emb_ctx* ctx, const void* indices, const void* offsets, int32_t itype,
-                               int64_t N, int32_t B, int32_t pool, const float* dY, void* ws,
-                               size_t ws_bytes, uint32_t* unique_keys, int32_t* counts, int32_t* inverse,
-                               int32_t* num_unique, float* reduced_grad, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by the dedup-only and the full backward call.
+int check_dedup_args(emb_ctx* ctx, const void* indices, const void* offsets, int32_t itype, int64_t N,
+                     int32_t B, int32_t pool, void* ws, size_t ws_bytes, uint32_t* unique_keys,
+                     int32_t* counts, int32_t* inverse, int32_t* num_unique) {
   if (!ctx) return fail(EMB_E_INVAL, "ctx is NULL");
   int rc = check_itype(itype);
   if (rc) return rc;
@@ -338,72 +357,142 @@ int emb_backward_unique_reduce(emb_ctx* ctx, const void* indices, const void* of
   if (N >= (1ll << 31)) return fail(EMB_E_INVAL, "N must be < 2^31");
   if (B == 0 && N > 0) return fail(EMB_E_INVAL, "B == 0 with N > 0");
   if (!ws || !num_unique) return fail(EMB_E_INVAL, "ws/num_unique is NULL");
-  if (N > 0 && (!indices || !offsets || !dY || !unique_keys || !counts || !inverse))
+  if (N > 0 && (!indices || !offsets || !unique_keys || !counts || !inverse))
     return fail(EMB_E_INVAL, "NULL buffer");
   if (!aligned(ws, 256)) return fail(EMB_E_INVAL, "ws must be 256-byte aligned");
-  if (dY && !aligned(dY, 16)) return fail(EMB_E_INVAL, "dY must be 16-byte aligned");
-  if (reduced_grad && !aligned(reduced_grad, 16)) return fail(EMB_E_INVAL, "reduced_grad must be 16-byte aligned");
   if ((long long)B * ctx->g.T * ctx->g.D >= (1ll << 32))
     return fail(EMB_E_INVAL, "dY must hold fewer than 2^32 elements (B*T*dim)");
   const WsLayout L = ws_layout(ctx->g, N, B);
   if (ws_bytes < L.total)
     return fail(EMB_E_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, L.total);
-  if ((rc = ensure_device(ctx))) return rc;
-  hipStream_t st = static_cast<hipStream_t>(hip_stream);
-  char* w = static_cast<char*>(ws);
-  ctx->last.valid = false;
+  return EMB_OK;
+}
+
+// Keys -> radix sort -> run-length encoding, on `st`.
+int run_dedup(emb_ctx* ctx, const void* indices, const void* offsets, int32_t itype, int64_t N, int32_t B,
+              int32_t pool, char* w, const WsLayout& L, uint32_t* unique_keys, int32_t* counts,
+              int32_t* inverse, int32_t* num_unique, hipStream_t st) {
   hipError_t e;
   if (N == 0) {
     KScope ks(ctx, EMB_K_RLE, st);
     e = launch_set_empty(L, w, num_unique, st);
     if (e != hipSuccess) return hip_fail(e, "empty backward");
-  } else {
+    return EMB_OK;
+  }
+  {
+    KScope ks(ctx, EMB_K_KEYS, st);
+    e = launch_keys(ctx->g, ctx->dc, indices, offsets, itype, N, B, pool, L, w, st);
+    if (e != hipSuccess) return hip_fail(e, "keys kernel");
+  }
+  uint64_t* a = reinterpret_cast<uint64_t*>(w + L.keys_a);
+  uint64_t* b = reinterpret_cast<uint64_t*>(w + L.keys_b);
+  uint32_t* ghist = reinterpret_cast<uint32_t*>(w + L.ghist);
+  uint32_t* dtot = reinterpret_cast<uint32_t*>(w + L.digit_tot);
+  const int rb = radix_bits_for(ctx->g.key_bits);
+  for (int shift = 0; shift < ctx->g.key_bits; shift += rb) {
     {
-      KScope ks(ctx, EMB_K_KEYS, st);
-      e = launch_keys(ctx->g, ctx->dc, indices, offsets, itype, N, B, pool, L, w, st);
-      if (e != hipSuccess) return hip_fail(e, "keys kernel");
-    }
-    uint64_t* a = reinterpret_cast<uint64_t*>(w + L.keys_a);
-    uint64_t* b = reinterpret_cast<uint64_t*>(w + L.keys_b);
-    uint32_t* ghist = reinterpret_cast<uint32_t*>(w + L.ghist);
-    uint32_t* dtot = reinterpret_cast<uint32_t*>(w + L.digit_tot);
-    for (int shift = 0; shift < ctx->g.key_bits; shift += kRadixBits) {
-      {
-        KScope ks(ctx, EMB_K_SORT_HIST, st);
-        if ((e = launch_sort_hist(a, (int)N, shift, ghist, L.nblk_sort, st)) != hipSuccess)
-          return hip_fail(e, "sort histogram");
-      }
-      {
-        KScope ks(ctx, EMB_K_SORT_SCAN, st);
-        if ((e = launch_sort_scan(ghist, L.nblk_sort, dtot, st)) != hipSuccess) return hip_fail(e, "sort scan");
-      }
-      {
-        KScope ks(ctx, EMB_K_SORT_SCATTER, st);
-        if ((e = launch_sort_scatter(a, b, (int)N, shift, ghist, dtot, L.nblk_sort, st)) != hipSuccess)
-          return hip_fail(e, "sort scatter");
-      }
-      uint64_t* tmp = a;
-      a = b;
-      b = tmp;
+      KScope ks(ctx, EMB_K_SORT_HIST, st);
+      if ((e = launch_sort_hist(rb, a, (int)N, shift, ghist, L.nblk_sort, st)) != hipSuccess)
+        return hip_fail(e, "sort histogram");
     }
     {
-      KScope ks(ctx, EMB_K_RLE, st);
-      RleOut o{unique_keys, counts, inverse, num_unique};
-      if ((e = launch_rle(a, (int)N, L, w, o, st)) != hipSuccess) return hip_fail(e, "run-length encode");
+      KScope ks(ctx, EMB_K_SORT_SCAN, st);
+      if ((e = launch_sort_scan(rb, ghist, L.nblk_sort, dtot, st)) != hipSuccess) return hip_fail(e, "sort scan");
     }
-    if (reduced_grad) {
-      {
-        KScope ks(ctx, EMB_K_REDUCE, st);
-        if ((e = launch_reduce(ctx->g, ctx->dc, 0, (int)N, B, pool, dY, L, w, unique_keys, num_unique,
-                               reduced_grad, 0.f, 0.f, st)) != hipSuccess)
-          return hip_fail(e, "segment reduce");
-      }
-      {
-        KScope ks(ctx, EMB_K_COMBINE, st);
-        if ((e = launch_combine(ctx->g, ctx->dc, 0, (int)N, L, w, unique_keys, reduced_grad, 0.f, 0.f, st)) !=
-            hipSuccess)
-          return hip_fail(e, "segment combine");
-      }
+    {
+      KScope ks(ctx, EMB_K_SORT_SCATTER, st);
+      if ((e = launch_sort_scatter(rb, a, b, (int)N, shift, ghist, dtot, L.nblk_sort, st)) != hipSuccess)
+        return hip_fail(e, "sort scatter");
+    }
+    uint64_t* tmp = a;
+    a = b;
+    b = tmp;
+  }
+  {
+    KScope ks(ctx, EMB_K_RLE, st);
+    RleOut o{unique_keys, counts, inverse, num_unique};
+    if ((e = launch_rle(a, (int)N, L, w, o, st)) != hipSuccess) return hip_fail(e, "run-length encode");
+  }
+  return EMB_OK;
+}
+
+bool same_dedup(const emb_ctx* c, const void* indices, const void* offsets, int32_t itype, int64_t N, int32_t B,
+                int32_t pool, const void* ws, const uint32_t* unique_keys, const int32_t* counts,
+                const int32_t* inverse, const int32_t* num_unique) {
+  const auto& d = c->dedup;
+  return d.valid && d.indices == indices && d.offsets == offsets && d.itype == itype && d.N == N && d.B == B &&
+         d.pool == pool && d.ws == ws && d.unique_keys == unique_keys && d.counts == counts &&
+         d.inverse == inverse && d.num_unique == num_unique;
+}
+
+}  // namespace
+
+extern "C" {
+
+int emb_backward_dedup(emb_ctx* ctx, const void* indices, const void* offsets, int32_t itype, int64_t N,
+                       int32_t B, int32_t pool, void* ws, size_t ws_bytes, uint32_t* unique_keys, int32_t* counts,
+                       int32_t* inverse, int32_t* num_unique, void* hip_stream) {
+  int rc = check_dedup_args(ctx, indices, offsets, itype, N, B, pool, ws, ws_bytes, unique_keys, counts, inverse,
+                            num_unique);
+  if (rc) return rc;
+  if ((rc = ensure_device(ctx))) return rc;
+  ctx->dedup.valid = false;
+  ctx->last.valid = false;
+  const WsLayout L = ws_layout(ctx->g, N, B);
+  rc = run_dedup(ctx, indices, offsets, itype, N, B, pool, static_cast<char*>(ws), L, unique_keys, counts,
+                 inverse, num_unique, static_cast<hipStream_t>(hip_stream));
+  if (rc) return rc;
+  auto& d = ctx->dedup;
+  d.indices = indices;
+  d.offsets = offsets;
+  d.itype = itype;
+  d.N = N;
+  d.B = B;
+  d.pool = pool;
+  d.ws = ws;
+  d.unique_keys = unique_keys;
+  d.counts = counts;
+  d.inverse = inverse;
+  d.num_unique = num_unique;
+  d.valid = true;
+  return ok();
+}
+
+int emb_backward_unique_reduce(emb_ctx* ctx, const void* indices, const void* offsets, int32_t itype,
+                               int64_t N, int32_t B, int32_t pool, const float* dY, void* ws,
+                               size_t ws_bytes, uint32_t* unique_keys, int32_t* counts, int32_t* inverse,
+                               int32_t* num_unique, float* reduced_grad, void* hip_stream) {
+  int rc = check_dedup_args(ctx, indices, offsets, itype, N, B, pool, ws, ws_bytes, unique_keys, counts, inverse,
+                            num_unique);
+  if (rc) return rc;
+  if (N > 0 && !dY) return fail(EMB_E_INVAL, "dY is NULL");
+  if (dY && !aligned(dY, 16)) return fail(EMB_E_INVAL, "dY must be 16-byte aligned");
+  if (reduced_grad && !aligned(reduced_grad, 16)) return fail(EMB_E_INVAL, "reduced_grad must be 16-byte aligned");
+  if ((rc = ensure_device(ctx))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  char* w = static_cast<char*>(ws);
+  const WsLayout L = ws_layout(ctx->g, N, B);
+  const bool done = same_dedup(ctx, indices, offsets, itype, N, B, pool, ws, unique_keys, counts, inverse,
+                               num_unique);
+  ctx->dedup.valid = false;  // a dedup is consumed by one backward
+  ctx->last.valid = false;
+  if (!done) {
+    rc = run_dedup(ctx, indices, offsets, itype, N, B, pool, w, L, unique_keys, counts, inverse, num_unique, st);
+    if (rc) return rc;
+  }
+  if (N > 0 && reduced_grad) {
+    hipError_t e;
+    {
+      KScope ks(ctx, EMB_K_REDUCE, st);
+      if ((e = launch_reduce(ctx->g, ctx->dc, 0, (int)N, B, pool, dY, L, w, unique_keys, num_unique, reduced_grad,
+                             0.f, 0.f, st)) != hipSuccess)
+        return hip_fail(e, "segment reduce");
+    }
+    {
+      KScope ks(ctx, EMB_K_COMBINE, st);
+      if ((e = launch_combine(ctx->g, ctx->dc, 0, (int)N, L, w, unique_keys, reduced_grad, 0.f, 0.f, st)) !=
+          hipSuccess)
+        return hip_fail(e, "segment combine");
     }
   }
   ctx->last.ws = ws;

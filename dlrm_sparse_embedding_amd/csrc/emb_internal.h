@@ -32,8 +32,8 @@ constexpr int kChunk1 = kChunk * kL1Tiles;  // 4096 positions
 constexpr int kSortThreads = 256;
 constexpr int kSortIPT = 8;
 constexpr int kSortTile = kSortThreads * kSortIPT;  // 2048 items
-constexpr int kRadixBits = 8;
-constexpr int kRadix = 1 << kRadixBits;
+constexpr int kRadixMaxBits = 9;
+constexpr int kRadixMax = 1 << kRadixMaxBits;
 
 inline int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 inline int next_pow2(int x) {
@@ -74,8 +74,8 @@ struct WsLayout {
   size_t tile_last_seg;         // int32 [ntiles] segment of a tile's last position
   size_t partial0;              // fp32 [2*ntiles][D]
   size_t partial1;              // fp32 [2*ntiles1][D]
-  size_t ghist;                 // uint32 [kRadix][nblk_sort]
-  size_t digit_tot;             // uint32 [kRadix]
+  size_t ghist;                 // uint32 [digits][nblk_sort]
+  size_t digit_tot;             // uint32 [digits]
   size_t rle_blk;               // uint32x4 [nblk_rle]
   size_t scalars;               // int32 [16]: [0] num_chunks
   size_t total;
@@ -97,10 +97,12 @@ hipError_t launch_keys(const Geom& g, const DevCtx& dc, const void* indices, con
                        int itype, long long N, int B, int pool, const WsLayout& L, char* ws,
                        hipStream_t st);
 
-hipError_t launch_sort_hist(const uint64_t* keys, int N, int shift, uint32_t* ghist, int nblk,
-                            hipStream_t st);
-hipError_t launch_sort_scan(uint32_t* ghist, int nblk, uint32_t* digit_tot, hipStream_t st);
-hipError_t launch_sort_scatter(const uint64_t* in, uint64_t* out, int N, int shift,
+// radix sort pass kernels; rb = digit bits (8 or 9, radix_bits_for(key_bits))
+int radix_bits_for(int key_bits);
+hipError_t launch_sort_hist(int rb, const uint64_t* keys, int N, int shift, uint32_t* ghist,
+                            int nblk, hipStream_t st);
+hipError_t launch_sort_scan(int rb, uint32_t* ghist, int nblk, uint32_t* digit_tot, hipStream_t st);
+hipError_t launch_sort_scatter(int rb, const uint64_t* in, uint64_t* out, int N, int shift,
                                const uint32_t* ghist, const uint32_t* digit_tot, int nblk,
                                hipStream_t st);
 

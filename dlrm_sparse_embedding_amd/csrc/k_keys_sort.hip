@@ -6,9 +6,10 @@
 // any gradient is reduced or a row is written, the step's lookups are grouped
 // by global key g = row_offset[t] + idx. Here the grouping is a sort: each
 // lookup i becomes the 64-bit word (g << 32 | i), and an LSD radix sort over
-// the low key_bits bits of g (8 bits per pass) orders the words by key, with
+// the low key_bits bits of g orders the words by key, with
 // positions ascending inside a key because every pass is stable.
 //
+// Digits are 8 bits, or 9 when that saves a pass (27-bit keys: 3 passes, not 4).
 // Sort pass = three kernels:
 //   hist    per 2048-item tile, count digits in LDS -> ghist[digit][tile]
 //   scan    one block per digit: exclusive scan of its row over tiles
@@ -96,24 +97,46 @@ hipError_t launch_keys(const Geom& g, const DevCtx& dc, const void* indices, con
 // radix sort
 // ---------------------------------------------------------------------------
 
+template <int RB>
 __device__ __forceinline__ uint32_t digit_of(uint64_t x, int shift) {
-  return (uint32_t)(x >> (32 + shift)) & (kRadix - 1);
+  return (uint32_t)(x >> (32 + shift)) & ((1u << RB) - 1u);
 }
 
+// Exclusive scan over R = 256 * PER digits held PER-per-thread (thread i owns
+// digits i*PER .. i*PER+PER-1). Contains __syncthreads.
+template <int PER>
+__device__ __forceinline__ void block_excl_scan_digits(const uint32_t* in, uint32_t* out, uint32_t* lds) {
+  uint32_t v[PER], sum = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    v[j] = in[j];
+    sum += v[j];
+  }
+  uint32_t tot;
+  uint32_t run = block_excl_scan_256(sum, lds, &tot);
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    out[j] = run;
+    run += v[j];
+  }
+}
+
+template <int RB>
 __global__ __launch_bounds__(256) void k_sort_hist(const uint64_t* __restrict__ keys, int N,
                                                    int shift, uint32_t* __restrict__ ghist,
                                                    int nblk) {
-  __shared__ uint32_t h[kRadix];
-  h[threadIdx.x] = 0;
+  constexpr int R = 1 << RB;
+  __shared__ uint32_t h[R];
+  for (int d = threadIdx.x; d < R; d += 256) h[d] = 0;
   __syncthreads();
   const long long base = (long long)blockIdx.x * kSortTile;
 #pragma unroll
   for (int k = 0; k < kSortIPT; ++k) {
     const long long i = base + k * 256 + threadIdx.x;
-    if (i < N) atomicAdd(&h[digit_of(keys[i], shift)], 1u);
+    if (i < N) atomicAdd(&h[digit_of<RB>(keys[i], shift)], 1u);
   }
   __syncthreads();
-  ghist[(size_t)threadIdx.x * nblk + blockIdx.x] = h[threadIdx.x];
+  for (int d = threadIdx.x; d < R; d += 256) ghist[(size_t)d * nblk + blockIdx.x] = h[d];
 }
 
 __global__ __launch_bounds__(256) void k_sort_scan(uint32_t* __restrict__ ghist, int nblk,
@@ -143,14 +166,17 @@ __global__ __launch_bounds__(256) void k_sort_scan(uint32_t* __restrict__ ghist,
   if (threadIdx.x == 0) digit_tot[blockIdx.x] = running;
 }
 
+template <int RB>
 __global__ __launch_bounds__(256) void k_sort_scatter(const uint64_t* __restrict__ in,
                                                       uint64_t* __restrict__ out, int N, int shift,
                                                       const uint32_t* __restrict__ ghist,
                                                       const uint32_t* __restrict__ digit_tot,
                                                       int nblk) {
-  __shared__ uint32_t s_gbase[kRadix];   // global start of this tile's digit-d run
-  __shared__ uint32_t s_wcnt[4][kRadix]; // per-wave digit counters, then per-wave offsets
-  __shared__ uint32_t s_bexcl[kRadix];   // tile-local start of digit d
+  constexpr int R = 1 << RB;
+  constexpr int PER = R / 256;
+  __shared__ uint32_t s_gbase[R];    // global start of this tile's digit-d run
+  __shared__ uint32_t s_wcnt[4][R];  // per-wave digit counters, then per-wave offsets
+  __shared__ uint32_t s_bexcl[R];    // tile-local start of digit d
   __shared__ uint64_t s_stage[kSortTile];
   __shared__ uint32_t s_scan[8];
   const int tid = threadIdx.x;
@@ -159,12 +185,19 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const uint64_t* __restrict
   const int blk = blockIdx.x;
 
   {
-    uint32_t tot;
-    const uint32_t pre = block_excl_scan_256(digit_tot[tid], s_scan, &tot);
-    s_gbase[tid] = pre + ghist[(size_t)tid * nblk + blk];
+    uint32_t in_[PER], pre[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) in_[j] = digit_tot[tid * PER + j];
+    block_excl_scan_digits<PER>(in_, pre, s_scan);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int d = tid * PER + j;
+      s_gbase[d] = pre[j] + ghist[(size_t)d * nblk + blk];
+    }
   }
 #pragma unroll
-  for (int w = 0; w < 4; ++w) s_wcnt[w][tid] = 0;
+  for (int w = 0; w < 4; ++w)
+    for (int d = tid; d < R; d += 256) s_wcnt[w][d] = 0;
   __syncthreads();
 
   const long long base = (long long)blk * kSortTile + wave * (64 * kSortIPT);
@@ -179,10 +212,10 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const uint64_t* __restrict
 #pragma unroll
   for (int k = 0; k < kSortIPT; ++k) {
     const bool valid = base + k * 64 + lane < N;
-    const uint32_t d = digit_of(item[k], shift);
+    const uint32_t d = digit_of<RB>(item[k], shift);
     uint64_t peers = __ballot(valid);
 #pragma unroll
-    for (int b = 0; b < kRadixBits; ++b) {
+    for (int b = 0; b < RB; ++b) {
       const bool bit = (d >> b) & 1u;
       const uint64_t bb = __ballot(bit);
       peers &= bit ? bb : ~bb;
@@ -199,20 +232,27 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const uint64_t* __restrict
   }
   __syncthreads();
   {
-    const uint32_t c0 = s_wcnt[0][tid], c1 = s_wcnt[1][tid], c2 = s_wcnt[2][tid], c3 = s_wcnt[3][tid];
-    s_wcnt[0][tid] = 0;
-    s_wcnt[1][tid] = c0;
-    s_wcnt[2][tid] = c0 + c1;
-    s_wcnt[3][tid] = c0 + c1 + c2;
-    uint32_t tot;
-    s_bexcl[tid] = block_excl_scan_256(c0 + c1 + c2 + c3, s_scan, &tot);
+    uint32_t tot_[PER], pre[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int d = tid * PER + j;
+      const uint32_t c0 = s_wcnt[0][d], c1 = s_wcnt[1][d], c2 = s_wcnt[2][d], c3 = s_wcnt[3][d];
+      s_wcnt[0][d] = 0;
+      s_wcnt[1][d] = c0;
+      s_wcnt[2][d] = c0 + c1;
+      s_wcnt[3][d] = c0 + c1 + c2;
+      tot_[j] = c0 + c1 + c2 + c3;
+    }
+    block_excl_scan_digits<PER>(tot_, pre, s_scan);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) s_bexcl[tid * PER + j] = pre[j];
   }
   __syncthreads();
 #pragma unroll
   for (int k = 0; k < kSortIPT; ++k) {
     const bool valid = base + k * 64 + lane < N;
     if (valid) {
-      const uint32_t d = digit_of(item[k], shift);
+      const uint32_t d = digit_of<RB>(item[k], shift);
       s_stage[s_bexcl[d] + s_wcnt[wave][d] + rank[k]] = item[k];
     }
   }
@@ -221,28 +261,41 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const uint64_t* __restrict
   const int cnt = rem < kSortTile ? (int)rem : kSortTile;
   for (int j = tid; j < cnt; j += 256) {
     const uint64_t x = s_stage[j];
-    const uint32_t d = digit_of(x, shift);
+    const uint32_t d = digit_of<RB>(x, shift);
     const size_t dst = (size_t)s_gbase[d] + (uint32_t)(j - (int)s_bexcl[d]);
     if (dst < (size_t)N) out[dst] = x;
   }
 }
 
-hipError_t launch_sort_hist(const uint64_t* keys, int N, int shift, uint32_t* ghist, int nblk,
-                            hipStream_t st) {
-  hipLaunchKernelGGL(k_sort_hist, dim3(nblk), dim3(256), 0, st, keys, N, shift, ghist, nblk);
+int radix_bits_for(int key_bits) {
+  const int p8 = (key_bits + 7) / 8;
+  const int p9 = (key_bits + 8) / 9;
+  return p9 < p8 ? 9 : 8;
+}
+
+hipError_t launch_sort_hist(int rb, const uint64_t* keys, int N, int shift, uint32_t* ghist,
+                            int nblk, hipStream_t st) {
+  if (rb == 9)
+    hipLaunchKernelGGL(k_sort_hist<9>, dim3(nblk), dim3(256), 0, st, keys, N, shift, ghist, nblk);
+  else
+    hipLaunchKernelGGL(k_sort_hist<8>, dim3(nblk), dim3(256), 0, st, keys, N, shift, ghist, nblk);
   return hipGetLastError();
 }
 
-hipError_t launch_sort_scan(uint32_t* ghist, int nblk, uint32_t* digit_tot, hipStream_t st) {
-  hipLaunchKernelGGL(k_sort_scan, dim3(kRadix), dim3(256), 0, st, ghist, nblk, digit_tot);
+hipError_t launch_sort_scan(int rb, uint32_t* ghist, int nblk, uint32_t* digit_tot, hipStream_t st) {
+  hipLaunchKernelGGL(k_sort_scan, dim3(1 << rb), dim3(256), 0, st, ghist, nblk, digit_tot);
   return hipGetLastError();
 }
 
-hipError_t launch_sort_scatter(const uint64_t* in, uint64_t* out, int N, int shift,
+hipError_t launch_sort_scatter(int rb, const uint64_t* in, uint64_t* out, int N, int shift,
                                const uint32_t* ghist, const uint32_t* digit_tot, int nblk,
                                hipStream_t st) {
-  hipLaunchKernelGGL(k_sort_scatter, dim3(nblk), dim3(256), 0, st, in, out, N, shift, ghist,
-                     digit_tot, nblk);
+  if (rb == 9)
+    hipLaunchKernelGGL(k_sort_scatter<9>, dim3(nblk), dim3(256), 0, st, in, out, N, shift, ghist,
+                       digit_tot, nblk);
+  else
+    hipLaunchKernelGGL(k_sort_scatter<8>, dim3(nblk), dim3(256), 0, st, in, out, N, shift, ghist,
+                       digit_tot, nblk);
   return hipGetLastError();
 }
 

@@ -87,6 +87,8 @@ def lib() -> ctypes.CDLL:
     L.emb_backward_unique_reduce.argtypes = [vp, vp, vp, i32, i64, i32, i32, vp, vp, sz, vp, vp, vp,
                                              vp, vp, vp]
     L.emb_backward_unique_reduce.restype = ctypes.c_int
+    L.emb_backward_dedup.argtypes = [vp, vp, vp, i32, i64, i32, i32, vp, sz, vp, vp, vp, vp, vp]
+    L.emb_backward_dedup.restype = ctypes.c_int
     L.emb_sparse_update.argtypes = [vp, i32, ctypes.c_float, ctypes.c_float, vp, vp, vp, vp]
     L.emb_sparse_update.restype = ctypes.c_int
     L.emb_last_error.argtypes = []
@@ -179,6 +181,16 @@ def emb_backward_unique_reduce(ctx: int, indices, offsets, B: int, pool: str, dY
         ctx, _ptr(indices), _ptr(offsets), _itype(indices), int(indices.numel()), int(B),
         POOL_CODE[pool], _ptr(dY), _ptr(ws), int(ws.numel() * ws.element_size()), _ptr(unique_keys),
         _ptr(counts), _ptr(inverse), _ptr(num_unique), _ptr(reduced_grad), _stream(stream)))
+
+
+def emb_backward_dedup(ctx: int, indices, offsets, B: int, pool: str, ws, unique_keys, counts, inverse,
+                       num_unique, stream=None) -> None:
+    if offsets.dtype != indices.dtype:
+        raise ValueError("indices and offsets must share one integer type")
+    _check(lib().emb_backward_dedup(
+        ctx, _ptr(indices), _ptr(offsets), _itype(indices), int(indices.numel()), int(B),
+        POOL_CODE[pool], _ptr(ws), int(ws.numel() * ws.element_size()), _ptr(unique_keys),
+        _ptr(counts), _ptr(inverse), _ptr(num_unique), _stream(stream)))
 
 
 def emb_sparse_update(ctx: int, opt: str, lr: float, eps: float, ws, dY=None, reduced_grad=None,
@@ -284,6 +296,10 @@ class EmbeddingTables:
         emb_backward_unique_reduce(self.ctx, indices, offsets, B, pool, dY, bufs["ws"],
                                    bufs["unique_keys"], bufs["counts"], bufs["inverse"],
                                    bufs["num_unique"], bufs["reduced_grad"], stream)
+
+    def dedup(self, indices, offsets, B: int, pool: str, bufs, stream=None) -> None:
+        emb_backward_dedup(self.ctx, indices, offsets, B, pool, bufs["ws"], bufs["unique_keys"],
+                           bufs["counts"], bufs["inverse"], bufs["num_unique"], stream)
 
     def update(self, opt: str, lr: float, eps: float, bufs, dY=None, stream=None) -> None:
         emb_sparse_update(self.ctx, opt, lr, eps, bufs["ws"], dY, bufs["reduced_grad"], stream)

@@ -163,6 +163,21 @@ int emb_backward_unique_reduce(emb_ctx* ctx, const void* indices, const void* of
                                uint32_t* unique_keys, int32_t* counts, int32_t* inverse,
                                int32_t* num_unique, float* reduced_grad, void* hip_stream);
 
+/* The dedup half of emb_backward_unique_reduce alone: global keys, sort,
+ * run-length encoding -> unique_keys, counts, inverse, *num_unique and the
+ * sorted segments in ws (same outputs, same layouts). It needs the batch's
+ * indices and offsets but not dY, so a caller may run it early -- e.g. on a
+ * second stream concurrently with emb_forward_pooled, the way EMBark dedups
+ * a batch's keys (unique-based compression) before the exchange. The next
+ * emb_backward_unique_reduce on this context with the same indices, offsets,
+ * itype, N, B, pool, ws and output buffers then skips its own dedup; any
+ * other backward discards it. The caller orders the two calls (same stream
+ * or an event) and keeps the buffers unchanged in between. */
+int emb_backward_dedup(emb_ctx* ctx, const void* indices, const void* offsets, int32_t itype,
+                       int64_t N, int32_t B, int32_t pool, void* ws, size_t ws_bytes,
+                       uint32_t* unique_keys, int32_t* counts, int32_t* inverse,
+                       int32_t* num_unique, void* hip_stream);
+
 /* Sparse optimizer step on the rows the last backward (with this ws) found,
  * in place, each unique row read and written exactly once:
  *   SGD:     w <- w - (lr*g)

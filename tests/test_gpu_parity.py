@@ -249,3 +249,42 @@ def test_two_adagrad_steps():
         for j, k in enumerate(u.tolist()):
             state[k] = (w_new[j].copy(), G_new[j].copy())
     tabs.close()
+
+
+def test_dedup_ahead_on_second_stream_matches_serial():
+    # emb_backward_dedup on a side stream, concurrent with the forward, then
+    # the backward (which skips its dedup) and the fused update: bit-identical
+    # to the one-stream path
+    cfg = W.make_config(2, batch=4096)
+    batch = W.make_batch(cfg, k=5)
+    dY = W.make_dy(cfg, k=5)
+    _say("dedup-ahead cfg2 B=4096")
+    ref = P.run_step(cfg, batch, dY, path="fused", sample_untouched=0)
+    tabs = P.make_tables(cfg)
+    idx, off, dy = P.to_dev(batch, dY)
+    bufs = tabs.backward_buffers(batch.N, cfg.batch, with_grad=False)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(main)
+    with torch.cuda.stream(side):
+        tabs.dedup(idx, off, cfg.batch, cfg.pool, bufs)
+    ev = torch.cuda.Event()
+    ev.record(side)
+    Y = tabs.forward(idx, off, cfg.batch, cfg.pool)
+    main.wait_event(ev)
+    tabs.backward(idx, off, cfg.batch, cfg.pool, dy, bufs)
+    tabs.update(cfg.opt, cfg.lr, cfg.eps, bufs, dY=dy)
+    torch.cuda.synchronize()
+    u, c, inv = P.oracle_dedup(cfg, batch)
+    P.check_dedup(bufs, u, c, inv)
+    w_new, G_new = P.read_rows(tabs, cfg, ref["keys"])
+    assert np.array_equal(w_new.view(np.uint32), ref["w_new"].view(np.uint32))
+    assert np.array_equal(G_new.view(np.uint32), ref["G_new"].view(np.uint32))
+    # a backward with a different workspace does its own dedup
+    bufs2 = tabs.backward_buffers(batch.N, cfg.batch, with_grad=True)
+    tabs.dedup(idx, off, cfg.batch, cfg.pool, bufs)
+    tabs.backward(idx, off, cfg.batch, cfg.pool, dy, bufs2)
+    torch.cuda.synchronize()
+    P.check_dedup(bufs2, u, c, inv)
+    del Y
+    tabs.close()
