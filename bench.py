@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--schedule", choices=["overlap", "serial"], default="overlap",
                     help="overlap: the key dedup (emb_backward_dedup) runs on a second stream "
                          "concurrently with the forward; serial: one stream, dedup inside the backward")
+    ap.add_argument("--reduce", choices=["fused", "atomic"], default="fused",
+                    help="fused: sorted-segment reduction fused with the optimizer (the path); atomic: the "
+                         "evidence variant, fp32 atomics into a materialised gradient, then the update")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times) and exit: the reference "
                          "point for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -123,14 +126,15 @@ def main() -> int:
     dy = torch.from_numpy(dY_host).cuda()
     Y = torch.empty((B, T * D), dtype=torch.float32, device="cuda")
     nmax = max(b.N for b in host_batches)
-    bufs = tabs.backward_buffers(nmax, B, with_grad=False)
+    bufs = tabs.backward_buffers(nmax, B, with_grad=args.reduce == "atomic")
     torch.cuda.synchronize()
     print(f"[bench] {len(dev)} batches on device, N = {[b.N for b in host_batches]}", file=sys.stderr, flush=True)
 
     # unique keys per batch (for the byte counts), read outside any timed region
     U_of = []
     for idx, off, n in dev:
-        tabs.backward(idx, off, B, cfg.pool, dy, bufs)
+        E.emb_backward_unique_reduce(tabs.ctx, idx, off, B, cfg.pool, dy, bufs["ws"], bufs["unique_keys"],
+                                     bufs["counts"], bufs["inverse"], bufs["num_unique"], None)
         torch.cuda.synchronize()
         U_of.append(int(bufs["num_unique"].item()))
 
@@ -157,8 +161,14 @@ def main() -> int:
             tabs.forward(idx, off, B, cfg.pool, out=Y)
         if evs:
             evs[1].record(main)
-        tabs.backward(idx, off, B, cfg.pool, dy, bufs)   # skips the dedup done ahead
-        tabs.update(cfg.opt, cfg.lr, cfg.eps, bufs, dY=dy)
+        if args.reduce == "fused":
+            tabs.backward(idx, off, B, cfg.pool, dy, bufs)   # skips the dedup done ahead
+            tabs.update(cfg.opt, cfg.lr, cfg.eps, bufs, dY=dy)
+        else:
+            E.emb_backward_unique_reduce(tabs.ctx, idx, off, B, cfg.pool, dy, bufs["ws"], bufs["unique_keys"],
+                                         bufs["counts"], bufs["inverse"], bufs["num_unique"], None)
+            tabs.atomic_reduce(off, n, B, cfg.pool, dy, bufs)
+            tabs.update(cfg.opt, cfg.lr, cfg.eps, bufs)
         ev_free.record(main)
         if evs:
             evs[2].record(main)
@@ -228,6 +238,9 @@ def main() -> int:
         "sort_scatter": Navg * 8 * 2,
         "sort_hist": Navg * 8,
         "keys": Navg * ib * 2 + Navg * (8 + 4),
+        # atomic reduction: every bag's dY row once, every lookup's atomic
+        # read-modify-write of its unique row (D*4 each way), inverse reads
+        "atomic": B * T * D * 4 + Navg * D * 4 * 2 + Navg * 4,
     }
     alg = per_launch.get(dominant)
     roofline = None
@@ -235,7 +248,7 @@ def main() -> int:
         achieved = alg / (kavg_us[dominant] * 1e-6) / 1e9
         wtag = f"cfg{args.config}" + ("_uniform" if args.uniform_keys else "")
         src = {"forward": "k_forward.hip", "reduce": "k_reduce.hip", "sort_scatter": "k_keys_sort.hip",
-               "sort_hist": "k_keys_sort.hip", "keys": "k_keys_sort.hip"}[dominant]
+               "sort_hist": "k_keys_sort.hip", "keys": "k_keys_sort.hip", "atomic": "k_atomic.hip"}[dominant]
         traffic = measured_traffic(dominant, wtag)
         roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
@@ -257,6 +270,7 @@ def main() -> int:
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "schedule": args.schedule,
+        "reduce": args.reduce,
         f"ms_per_step_{other}": round(other_ms / K, 4),
         "higher_is_better": True,
         "scaling": "weak",

@@ -547,6 +547,31 @@ int emb_sparse_update(emb_ctx* ctx, int32_t opt, float lr, float eps, const void
   return ok();
 }
 
+int emb_backward_atomic_reduce(emb_ctx* ctx, const void* offsets, int32_t itype, int64_t N, int32_t B,
+                               int32_t pool, const float* dY, const int32_t* inverse, const int32_t* num_unique,
+                               float* reduced_grad, void* hip_stream) {
+  if (!ctx) return fail(EMB_E_INVAL, "ctx is NULL");
+  int rc = check_itype(itype);
+  if (rc) return rc;
+  if ((rc = check_pool(pool))) return rc;
+  if (B < 0 || N < 0) return fail(EMB_E_INVAL, "negative B or N");
+  if (N >= (1ll << 31)) return fail(EMB_E_INVAL, "N must be < 2^31");
+  if (B == 0 && N > 0) return fail(EMB_E_INVAL, "B == 0 with N > 0");
+  if (!num_unique || !reduced_grad) return fail(EMB_E_INVAL, "num_unique/reduced_grad is NULL");
+  if (N > 0 && (!offsets || !dY || !inverse)) return fail(EMB_E_INVAL, "NULL buffer");
+  if (!aligned(reduced_grad, 16) || (dY && !aligned(dY, 16)))
+    return fail(EMB_E_INVAL, "dY/reduced_grad must be 16-byte aligned");
+  if ((long long)B * ctx->g.T * ctx->g.D >= (1ll << 32))
+    return fail(EMB_E_INVAL, "dY must hold fewer than 2^32 elements (B*T*dim)");
+  if (N == 0) return ok();
+  if ((rc = ensure_device(ctx))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  KScope ks(ctx, EMB_K_ATOMIC, st);
+  hipError_t e = launch_atomic_reduce(ctx->g, offsets, itype, N, B, pool, dY, inverse, num_unique, reduced_grad, st);
+  if (e != hipSuccess) return hip_fail(e, "atomic reduce");
+  return ok();
+}
+
 int emb_check_device_error(emb_ctx* ctx, void* hip_stream) {
   if (!ctx) return fail(EMB_E_INVAL, "ctx is NULL");
   if (!ctx->dev_block) return ok();

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "emb.h"
 
 namespace emb {
@@ -124,6 +126,10 @@ hipError_t launch_reduce(const Geom& g, const DevCtx& dc, int mode, int N, int B
 hipError_t launch_combine(const Geom& g, const DevCtx& dc, int mode, int N, const WsLayout& L,
                           const char* ws, const uint32_t* unique_keys, float* grad_out, float lr,
                           float eps, hipStream_t st);
+// zero grad[0..U) and scatter-add every lookup's scaled dY row with fp32 atomics
+hipError_t launch_atomic_reduce(const Geom& g, const void* offsets, int itype, long long N, int B,
+                                int pool, const float* dY, const int32_t* inverse,
+                                const int32_t* num_unique, float* grad, hipStream_t st);
 // opt: 1 = SGD, 2 = Adagrad; reads grad_in[u] for u < *num_unique
 hipError_t launch_apply(const Geom& g, const DevCtx& dc, int opt, int N,
                         const uint32_t* unique_keys, const int32_t* num_unique,

@@ -38,7 +38,7 @@ EMB_OPT_SGD, EMB_OPT_ADAGRAD = 0, 1
 EMB_MAX_SLICES = 4
 
 KERNELS = ["init", "forward", "keys", "sort_hist", "sort_scan", "sort_scatter", "rle", "reduce",
-           "combine", "apply"]
+           "combine", "apply", "atomic"]
 
 DTYPE_CODE = {"f32": EMB_F32, "bf16": EMB_BF16, "f16": EMB_F16}
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
@@ -89,6 +89,8 @@ def lib() -> ctypes.CDLL:
     L.emb_backward_unique_reduce.restype = ctypes.c_int
     L.emb_backward_dedup.argtypes = [vp, vp, vp, i32, i64, i32, i32, vp, sz, vp, vp, vp, vp, vp]
     L.emb_backward_dedup.restype = ctypes.c_int
+    L.emb_backward_atomic_reduce.argtypes = [vp, vp, i32, i64, i32, i32, vp, vp, vp, vp, vp]
+    L.emb_backward_atomic_reduce.restype = ctypes.c_int
     L.emb_sparse_update.argtypes = [vp, i32, ctypes.c_float, ctypes.c_float, vp, vp, vp, vp]
     L.emb_sparse_update.restype = ctypes.c_int
     L.emb_last_error.argtypes = []
@@ -191,6 +193,13 @@ def emb_backward_dedup(ctx: int, indices, offsets, B: int, pool: str, ws, unique
         ctx, _ptr(indices), _ptr(offsets), _itype(indices), int(indices.numel()), int(B),
         POOL_CODE[pool], _ptr(ws), int(ws.numel() * ws.element_size()), _ptr(unique_keys),
         _ptr(counts), _ptr(inverse), _ptr(num_unique), _stream(stream)))
+
+
+def emb_backward_atomic_reduce(ctx: int, offsets, N: int, B: int, pool: str, dY, inverse, num_unique,
+                               reduced_grad, stream=None) -> None:
+    _check(lib().emb_backward_atomic_reduce(
+        ctx, _ptr(offsets), _itype(offsets), int(N), int(B), POOL_CODE[pool], _ptr(dY), _ptr(inverse),
+        _ptr(num_unique), _ptr(reduced_grad), _stream(stream)))
 
 
 def emb_sparse_update(ctx: int, opt: str, lr: float, eps: float, ws, dY=None, reduced_grad=None,
@@ -300,6 +309,10 @@ class EmbeddingTables:
     def dedup(self, indices, offsets, B: int, pool: str, bufs, stream=None) -> None:
         emb_backward_dedup(self.ctx, indices, offsets, B, pool, bufs["ws"], bufs["unique_keys"],
                            bufs["counts"], bufs["inverse"], bufs["num_unique"], stream)
+
+    def atomic_reduce(self, offsets, N: int, B: int, pool: str, dY, bufs, stream=None) -> None:
+        emb_backward_atomic_reduce(self.ctx, offsets, N, B, pool, dY, bufs["inverse"], bufs["num_unique"],
+                                   bufs["reduced_grad"], stream)
 
     def update(self, opt: str, lr: float, eps: float, bufs, dY=None, stream=None) -> None:
         emb_sparse_update(self.ctx, opt, lr, eps, bufs["ws"], dY, bufs["reduced_grad"], stream)

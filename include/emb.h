@@ -193,6 +193,18 @@ int emb_sparse_update(emb_ctx* ctx, int32_t opt, float lr, float eps,
                       const void* ws, const float* dY, const float* reduced_grad,
                       void* hip_stream);
 
+/* Evidence variant of the gradient reduction (atomics instead of sorted
+ * segments), for measuring the two against each other: zeroes
+ * reduced_grad[0..U) and adds scale_i * dY[b(i)][t(i)*dim ...] into
+ * reduced_grad[inverse[i]] for every lookup with fp32 atomic adds, one
+ * subgroup per bag (the bag's dY row is read once). inverse and num_unique
+ * come from a preceding dedup of the same batch. The result equals the
+ * sorted path's reduced_grad up to fp32 summation order, which here is not
+ * deterministic. emb_sparse_update with this reduced_grad applies it. */
+int emb_backward_atomic_reduce(emb_ctx* ctx, const void* offsets, int32_t itype, int64_t N,
+                               int32_t B, int32_t pool, const float* dY, const int32_t* inverse,
+                               const int32_t* num_unique, float* reduced_grad, void* hip_stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* emb_last_error(void);
 
@@ -213,7 +225,8 @@ int emb_check_device_error(emb_ctx* ctx, void* hip_stream);
 #define EMB_K_REDUCE        7   /* segmented reduce (+ fused update) */
 #define EMB_K_COMBINE       8   /* long-segment combine (+ update) */
 #define EMB_K_APPLY         9   /* update from a materialised gradient */
-#define EMB_K_COUNT        10
+#define EMB_K_ATOMIC       10   /* atomic reduction (evidence variant) */
+#define EMB_K_COUNT        11
 
 /* enable != 0: from now on every kernel launch of this context is
  * bracketed by HIP events recorded on the launch stream. */

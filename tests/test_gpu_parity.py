@@ -288,3 +288,31 @@ def test_dedup_ahead_on_second_stream_matches_serial():
     P.check_dedup(bufs2, u, c, inv)
     del Y
     tabs.close()
+
+
+@pytest.mark.parametrize("cfg_id", [2, 4, 5])
+def test_atomic_reduce_matches_oracle(cfg_id):
+    # the evidence variant: dedup, then fp32-atomic scatter-add of every
+    # lookup's gradient, then the update from the materialised gradient
+    cfg = W.make_config(cfg_id, **REDUCED[cfg_id])
+    batch = W.make_batch(cfg)
+    dY = W.make_dy(cfg)
+    _say(f"atomic cfg{cfg_id} N={batch.N}")
+    tabs = P.make_tables(cfg)
+    idx, off, dy = P.to_dev(batch, dY)
+    bufs = tabs.backward_buffers(batch.N, cfg.batch, with_grad=True)
+    E.emb_backward_unique_reduce(tabs.ctx, idx, off, cfg.batch, cfg.pool, dy, bufs["ws"], bufs["unique_keys"],
+                                 bufs["counts"], bufs["inverse"], bufs["num_unique"], None)
+    tabs.atomic_reduce(off, batch.N, cfg.batch, cfg.pool, dy, bufs)
+    torch.cuda.synchronize()
+    u, c, inv = P.oracle_dedup(cfg, batch)
+    U = P.check_dedup(bufs, u, c, inv)
+    g_ref, m_ref = P.grad_bounds(cfg, batch, dY, inv, U)
+    P.check_grad(bufs["reduced_grad"][:U].cpu().numpy(), g_ref, m_ref)
+    w_old = P.stored_init(cfg, u)
+    G_old = np.zeros_like(w_old) if cfg.opt == "adagrad" else None
+    tabs.update(cfg.opt, cfg.lr, cfg.eps, bufs)
+    torch.cuda.synchronize()
+    w_new, G_new = P.read_rows(tabs, cfg, u)
+    P.check_update(cfg, w_new, G_new, w_old, G_old, g_ref, m_ref)
+    tabs.close()
