@@ -113,6 +113,7 @@ struct RleArgs {
   int32_t* inverse;
   int32_t* seg_off;
   int4* desc;
+  int32_t* counts;
   int32_t* chunk_seg;
   int32_t* tile_first_seg;
   int32_t* tile_last_seg;
@@ -207,6 +208,7 @@ __global__ __launch_bounds__(256) void k_rle_write(RleArgs a) {
       a.unique_keys[seg] = key;
       a.seg_off[seg] = (int32_t)i;
     }
+    if (fl & (1u << (16 + k))) a.counts[seg] = (int32_t)i + 1 - seg_start;  // segment end
     if ((i % kChunk) == 0) a.tile_first_seg[i / kChunk] = seg;
     if ((i % kChunk) == kChunk - 1 || i == a.N - 1) a.tile_last_seg[i / kChunk] = seg;
     if (i == a.N - 1) a.seg_off[seg + 1] = a.N;
@@ -220,14 +222,6 @@ __global__ __launch_bounds__(256) void k_rle_write(RleArgs a) {
       a.chunk_seg[chk] = seg;
     }
   }
-}
-
-__global__ __launch_bounds__(256) void k_counts(const int32_t* __restrict__ seg_off,
-                                                const int32_t* __restrict__ num_unique,
-                                                int32_t* __restrict__ counts, int N) {
-  const int U = min(*num_unique, N);
-  for (int u = blockIdx.x * 256 + threadIdx.x; u < U; u += gridDim.x * 256)
-    counts[u] = seg_off[u + 1] - seg_off[u];
 }
 
 __global__ void k_set_empty(int32_t* num_unique, int32_t* num_chunks) {
@@ -252,15 +246,13 @@ hipError_t launch_rle(const uint64_t* sorted, int N, const WsLayout& L, char* ws
   a.inverse = o.inverse;
   a.seg_off = reinterpret_cast<int32_t*>(ws + L.seg_off);
   a.desc = reinterpret_cast<int4*>(ws + L.desc);
+  a.counts = o.counts;
   a.chunk_seg = reinterpret_cast<int32_t*>(ws + L.chunk_seg);
   a.tile_first_seg = reinterpret_cast<int32_t*>(ws + L.tile_first_seg);
   a.tile_last_seg = reinterpret_cast<int32_t*>(ws + L.tile_last_seg);
   a.sorted_bag = reinterpret_cast<int32_t*>(ws + L.sorted_bag);
   a.N = N;
   hipLaunchKernelGGL(k_rle_write, dim3(nblk), dim3(256), 0, st, a);
-  const int cgrid = ceil_div(N, 256) < 8192 ? ceil_div(N, 256) : 8192;
-  hipLaunchKernelGGL(k_counts, dim3(cgrid), dim3(256), 0, st,
-                     reinterpret_cast<const int32_t*>(ws + L.seg_off), o.num_unique, o.counts, N);
   return hipGetLastError();
 }
 
