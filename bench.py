@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--reduce", choices=["fused", "atomic"], default="fused",
                     help="fused: sorted-segment reduction fused with the optimizer (the path); atomic: the "
                          "evidence variant, fp32 atomics into a materialised gradient, then the update")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="only time plain library kernels (copy, read-only sum, fill) over 4 GiB: the "
+                         "practical HBM ceiling the path's kernels are compared with")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times) and exit: the reference "
                          "point for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -91,6 +94,27 @@ def main() -> int:
     import numpy as np
     import torch
     from dataclasses import replace
+
+    if args.ceiling:
+        n = (4 << 30) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        acc = torch.empty((), dtype=torch.float32, device="cuda")
+        res = {}
+        for name, nbytes, fn in (("copy", 2 * n * 4, lambda: dst.copy_(src)),
+                                 ("read_sum", n * 4, lambda: torch.sum(src, dim=0, out=acc)),
+                                 ("fill", n * 4, lambda: dst.fill_(1.0))):
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(10):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            res[name + "_GBps"] = round(nbytes * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+        print(json.dumps({"ceiling": res, "bytes_per_buffer": n * 4}), flush=True)
+        return 0
 
     if args.calibrate_copy:
         n = args.calibrate_copy * (1 << 20) // 4

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
+#include <cstdlib>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -81,6 +82,8 @@ struct emb_ctx {
     const int32_t* num_unique = nullptr;
     bool valid = false;
   } dedup;
+  // cap on forward blocks (0 = one block per work unit), see ensure_device
+  int fwd_max_blocks = 0;
   // timing
   bool timing = false;
   std::vector<TimedLaunch> pending;
@@ -120,6 +123,13 @@ int ensure_device(emb_ctx* c) {
   }
   c->dev_block = p;
   c->device = dev;
+  // Forward grid cap: kFwdBlocksPerCU blocks per compute unit (EMB_FWD_BLOCKS_PER_CU
+  // overrides it; 0 = uncapped), leaving wave slots to a dedup on another stream.
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
+  int per_cu = kFwdBlocksPerCU;
+  if (const char* v = std::getenv("EMB_FWD_BLOCKS_PER_CU")) per_cu = std::atoi(v);
+  c->fwd_max_blocks = per_cu > 0 ? per_cu * cus : 0;
   c->dc.tables = reinterpret_cast<const DevTable*>(p);
   c->dc.row_off = reinterpret_cast<const uint32_t*>(static_cast<char*>(p) + ro_off);
   c->dc.err_flag = reinterpret_cast<int*>(static_cast<char*>(p) + err_off);
@@ -331,7 +341,8 @@ int emb_forward_pooled(emb_ctx* ctx, const void* indices, const void* offsets, i
   if ((rc = ensure_device(ctx))) return rc;
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   KScope ks(ctx, EMB_K_FORWARD, st);
-  hipError_t e = launch_forward(ctx->g, ctx->dc, indices, offsets, itype, N, B, pool, out, st);
+  hipError_t e = launch_forward(ctx->g, ctx->dc, indices, offsets, itype, N, B, pool, out,
+                                ctx->fwd_max_blocks, st);
   if (e != hipSuccess) return hip_fail(e, "forward kernel");
   return ok();
 }

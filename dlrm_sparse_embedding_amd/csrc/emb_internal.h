@@ -30,6 +30,9 @@ constexpr int kChunk = 128;
 constexpr int kL1Tiles = 32;
 constexpr int kChunk1 = kChunk * kL1Tiles;  // 4096 positions
 
+// Forward grid cap in blocks per compute unit (0 = uncapped).
+constexpr int kFwdBlocksPerCU = 0;
+
 // Radix sort / run-length tiles.
 constexpr int kSortThreads = 256;
 constexpr int kSortIPT = 8;
@@ -92,8 +95,10 @@ WsLayout ws_layout(const Geom& g, long long N, int B);
 hipError_t launch_init_slice(const Geom& g, const DevCtx& dc, int t, int s, int64_t rows, void* w,
                              float* state, uint64_t seed, hipStream_t st);
 
+// max_blocks > 0 caps the grid (the kernel strides over the rest)
 hipError_t launch_forward(const Geom& g, const DevCtx& dc, const void* indices, const void* offsets,
-                          int itype, long long N, int B, int pool, float* out, hipStream_t st);
+                          int itype, long long N, int B, int pool, float* out, int max_blocks,
+                          hipStream_t st);
 
 hipError_t launch_keys(const Geom& g, const DevCtx& dc, const void* indices, const void* offsets,
                        int itype, long long N, int B, int pool, const WsLayout& L, char* ws,

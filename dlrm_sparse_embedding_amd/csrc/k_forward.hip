@@ -18,7 +18,8 @@
 // The run's bag boundaries (bps+1 offsets) sit one per lane and are read by
 // lane shuffles (ds_bpermute), not by dependent global loads. Pooled rows
 // are written with non-temporal stores so the L2 keeps Zipf-hot table rows.
-// Blocks are remapped so each XCD works on a contiguous slice of the bags.
+// The grid may be capped (grid-stride over the work) so that the dedup, run
+// on a second stream, keeps some wave slots while the forward streams.
 #include "emb_device.h"
 
 namespace emb {
@@ -39,114 +40,112 @@ struct FwdArgs {
   int mean;
 };
 
-__device__ __forceinline__ long long shfl64(long long v, int src, int width) {
-  const int lo = __shfl((int)(v & 0xffffffffll), src, width);
-  const int hi = __shfl((int)(v >> 32), src, width);
-  return ((long long)hi << 32) | (unsigned int)lo;
-}
-
 // 8 waves/SIMD with 4 rows in flight per subgroup measured faster than 5
 // waves/SIMD with 8 rows (293 -> 277 us on the 26x4Mx128 one-hot workload).
+// Positions are 32-bit (N < 2^31 is validated) to stay within 64 VGPRs.
 template <int DT, typename IDX, int LPR>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_forward(FwdArgs a) {
   constexpr int CPL = 16 / Stor<DT>::kBytes;  // columns per lane
   constexpr int SGW = 256 / LPR;              // subgroups per block
   constexpr int U = 4;                        // rows in flight per subgroup
-  const int blk = xcd_remap(blockIdx.x, gridDim.x);
-  if (blk >= a.nblk) return;
   const int lsg = threadIdx.x & (LPR - 1);
-  const long long sg = (long long)blk * SGW + threadIdx.x / LPR;
-  if (sg >= a.total_sg) return;
+  const int N = (int)a.N;
+  // grid-stride over logical blocks: the grid may be capped below the work so
+  // that kernels on another stream (the dedup) keep wave slots
+  for (int blk = blockIdx.x; blk < a.nblk; blk += gridDim.x) {
+    const long long sg = (long long)blk * SGW + threadIdx.x / LPR;
+    if (sg >= a.total_sg) break;
 
-  const int t = (int)(sg / a.sg_per_table);
-  const int b0 = (int)(sg - (long long)t * a.sg_per_table) * a.bps;
-  const int nb = min(a.bps, a.B - b0);
-  const long long bag0 = (long long)t * a.B + b0;
+    const int t = (int)(sg / a.sg_per_table);
+    const int b0 = (int)(sg - (long long)t * a.sg_per_table) * a.bps;
+    const int nb = min(a.bps, a.B - b0);
+    const long long bag0 = (long long)t * a.B + b0;
 
-  // offsets are clamped into [0, N] so that malformed input can never index
-  // outside `indices`
-  long long my_off = 0;
-  if (lsg <= nb) my_off = min(max(ld_idx<IDX>(a.offsets, bag0 + lsg), 0ll), a.N);
-  const long long P0 = shfl64(my_off, 0, LPR);
-  const long long P1 = shfl64(my_off, nb, LPR);
+    // offsets are clamped into [0, N] so that malformed input can never index
+    // outside `indices`; lane j holds the offset of bag b0 + j
+    int my_off = 0;
+    if (lsg <= nb) my_off = (int)min(max(ld_idx<IDX>(a.offsets, bag0 + lsg), 0ll), (long long)N);
+    const int P0 = __shfl(my_off, 0, LPR);
+    const int P1 = __shfl(my_off, nb, LPR);
 
-  const long long ro = a.row_off[t];
-  const long long rows_t = (long long)a.row_off[t + 1] - ro;
-  const int c0 = lsg * CPL;
-  const bool act = c0 < a.D;
-  const int s = act ? c0 / a.Dsl : 0;
-  const int cs = c0 - s * a.Dsl;
-  const char* wbase =
-      reinterpret_cast<const char*>(a.tables[t].w[s]) + (size_t)cs * Stor<DT>::kBytes;
-  const size_t rstride = (size_t)a.Dsl * Stor<DT>::kBytes;
-  const size_t ostride = (size_t)a.T * a.D;
-  float* obase = a.out + (size_t)b0 * ostride + (size_t)t * a.D + c0;
+    const uint32_t ro = a.row_off[t];
+    const uint32_t rows_t = a.row_off[t + 1] - ro;
+    const int c0 = lsg * CPL;
+    const bool act = c0 < a.D;
+    const int s = act ? c0 / a.Dsl : 0;
+    const int cs = c0 - s * a.Dsl;
+    const char* wbase =
+        reinterpret_cast<const char*>(a.tables[t].w[s]) + (size_t)cs * Stor<DT>::kBytes;
+    const size_t rstride = (size_t)a.Dsl * Stor<DT>::kBytes;
+    const size_t ostride = (size_t)a.T * a.D;
+    float* obase = a.out + (size_t)b0 * ostride + (size_t)t * a.D + c0;
 
-  float acc[CPL];
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
-
-  int cur = 0;
-  long long cur_start = P0;
-  long long cur_end = shfl64(my_off, nb > 0 ? 1 : 0, LPR);
-  int bad = 0;
-
-  auto flush = [&](long long L) {
-    float* o = obase + (size_t)cur * ostride;
-    if (act) {
-      if (a.mean && L > 0) {
-        const float fl = (float)L;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) acc[c] = __fdiv_rn(acc[c], fl);
-      }
-#pragma unroll
-      for (int c = 0; c < CPL; c += 4) {
-        f4 v = {acc[c], acc[c + 1], acc[c + 2], acc[c + 3]};
-        __builtin_nontemporal_store(v, reinterpret_cast<f4*>(o + c));
-      }
-    }
+    float acc[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
-  };
 
-  for (long long p = P0; p < P1; p += U) {
-    u4 v[U];
+    int cur = 0;
+    int cur_start = P0;
+    int cur_end = __shfl(my_off, nb > 0 ? 1 : 0, LPR);
+    int bad = 0;
+
+    auto flush = [&](int L) {
+      float* o = obase + (size_t)cur * ostride;
+      if (act) {
+        if (a.mean && L > 0) {
+          const float fl = (float)L;
 #pragma unroll
-    for (int k = 0; k < U; ++k) {
-      v[k] = u4{0u, 0u, 0u, 0u};
-      if (p + k < P1) {
-        const long long r = ld_idx<IDX>(a.indices, p + k);
-        if (r >= 0 && r < rows_t) {
-          if (act) v[k] = *reinterpret_cast<const u4*>(wbase + (size_t)r * rstride);
-        } else {
-          bad = 1;
+          for (int c = 0; c < CPL; ++c) acc[c] = __fdiv_rn(acc[c], fl);
+        }
+#pragma unroll
+        for (int c = 0; c < CPL; c += 4) {
+          f4 v = {acc[c], acc[c + 1], acc[c + 2], acc[c + 3]};
+          __builtin_nontemporal_store(v, reinterpret_cast<f4*>(o + c));
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+    };
+
+    for (int p = P0; p < P1; p += U) {
+      u4 v[U];
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        v[k] = u4{0u, 0u, 0u, 0u};
+        if (p + k < P1) {
+          const long long r = ld_idx<IDX>(a.indices, p + k);
+          if (r >= 0 && r < (long long)rows_t) {
+            if (act) v[k] = *reinterpret_cast<const u4*>(wbase + (size_t)r * rstride);
+          } else {
+            bad = 1;
+          }
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        if (p + k < P1) {
+          while (p + k >= cur_end && cur + 1 < nb) {
+            flush(cur_end - cur_start);
+            ++cur;
+            cur_start = cur_end;
+            cur_end = __shfl(my_off, cur + 1, LPR);
+          }
+          float f[CPL];
+          widen16<DT>(v[k], f);
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) acc[c] += f[c];
         }
       }
     }
-#pragma unroll
-    for (int k = 0; k < U; ++k) {
-      if (p + k < P1) {
-        while (p + k >= cur_end && cur + 1 < nb) {
-          flush(cur_end - cur_start);
-          ++cur;
-          cur_start = cur_end;
-          cur_end = shfl64(my_off, cur + 1, LPR);
-        }
-        float f[CPL];
-        widen16<DT>(v[k], f);
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) acc[c] += f[c];
-      }
+    // the bag in progress, then any empty bags that close the run
+    while (cur < nb) {
+      flush(cur_end - cur_start);
+      ++cur;
+      cur_start = cur_end;
+      cur_end = __shfl(my_off, min(cur + 1, nb), LPR);
     }
+    if (bad && lsg == 0) atomicOr(a.err, 1);
   }
-  // the bag in progress, then any empty bags that close the run
-  while (cur < nb) {
-    flush(cur_end - cur_start);
-    ++cur;
-    cur_start = cur_end;
-    cur_end = shfl64(my_off, min(cur + 1, nb), LPR);
-  }
-  if (bad && lsg == 0) atomicOr(a.err, 1);
 }
 
 #define FWD_LAUNCH(DT, IDX, LPR)                                                        \
@@ -171,7 +170,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
   }
 
 hipError_t launch_forward(const Geom& g, const DevCtx& dc, const void* indices, const void* offsets,
-                          int itype, long long N, int B, int pool, float* out, hipStream_t st) {
+                          int itype, long long N, int B, int pool, float* out, int max_blocks,
+                          hipStream_t st) {
   if (B == 0 || g.T == 0) return hipSuccess;
   const int cpl = 16 / (g.dtype == EMB_F32 ? 4 : 2);
   int lpr = next_pow2((g.D + cpl - 1) / cpl);
@@ -200,7 +200,7 @@ hipError_t launch_forward(const Geom& g, const DevCtx& dc, const void* indices, 
   const int sgw = 256 / lpr;
   args.nblk = (int)((args.total_sg + sgw - 1) / sgw);
   args.mean = pool == EMB_POOL_MEAN;
-  const int grid = round_up8(args.nblk);
+  const int grid = max_blocks > 0 && max_blocks < args.nblk ? max_blocks : args.nblk;
   switch (g.dtype) {
     case EMB_F32:
       FWD_IDX_SWITCH(EMB_F32)

@@ -17,7 +17,7 @@
 //
 // Work split. Segments are cut into chunks (at segment starts and every
 // kChunk sorted positions). One subgroup of LPR lanes (4 fp32 columns per
-// lane, so a dY row is one coalesced access) reduces one chunk, keeping 8 dY
+// lane, so a dY row is one coalesced access) reduces one chunk, keeping 6 dY
 // rows in flight; a chunk that is a whole segment applies the optimizer
 // right there with the weight (and state) row prefetched before the dY loop,
 // so the reduced gradient never leaves VGPRs. A segment longer than a tile
@@ -129,7 +129,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
   extern __shared__ uint32_t s_ro[];
   for (int i = threadIdx.x; i <= a.T; i += 256) s_ro[i] = a.row_off[i];
   __syncthreads();
-  constexpr int U = 8;
+  // dY rows in flight: the largest count that fits 64 VGPRs without spills at
+  // 8 waves/SIMD (spills cost scratch traffic in HBM: measured ~270 MB/launch)
+  constexpr int U = (MODE == 2 && MEAN) ? 4 : 6;
   constexpr int SGW = 256 / LPR;
   const int lsg = threadIdx.x & (LPR - 1);
   const int c0 = lsg * 4;
