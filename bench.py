@@ -42,7 +42,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, help="workload 1..5 (3 = the headline)")
     ap.add_argument("--batches", type=int, default=4)
-    ap.add_argument("--cpu-sample", type=int, default=32768, help="samples of batch 0 the oracle runs on")
+    ap.add_argument("--cpu-sample", type=int, default=0,
+                    help="samples per batch the oracle runs on (0 = the whole batch)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="the oracle runs on successive cycled batches until this much CPU time is spent")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--uniform-keys", action="store_true", help="control run: uniform keys instead of Zipf")
     ap.add_argument("--schedule", choices=["overlap", "serial"], default="overlap",
@@ -216,13 +219,17 @@ def main() -> int:
         total = t0.elapsed_time(t1)
         fwd = sum(e[0].elapsed_time(e[1]) for e in ev)
         bwd = sum(e[1].elapsed_time(e[2]) for e in ev)
+        per_step = sorted(e[0].elapsed_time(e[2]) for e in ev)
         print(f"[bench] {sched}: {K} steps {total:.3f} ms (wall {wall * 1e3:.1f} ms)", file=sys.stderr, flush=True)
-        return total, fwd, bwd
+        return total, fwd, bwd, per_step
 
     K = args.steps
     other = "serial" if args.schedule == "overlap" else "overlap"
-    total_ms, fwd_ms, bwd_ms = timed(args.schedule, K)
-    other_ms, _, _ = timed(other, K)
+    total_ms, fwd_ms, bwd_ms, per_step = timed(args.schedule, K)
+    other_ms, _, _, _ = timed(other, K)
+
+    def pct(q):
+        return round(float(np.percentile(np.asarray(per_step), q)), 4)
 
     # algorithmic bytes per step (SURVEY-style formula, actual N and U)
     ib = 4 if host_batches[0].indices.dtype == np.int32 else 8
@@ -282,7 +289,7 @@ def main() -> int:
     # CPU oracle on a bounded sample of batch 0
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, host_batches[0], dY_host, args.cpu_sample)
+        cpu = cpu_baseline(cfg, host_batches, dY_host, args.cpu_sample, args.cpu_seconds)
 
     ms_step = total_ms / K
     out = {
@@ -293,6 +300,7 @@ def main() -> int:
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_p10_p50_p90": [pct(10), pct(50), pct(90)],
         "schedule": args.schedule,
         "reduce": args.reduce,
         f"ms_per_step_{other}": round(other_ms / K, 4),
@@ -330,46 +338,70 @@ def main() -> int:
     return 0
 
 
-def cpu_baseline(cfg, batch, dY, n_samples):
-    """The oracle, as it stands, on the first n_samples samples of the batch
-    (every table): forward, dedup, reduced gradient, optimizer step."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, batches, dY, n_samples, seconds):
+    """The oracle, as it stands, on the cycled batches of the workload (the
+    first n_samples samples of each, every table; 0 = whole batches): forward,
+    dedup, reduced gradient, optimizer step. Batches are taken in turn until
+    `seconds` of CPU time have been spent. numpy's thread pools are held to one
+    thread, so `cores` is what it used."""
     import numpy as np
+    from threadpoolctl import threadpool_limits
 
     import oracle as O
     from dlrm_sparse_embedding_amd import workloads as W
 
     B = cfg.batch
-    s = np.arange(min(n_samples, B))
-    lens, keys = [], []
-    for t in range(cfg.T):
-        a, b = int(batch.offsets[t * B]), int(batch.offsets[t * B + len(s)])
-        lens.append(np.diff(batch.offsets[t * B:t * B + len(s) + 1].astype(np.int64)))
-        keys.append(batch.indices[a:b])
-    sub = W.make_batch_from_lengths(lens, keys, len(s))
-    dYs = np.ascontiguousarray(dY[s])
-    # untimed preparation: the stored contents of the touched rows
-    otabs = [O.TouchedRows(cfg.init_seed, t, cfg.dim, cfg.dtype,
-                           sub.indices[int(sub.offsets[t * len(s)]):int(sub.offsets[(t + 1) * len(s)])])
-             for t in range(cfg.T)]
+    ns = B if n_samples <= 0 else min(n_samples, B)
     ro = cfg.row_offset()
-    t0 = time.perf_counter()
-    O.pooled_forward(otabs, sub.indices, sub.offsets, cfg.T, len(s), cfg.dim, cfg.pool)
-    g = O.global_keys(sub.indices, sub.offsets, ro, cfg.T, len(s))
-    u, c, inv = O.dedup(g)
-    gU = O.reduced_grad(dYs, sub.offsets, cfg.T, len(s), cfg.dim, cfg.pool, inv, len(u))
-    t_of = np.searchsorted(ro, u, side="right") - 1
-    w_old = np.concatenate([otabs[t][u[t_of == t] - ro[t]] for t in range(cfg.T)])
-    G_old = np.zeros_like(w_old) if cfg.opt == "adagrad" else None
-    O.update_rows(w_old, G_old, gU, cfg.opt, cfg.lr, cfg.eps, cfg.dtype)
-    el = time.perf_counter() - t0
+    total_n = total_u = 0
+    el = 0.0
+    used = 0
+    with threadpool_limits(limits=1):
+        for batch in batches:
+            lens, keys = [], []
+            for t in range(cfg.T):
+                a, b = int(batch.offsets[t * B]), int(batch.offsets[t * B + ns])
+                lens.append(np.diff(batch.offsets[t * B:t * B + ns + 1].astype(np.int64)))
+                keys.append(batch.indices[a:b])
+            sub = W.make_batch_from_lengths(lens, keys, ns)
+            dYs = np.ascontiguousarray(dY[:ns])
+            # untimed preparation: the stored contents of the touched rows
+            otabs = [O.TouchedRows(cfg.init_seed, t, cfg.dim, cfg.dtype,
+                                   sub.indices[int(sub.offsets[t * ns]):int(sub.offsets[(t + 1) * ns])])
+                     for t in range(cfg.T)]
+            t0 = time.perf_counter()
+            O.pooled_forward(otabs, sub.indices, sub.offsets, cfg.T, ns, cfg.dim, cfg.pool)
+            g = O.global_keys(sub.indices, sub.offsets, ro, cfg.T, ns)
+            u, c, inv = O.dedup(g)
+            gU = O.reduced_grad(dYs, sub.offsets, cfg.T, ns, cfg.dim, cfg.pool, inv, len(u))
+            t_of = np.searchsorted(ro, u, side="right") - 1
+            w_old = np.concatenate([otabs[t][u[t_of == t] - ro[t]] for t in range(cfg.T)])
+            G_old = np.zeros_like(w_old) if cfg.opt == "adagrad" else None
+            O.update_rows(w_old, G_old, gU, cfg.opt, cfg.lr, cfg.eps, cfg.dtype)
+            el += time.perf_counter() - t0
+            total_n += sub.N
+            total_u += len(u)
+            used += 1
+            if el >= seconds:
+                break
     try:
         avail = len(os.sched_getaffinity(0))
     except Exception:
         avail = os.cpu_count()
-    return {"value": round(sub.N / el, 1), "unit": "lookups/s", "cores": 1, "kind": "oracle",
-            "sample": (f"first {len(s)} samples of the batch, all {cfg.T} tables ({sub.N} lookups, "
-                       f"{len(u)} unique keys): forward + dedup + reduce + optimizer, {el:.2f} s, "
-                       f"single-threaded numpy; {avail} host cores available")}
+    return {"value": round(total_n / el, 1), "unit": "lookups/s", "cores": 1, "kind": "oracle",
+            "sample": (f"{used} batch(es) x first {ns} samples, all {cfg.T} tables ({total_n} lookups, "
+                       f"{total_u} unique keys in total): forward + dedup + reduce + optimizer, {el:.2f} s, "
+                       f"single-threaded numpy on {cpu_model()}; {avail} host cores available")}
 
 
 if __name__ == "__main__":

@@ -596,7 +596,13 @@ int emb_check_device_error(emb_ctx* ctx, void* hip_stream) {
     const int zero = 0;
     e = hipMemcpy(ctx->dc.err_flag, &zero, sizeof(int), hipMemcpyHostToDevice);
     if (e != hipSuccess) return hip_fail(e, "hipMemcpy(clear err flag)");
-    return fail(EMB_E_BOUNDS, "a kernel saw an index outside [0, rows)");
+    if (flag & 1) {
+      return fail(EMB_E_BOUNDS, (flag & 2) ? "a kernel saw an index outside [0, rows), and offsets that "
+                                             "break the CSR contract"
+                                           : "a kernel saw an index outside [0, rows)");
+    }
+    return fail(EMB_E_INVAL, "offsets break the CSR contract (offsets[0] = 0, non-decreasing, "
+                             "offsets[T*B] = N)");
   }
   return ok();
 }

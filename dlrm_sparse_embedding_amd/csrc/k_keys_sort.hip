@@ -41,31 +41,68 @@ struct KeysArgs {
   uint32_t total_rows;
 };
 
+// One wave per group of 64 consecutive bags (table-major bag ids g0 ..
+// g0+63). Lane j holds bag g0+j's clamped range [s_j, e_j); the wave then
+// walks the group's positions 64 at a time, so index loads and key / bag
+// stores are coalesced whatever the bag lengths, and finds each position's
+// bag as the last lane whose start is <= the position (a 6-step binary search
+// over the lanes' starts by cross-lane reads).
+//
+// Group g owns positions [lo_g, hi_g) with lo_g = clamp(offsets[g0]) (0 for
+// the first group) and hi_g = lo of the next group (N for the last). These
+// intervals cover [0, N) for any offsets, so every position gets an in-range
+// key and bag even when the offsets break the contract; such offsets raise
+// bit 2 of the error flag, an index outside its table bit 1.
 template <typename IDX>
 __global__ __launch_bounds__(256) void k_keys(KeysArgs a) {
-  const long long bag = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (bag >= (long long)a.T * a.B) return;
-  const int t = (int)(bag / a.B);
-  // clamped into [0, N]: malformed offsets cannot index outside the buffers
-  const long long s = min(max(ld_idx<IDX>(a.offsets, bag), 0ll), a.N);
-  const long long e = min(max(ld_idx<IDX>(a.offsets, bag + 1), s), a.N);
-  const uint32_t ro = a.row_off[t];
-  const long long rows_t = (long long)a.row_off[t + 1] - ro;
-  if (a.inv_len) a.inv_len[bag] = e > s ? __fdiv_rn(1.0f, (float)(e - s)) : 0.f;
-  bool bad = false;
-  for (long long p = s; p < e; ++p) {
-    const long long r = ld_idx<IDX>(a.indices, p);
-    uint32_t key;
-    if (r >= 0 && r < rows_t) {
-      key = ro + (uint32_t)r;
-    } else {
-      key = a.total_rows;  // sentinel: sorts last, never applied
-      bad = true;
-    }
-    a.keys[p] = ((uint64_t)key << 32) | (uint32_t)p;
-    a.bag_of_pos[p] = (int32_t)bag;
+  const long long nbags = (long long)a.T * a.B;
+  const long long g0 = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * 64;
+  if (g0 >= nbags) return;  // uniform over the wave
+  const int lane = threadIdx.x & 63;
+  const long long bag = g0 + lane;
+  const int N = (int)a.N;
+  int s = N, e = N, nxt = N, flag = 0;  // lanes past the last bag: empty at N
+  uint32_t ro = 0, rows = 0;
+  if (bag < nbags) {
+    const int t = (int)(bag / a.B);
+    const long long o0 = ld_idx<IDX>(a.offsets, bag);
+    const long long o1 = ld_idx<IDX>(a.offsets, bag + 1);
+    if (o0 < 0 || o1 < o0 || o1 > N || (bag == 0 && o0 != 0) || (bag == nbags - 1 && o1 != N))
+      flag |= 2;
+    s = (int)min(max(o0, 0ll), (long long)N);
+    nxt = (int)min(max(o1, 0ll), (long long)N);
+    e = max(nxt, s);
+    ro = a.row_off[t];
+    rows = a.row_off[t + 1] - ro;
+    if (a.inv_len) a.inv_len[bag] = e > s ? __fdiv_rn(1.0f, (float)(e - s)) : 0.f;
   }
-  if (bad) atomicOr(a.err, 1);
+  const int lo = g0 == 0 ? 0 : __shfl(s, 0);
+  const int hi = g0 + 64 < nbags ? __shfl(nxt, 63) : N;
+  for (int p0 = lo; p0 < hi; p0 += 64) {  // trip count uniform: every lane joins the cross-lane reads
+    const int p = p0 + lane;
+    int j = 0;
+#pragma unroll
+    for (int st = 32; st >= 1; st >>= 1) {
+      if (__shfl(s, j + st) <= p) j += st;
+    }
+    const int sj = __shfl(s, j), ej = __shfl(e, j);
+    const uint32_t roj = __shfl(ro, j), rowsj = __shfl(rows, j);
+    if (p < hi) {
+      uint32_t key = a.total_rows;  // sentinel: sorts last, never applied
+      if (p < sj || p >= ej) {
+        flag |= 2;
+      } else {
+        const long long r = ld_idx<IDX>(a.indices, p);
+        if (r >= 0 && r < (long long)rowsj)
+          key = roj + (uint32_t)r;
+        else
+          flag |= 1;
+      }
+      a.keys[p] = ((uint64_t)key << 32) | (uint32_t)p;
+      a.bag_of_pos[p] = (int32_t)(g0 + j);
+    }
+  }
+  if (flag) atomicOr(a.err, flag);
 }
 
 hipError_t launch_keys(const Geom& g, const DevCtx& dc, const void* indices, const void* offsets,
@@ -84,7 +121,7 @@ hipError_t launch_keys(const Geom& g, const DevCtx& dc, const void* indices, con
   a.B = B;
   a.total_rows = g.total_rows;
   const long long bags = (long long)g.T * B;
-  const int grid = ceil_div(bags, 256);
+  const int grid = ceil_div(bags, 256);  // 4 waves x 64 bags per block
   if (grid == 0) return hipSuccess;
   if (itype == EMB_I32)
     hipLaunchKernelGGL(k_keys<int32_t>, dim3(grid), dim3(256), 0, st, a);
@@ -100,6 +137,20 @@ hipError_t launch_keys(const Geom& g, const DevCtx& dc, const void* indices, con
 template <int RB>
 __device__ __forceinline__ uint32_t digit_of(uint64_t x, int shift) {
   return (uint32_t)(x >> (32 + shift)) & ((1u << RB) - 1u);
+}
+
+// Mask of the wave's lanes that are valid and hold the same RB-bit digit as
+// this lane (one ballot per digit bit).
+template <int RB>
+__device__ __forceinline__ uint64_t digit_peers(uint32_t d, bool valid) {
+  uint64_t peers = __ballot(valid);
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    const bool bit = (d >> b) & 1u;
+    const uint64_t bb = __ballot(bit);
+    peers &= bit ? bb : ~bb;
+  }
+  return peers;
 }
 
 // Exclusive scan over R = 256 * PER digits held PER-per-thread (thread i owns
@@ -130,10 +181,16 @@ __global__ __launch_bounds__(256) void k_sort_hist(const uint64_t* __restrict__ 
   for (int d = threadIdx.x; d < R; d += 256) h[d] = 0;
   __syncthreads();
   const long long base = (long long)blockIdx.x * kSortTile;
+  // equal digits of a wave are counted by one LDS add from their first lane:
+  // skewed keys put many lanes on one bin, which would serialise per-lane adds
+  const uint64_t lt = lanemask_lt();
 #pragma unroll
   for (int k = 0; k < kSortIPT; ++k) {
     const long long i = base + k * 256 + threadIdx.x;
-    if (i < N) atomicAdd(&h[digit_of<RB>(keys[i], shift)], 1u);
+    const bool valid = i < N;
+    const uint32_t d = valid ? digit_of<RB>(keys[i], shift) : 0u;
+    const uint64_t peers = digit_peers<RB>(d, valid);
+    if (valid && (peers & lt) == 0) atomicAdd(&h[d], (uint32_t)__popcll(peers));
   }
   __syncthreads();
   for (int d = threadIdx.x; d < R; d += 256) ghist[(size_t)d * nblk + blockIdx.x] = h[d];
@@ -213,13 +270,7 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const uint64_t* __restrict
   for (int k = 0; k < kSortIPT; ++k) {
     const bool valid = base + k * 64 + lane < N;
     const uint32_t d = digit_of<RB>(item[k], shift);
-    uint64_t peers = __ballot(valid);
-#pragma unroll
-    for (int b = 0; b < RB; ++b) {
-      const bool bit = (d >> b) & 1u;
-      const uint64_t bb = __ballot(bit);
-      peers &= bit ? bb : ~bb;
-    }
+    const uint64_t peers = digit_peers<RB>(d, valid);
     const uint32_t before = (uint32_t)__popcll(peers & lt);
     uint32_t basev = 0;
     if (valid) basev = s_wcnt[wave][d];

@@ -208,9 +208,15 @@ int emb_backward_atomic_reduce(emb_ctx* ctx, const void* offsets, int32_t itype,
 /* Message of the last failed call on this thread ("" if none). */
 const char* emb_last_error(void);
 
-/* Synchronises hip_stream, then returns EMB_E_BOUNDS if any kernel of this
- * context saw an out-of-range index since the last check (and clears the
- * flag), else EMB_OK. */
+/* Synchronises hip_stream, then reports (and clears) what the kernels of
+ * this context flagged since the last check: EMB_E_BOUNDS if one saw an
+ * index outside [0, rows_t); else EMB_E_INVAL if the backward's key build
+ * saw offsets that break the CSR contract above (offsets[0] != 0, a
+ * decreasing step, or offsets[T*B] != N); else EMB_OK. Malformed offsets
+ * never make a kernel access memory outside the caller's buffers: every
+ * kernel clamps offsets into [0, N], and the key build still gives every
+ * position in [0, N) an in-range key or the never-applied sentinel, but the
+ * results of such a call are unspecified. */
 int emb_check_device_error(emb_ctx* ctx, void* hip_stream);
 
 /* ---- measurement ------------------------------------------------------ */

@@ -224,6 +224,44 @@ def test_out_of_range_index_flagged_not_applied():
     tabs.close()
 
 
+@pytest.mark.parametrize("case", ["decreasing", "short_end", "long_end", "nonzero_start"])
+def test_malformed_offsets_flagged(case):
+    # offsets that break the CSR contract: the backward's key build reports
+    # EMB_E_INVAL through the device flag; every kernel clamps offsets into
+    # [0, N], so the whole step still runs inside the caller's buffers
+    cfg = _custom_cfg([50, 60], B=8, opt="sgd")
+    rng = np.random.default_rng(11)
+    lens = [rng.integers(0, 4, 8), rng.integers(0, 4, 8)]
+    keys = [rng.integers(0, 50, int(lens[0].sum())), rng.integers(0, 60, int(lens[1].sum()))]
+    batch = W.make_batch_from_lengths(lens, keys, 8)
+    off = batch.offsets.copy()
+    N = batch.N
+    if case == "decreasing":
+        off[5] = off[7] + 1
+        off[6] = 0
+    elif case == "short_end":
+        off[-1] = N - 3
+        off[-2] = min(off[-2], N - 3)
+    elif case == "long_end":
+        off[-1] = N + 5
+    else:
+        off[0] = 2
+    _say("malformed offsets", case)
+    tabs = P.make_tables(cfg)
+    idx = torch.from_numpy(batch.indices).cuda()
+    offd = torch.from_numpy(off).cuda()
+    dy = torch.ones((8, 32), dtype=torch.float32, device="cuda")
+    tabs.forward(idx, offd, 8, "mean")
+    bufs = tabs.backward_buffers(N, 8, with_grad=False)
+    tabs.backward(idx, offd, 8, "mean", dy, bufs)
+    tabs.update("sgd", 0.5, 0.0, bufs, dY=dy)
+    with pytest.raises(E.EmbError) as ei:
+        tabs.check_device_error()
+    assert ei.value.code == E.EMB_E_INVAL
+    tabs.check_device_error()                # flag was cleared
+    tabs.close()
+
+
 def test_two_adagrad_steps():
     cfg = W.make_config(2, batch=3000)
     b1, b2 = W.make_batch(cfg, k=0), W.make_batch(cfg, k=1)
