@@ -32,6 +32,12 @@ What is computed, and where the pages define it
   fp32 operation, in exactly that order. The result is rounded to the storage
   type with round-to-nearest-even (bf16/fp16); the stored low-precision value
   is the only copy of the weight.
+* FP32 master weights (same slide): read as the scheme in which the optimizer
+  keeps an fp32 master copy of every low-precision table and, each iteration,
+  updates the master in fp32 and casts it to the low-precision weights the
+  lookups read. Written out as: m' = the fp32 optimizer step of m, and the
+  stored copy = round-to-nearest-even(m'). The stored copy is never read by
+  the update.
 * Untouched rows -- a dense step with g = 0 and G = 0 leaves w and G bit for
   bit unchanged, so only touched rows are computed.
 * Table contents -- synthetic: each element is a counter hash of (seed, table,
@@ -47,7 +53,7 @@ __all__ = [
     "splitmix64", "init_values", "bf16_bits_rne", "bf16_bits_to_f32", "f16_rne",
     "to_storage", "TouchedRows", "pooled_forward", "global_keys", "dedup",
     "bag_of_positions", "reduced_grad", "sgd_step", "adagrad_step",
-    "update_rows",
+    "update_rows", "update_rows_master",
 ]
 
 _U64 = np.uint64
@@ -283,3 +289,22 @@ def update_rows(w_stored: np.ndarray, G: np.ndarray | None, g: np.ndarray, opt: 
     else:
         raise ValueError(opt)
     return to_storage(w1, dtype), G1
+
+
+def update_rows_master(master: np.ndarray, G: np.ndarray | None, g: np.ndarray, opt: str,
+                       lr: float, eps: float, dtype: str):
+    """One optimizer step on touched rows of a table kept as an fp32 master
+    plus a low-precision copy (GTC 2022 deck, slide "WEIGHT CONVERSION FOR
+    MIXED PRECISION TRAINING"): the fp32 step runs on the master, and the copy
+    is the master rounded to the storage type (RNE). Returns
+    (master', copy', G'), the copy widened to fp32."""
+    m32 = np.asarray(master, dtype=np.float32)
+    if opt == "sgd":
+        m1, G1 = sgd_step(m32, g, lr), G
+    elif opt == "adagrad":
+        if G is None:
+            raise ValueError("adagrad needs its accumulator")
+        m1, G1 = adagrad_step(m32, G, g, lr, eps)
+    else:
+        raise ValueError(opt)
+    return m1, to_storage(m1, dtype), G1

@@ -474,3 +474,77 @@ def test_low_precision_update_rounds_rne():
         got, _ = O.update_rows(w, None, g, "sgd", 0.01, 0.0, dt)
         ref = torch.from_numpy(O.sgd_step(w, g, 0.01)).to(torch.bfloat16 if dt == "bf16" else torch.float16).float().numpy()
         assert np.array_equal(got, ref)
+
+
+# ---------------------------------------------------------------------------
+# FP32 master weights + low-precision copy
+# ---------------------------------------------------------------------------
+
+def _master_pin_ok(step, opt, dt, seed=0, steps=3):
+    """`steps` optimizer steps on an fp32 master against torch.optim on an fp32
+    parameter (the library routine), and the copy against torch's RNE cast of
+    the oracle's own master."""
+    w, _, tr = _dense_opt_case(seed)
+    lr, eps = 0.01, 1e-8
+    rng = np.random.default_rng(seed + 100)
+    p = torch.nn.Parameter(torch.from_numpy(w.copy()))
+    o = (torch.optim.SGD([p], lr=lr) if opt == "sgd"
+         else torch.optim.Adagrad([p], lr=lr, eps=eps, initial_accumulator_value=0.0))
+    m = w[tr].copy()
+    G = np.zeros_like(m) if opt == "adagrad" else None
+    ok = True
+    for _ in range(steps):
+        g = np.zeros_like(w)
+        g[tr] = rng.standard_normal((len(tr), w.shape[1])).astype(np.float32)
+        p.grad = torch.from_numpy(g.copy())
+        o.step()
+        m, copy, G = step(m, G, g[tr], opt, lr, eps, dt)
+        tdt = torch.bfloat16 if dt == "bf16" else torch.float16
+        ok = ok and np.array_equal(copy, torch.from_numpy(np.asarray(m, np.float32)).to(tdt).float().numpy())
+    ref = p.detach().numpy()[tr]
+    # torch fuses lr*g into the subtraction; per step the two differ by an ulp
+    # of the operands' magnitude
+    scale = np.maximum(np.abs(w[tr]), np.abs(ref - w[tr]))
+    ok = ok and _f32_scaled_close(m, ref, scale, 2 * steps)
+    return bool(ok)
+
+
+@pytest.mark.parametrize("opt", ["sgd", "adagrad"])
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_master_update_vs_torch_optim(opt, dt):
+    for seed in range(2):
+        assert _master_pin_ok(O.update_rows_master, opt, dt, seed)
+
+
+def test_master_keeps_updates_below_half_ulp():
+    # w = 1 in bf16 (ulp 2^-7): an SGD step of 1e-3 is below half an ulp, so a
+    # table whose bf16 value is the only copy never moves, while the fp32
+    # master accumulates the steps and its RNE copy moves once they add up
+    w = np.ones((4, 8), np.float32)
+    g = np.full_like(w, 0.1)
+    lr = 0.01
+    only = w.copy()
+    m = w.copy()
+    for k in range(1, 11):
+        only, _ = O.update_rows(only, None, g, "sgd", lr, 0.0, "bf16")
+        m, copy, _ = O.update_rows_master(m, None, g, "sgd", lr, 0.0, "bf16")
+        assert np.all(np.abs(m.astype(np.float64) - (1.0 - k * 1e-3)) <= k * 2.0 ** -23)
+    assert np.all(only == 1.0)
+    assert np.all(copy == np.float32(0.98828125))    # RNE of 0.99 in bf16
+
+
+def test_master_pin_catches_mistakes():
+    def steps_from_copy(m, G, g, opt, lr, eps, dt):     # updates the rounded copy
+        return O.update_rows_master(O.to_storage(m, dt), G, g, opt, lr, eps, dt)
+
+    def truncating_copy(m, G, g, opt, lr, eps, dt):        # bf16 by truncation
+        m1, _, G1 = O.update_rows_master(m, G, g, opt, lr, eps, dt)
+        c = ((np.asarray(m1, np.float32).view(np.uint32) >> 16) << 16).view(np.float32)
+        return m1, c, G1
+
+    def sign_flip(m, G, g, opt, lr, eps, dt):
+        return O.update_rows_master(m, G, -g, opt, lr, eps, dt)
+
+    assert not _master_pin_ok(steps_from_copy, "sgd", "bf16")
+    assert not _master_pin_ok(truncating_copy, "adagrad", "bf16")
+    assert not _master_pin_ok(sign_flip, "adagrad", "f16")
