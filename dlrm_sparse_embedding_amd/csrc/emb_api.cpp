@@ -109,6 +109,7 @@ int ensure_device(emb_ctx* c) {
     for (int s = 0; s < EMB_MAX_SLICES; ++s) {
       ht[t].w[s] = c->desc[t].weights[s];
       ht[t].g[s] = c->desc[t].state[s];
+      ht[t].m[s] = c->desc[t].master[s];
     }
   }
   uint32_t* hro = reinterpret_cast<uint32_t*>(host.data() + ro_off);
@@ -246,6 +247,9 @@ int emb_create_tables(const emb_table_desc* descs, int32_t num_tables, emb_ctx**
     if (d0.dim * eb > 64 * 16)
       return fail(EMB_E_INVAL, "dim %d too wide (row bytes must be <= 1024)", d0.dim);
     const bool state0 = d0.state[0] != nullptr;
+    const bool master0 = d0.master[0] != nullptr;
+    if (master0 && d0.dtype == EMB_F32)
+      return fail(EMB_E_INVAL, "fp32 master weights are only for bf16 / fp16 tables");
     int64_t sum = 0;
     for (int t = 0; t < num_tables; ++t) {
       const emb_table_desc& d = descs[t];
@@ -263,6 +267,12 @@ int emb_create_tables(const emb_table_desc* descs, int32_t num_tables, emb_ctx**
           return fail(EMB_E_INVAL, "table %d: state must be given for all slices of all tables or none", t);
         if (used && d.state[s] && !aligned(d.state[s], 16))
           return fail(EMB_E_INVAL, "table %d: state[%d] not 16-byte aligned", t, s);
+        if (used && ((d.master[s] != nullptr) != master0))
+          return fail(EMB_E_INVAL, "table %d: master must be given for all slices of all tables or none", t);
+        if (used && d.master[s] && !aligned(d.master[s], 16))
+          return fail(EMB_E_INVAL, "table %d: master[%d] not 16-byte aligned", t, s);
+        if (!used && (d.state[s] || d.master[s] || d.weights[s]))
+          return fail(EMB_E_INVAL, "table %d: pointers of slice %d >= col_slices must be NULL", t, s);
       }
       sum += d.rows;
       if (sum >= (int64_t)0xFFFFFFFFll) return fail(EMB_E_INVAL, "sum of rows must be < 2^32 - 1");
@@ -278,6 +288,7 @@ int emb_create_tables(const emb_table_desc* descs, int32_t num_tables, emb_ctx**
     c->g.Dsl = Dsl;
     c->g.nslices = d0.col_slices;
     c->g.dtype = d0.dtype;
+    c->g.master = master0;
     c->g.total_rows = (uint32_t)sum;
     int bits = 1;
     while (bits < 32 && (1ull << bits) <= (uint64_t)sum) ++bits;
@@ -319,7 +330,7 @@ int emb_init_uniform(emb_ctx* ctx, uint64_t seed, void* hip_stream) {
     for (int s = 0; s < ctx->g.nslices; ++s) {
       KScope ks(ctx, EMB_K_INIT, st);
       hipError_t e = launch_init_slice(ctx->g, ctx->dc, t, s, ctx->desc[t].rows, ctx->desc[t].weights[s],
-                                       ctx->desc[t].state[s], seed, st);
+                                       ctx->desc[t].state[s], ctx->desc[t].master[s], seed, st);
       if (e != hipSuccess) return hip_fail(e, "init kernel");
     }
   }

@@ -12,11 +12,17 @@
 
 namespace emb {
 
-// Per-table device descriptor (weights / Adagrad state per column slice).
+// Per-table device descriptor (weights / Adagrad state / fp32 master per
+// column slice; state and master pointers are null when absent).
 struct DevTable {
   void* w[EMB_MAX_SLICES];
   float* g[EMB_MAX_SLICES];
+  float* m[EMB_MAX_SLICES];
 };
+
+// Update-kernel type code: the storage type, or'ed with kMasterBit when the
+// table is stepped from an fp32 master and the storage holds its RNE copy.
+constexpr int kMasterBit = 8;
 
 // Upper bound on tables per context: the row-offset array is staged in LDS
 // by the update kernels (4 bytes per entry).
@@ -55,6 +61,7 @@ struct Geom {
   int Dsl;        // width of one column slice
   int nslices;
   int dtype;      // EMB_F32 / EMB_BF16 / EMB_F16
+  bool master;    // fp32 master weights present (low-precision storage only)
   uint32_t total_rows;
   int key_bits;   // bits needed for keys 0..total_rows (total_rows = invalid-index sentinel)
 };
@@ -93,7 +100,7 @@ WsLayout ws_layout(const Geom& g, long long N, int B);
 // handled by the host layer around these calls.
 
 hipError_t launch_init_slice(const Geom& g, const DevCtx& dc, int t, int s, int64_t rows, void* w,
-                             float* state, uint64_t seed, hipStream_t st);
+                             float* state, float* master, uint64_t seed, hipStream_t st);
 
 // max_blocks > 0 caps the grid (the kernel strides over the rest)
 hipError_t launch_forward(const Geom& g, const DevCtx& dc, const void* indices, const void* offsets,
@@ -136,7 +143,7 @@ hipError_t launch_atomic_reduce(const Geom& g, const void* offsets, int itype, l
                                 int pool, const float* dY, const int32_t* inverse,
                                 const int32_t* num_unique, float* grad, hipStream_t st);
 // opt: 1 = SGD, 2 = Adagrad; reads grad_in[u] for u < *num_unique
-hipError_t launch_apply(const Geom& g, const DevCtx& dc, int opt, int N,
+hipError_t launch_apply(const Geom& g, const DevCtx& dc, int mode, int N,
                         const uint32_t* unique_keys, const int32_t* num_unique,
                         const float* grad_in, float lr, float eps, hipStream_t st);
 

@@ -12,8 +12,11 @@
 //   SGD:     w <- w - (lr*g)
 //   Adagrad: G <- G + g*g;  w <- w - (lr*g) / (sqrt(G) + eps)
 // each operation rounded separately (no contraction), and w rounded back to
-// the storage type with round-to-nearest-even. Rows no lookup touched are
-// never read or written.
+// the storage type with round-to-nearest-even. A low-precision table with an
+// fp32 master (the same slide: FP32 master weights cast to the low-precision
+// weights) steps the master instead and writes the master and its RNE cast in
+// the same pass; its stored copy is never read here. Rows no lookup touched
+// are never read or written.
 //
 // Work split. Segments are cut into chunks (at segment starts and every
 // kChunk sorted positions). One subgroup of LPR lanes (4 fp32 columns per
@@ -63,21 +66,33 @@ __device__ __forceinline__ int table_of(const uint32_t* s_ro, int T, uint32_t ke
   return lo;
 }
 
+// DT below is the update type code: storage type, | kMasterBit with a master.
 template <int DT>
 __device__ __forceinline__ void row_ptrs(const RedArgs& a, int t, uint32_t r, int c0, char** wp,
-                                         float** gp) {
+                                         float** gp, float** mp) {
   const int s = c0 / a.Dsl;
   const int cs = c0 - s * a.Dsl;
   const size_t e = (size_t)r * a.Dsl + cs;
-  *wp = reinterpret_cast<char*>(a.tables[t].w[s]) + e * Stor<DT>::kBytes;
+  *wp = reinterpret_cast<char*>(a.tables[t].w[s]) + e * Stor<(DT & 7)>::kBytes;
   float* g = a.tables[t].g[s];
   *gp = g ? g + e : nullptr;
+  if constexpr ((DT & kMasterBit) != 0) *mp = a.tables[t].m[s] + e;
+}
+
+// The fp32 value the optimizer steps: the master if there is one, else the
+// widened stored weight.
+template <int DT>
+__device__ __forceinline__ void load_weight(const char* wp, const float* mp, float* wv) {
+  if constexpr ((DT & kMasterBit) != 0)
+    load4<EMB_F32>(mp, wv);
+  else
+    load4<(DT & 7)>(wp, wv);
 }
 
 // mode 1 = SGD, 2 = Adagrad
 template <int DT, int MODE>
-__device__ __forceinline__ void row_update(char* wp, float* gp, const float* wv, const float* Gv,
-                                           const float* g, float lr, float eps) {
+__device__ __forceinline__ void row_update(char* wp, float* gp, float* mp, const float* wv,
+                                           const float* Gv, const float* g, float lr, float eps) {
 #pragma clang fp contract(off)
   float nw[4];
   if constexpr (MODE == 1) {
@@ -94,7 +109,11 @@ __device__ __forceinline__ void row_update(char* wp, float* gp, const float* wv,
     f4 v = {ng[0], ng[1], ng[2], ng[3]};
     *reinterpret_cast<f4*>(gp) = v;
   }
-  store4<DT>(wp, nw);
+  if constexpr ((DT & kMasterBit) != 0) {
+    f4 m = {nw[0], nw[1], nw[2], nw[3]};
+    *reinterpret_cast<f4*>(mp) = m;
+  }
+  store4<(DT & 7)>(wp, nw);
 }
 
 // Applies the finished gradient of unique key `key` (segment `seg`): mode 0
@@ -109,11 +128,12 @@ __device__ __forceinline__ void finish_row(const RedArgs& a, const uint32_t* s_r
     const int t = table_of(s_ro, a.T, key);
     char* wp;
     float* gp;
-    row_ptrs<DT>(a, t, key - s_ro[t], c0, &wp, &gp);
+    float* mp = nullptr;
+    row_ptrs<DT>(a, t, key - s_ro[t], c0, &wp, &gp, &mp);
     float wv[4], Gv[4] = {0.f, 0.f, 0.f, 0.f};
-    load4<DT>(wp, wv);
+    load_weight<DT>(wp, mp, wv);
     if constexpr (MODE == 2) load4<EMB_F32>(gp, Gv);
-    row_update<DT, MODE>(wp, gp, wv, Gv, g, a.lr, a.eps);
+    row_update<DT, MODE>(wp, gp, mp, wv, Gv, g, a.lr, a.eps);
   }
 }
 
@@ -157,11 +177,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
 
     char* wp = nullptr;
     float* gp = nullptr;
+    float* mp = nullptr;
     float wv[4] = {0.f, 0.f, 0.f, 0.f}, Gv[4] = {0.f, 0.f, 0.f, 0.f};
     if constexpr (MODE != 0) {
       if (whole && act) {  // prefetch the row so its latency overlaps the dY loads
-        row_ptrs<DT>(a, t, key - s_ro[t], c0, &wp, &gp);
-        load4<DT>(wp, wv);
+        row_ptrs<DT>(a, t, key - s_ro[t], c0, &wp, &gp, &mp);
+        load_weight<DT>(wp, mp, wv);
         if constexpr (MODE == 2) load4<EMB_F32>(gp, Gv);
       }
     }
@@ -203,7 +224,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
           *reinterpret_cast<f4*>(a.grad + (size_t)seg * a.D + c0) = o;
         }
       } else {
-        row_update<DT, MODE>(wp, gp, wv, Gv, acc, a.lr, a.eps);
+        row_update<DT, MODE>(wp, gp, mp, wv, Gv, acc, a.lr, a.eps);
       }
     } else {
       const int j = cb / kChunk;
@@ -399,23 +420,34 @@ static void launch_apply_t(int lpr, int grid, size_t smem, hipStream_t st, const
 #undef L_AP
 }
 
-#define DISPATCH_DT_MODE(FN, ...)                                   \
-  switch (g.dtype) {                                                \
-    case EMB_F32:                                                   \
-      if (mode == 0) FN<EMB_F32, 0>(__VA_ARGS__);                   \
-      else if (mode == 1) FN<EMB_F32, 1>(__VA_ARGS__);              \
-      else FN<EMB_F32, 2>(__VA_ARGS__);                             \
-      break;                                                        \
-    case EMB_BF16:                                                  \
-      if (mode == 0) FN<EMB_BF16, 0>(__VA_ARGS__);                  \
-      else if (mode == 1) FN<EMB_BF16, 1>(__VA_ARGS__);             \
-      else FN<EMB_BF16, 2>(__VA_ARGS__);                            \
-      break;                                                        \
-    default:                                                        \
-      if (mode == 0) FN<EMB_F16, 0>(__VA_ARGS__);                   \
-      else if (mode == 1) FN<EMB_F16, 1>(__VA_ARGS__);              \
-      else FN<EMB_F16, 2>(__VA_ARGS__);                             \
-      break;                                                        \
+// Mode 0 (materialise the gradient) touches no weights, so it has one
+// instantiation; modes 1/2 are instantiated per update type code.
+#define DISPATCH_DT_MODE(FN, ...)                                                  \
+  if (mode == 0) {                                                                 \
+    FN<EMB_F32, 0>(__VA_ARGS__);                                                   \
+  } else {                                                                         \
+    switch (g.dtype | (g.master ? kMasterBit : 0)) {                               \
+      case EMB_F32:                                                                \
+        if (mode == 1) FN<EMB_F32, 1>(__VA_ARGS__);                                \
+        else FN<EMB_F32, 2>(__VA_ARGS__);                                          \
+        break;                                                                     \
+      case EMB_BF16:                                                               \
+        if (mode == 1) FN<EMB_BF16, 1>(__VA_ARGS__);                               \
+        else FN<EMB_BF16, 2>(__VA_ARGS__);                                         \
+        break;                                                                     \
+      case EMB_F16:                                                                \
+        if (mode == 1) FN<EMB_F16, 1>(__VA_ARGS__);                                \
+        else FN<EMB_F16, 2>(__VA_ARGS__);                                          \
+        break;                                                                     \
+      case EMB_BF16 | kMasterBit:                                                  \
+        if (mode == 1) FN<EMB_BF16 | kMasterBit, 1>(__VA_ARGS__);                  \
+        else FN<EMB_BF16 | kMasterBit, 2>(__VA_ARGS__);                            \
+        break;                                                                     \
+      default:                                                                     \
+        if (mode == 1) FN<EMB_F16 | kMasterBit, 1>(__VA_ARGS__);                   \
+        else FN<EMB_F16 | kMasterBit, 2>(__VA_ARGS__);                             \
+        break;                                                                     \
+    }                                                                              \
   }
 
 template <int DT, int MODE>
@@ -467,7 +499,7 @@ hipError_t launch_combine(const Geom& g, const DevCtx& dc, int mode, int N, cons
   return hipGetLastError();
 }
 
-hipError_t launch_apply(const Geom& g, const DevCtx& dc, int opt, int N,
+hipError_t launch_apply(const Geom& g, const DevCtx& dc, int mode, int N,
                         const uint32_t* unique_keys, const int32_t* num_unique,
                         const float* grad_in, float lr, float eps, hipStream_t st) {
   RedArgs a{};
@@ -488,7 +520,6 @@ hipError_t launch_apply(const Geom& g, const DevCtx& dc, int opt, int N,
   const long long want = ((long long)N + sgw - 1) / sgw;
   const int grid = (int)(want < 16384 ? (want > 0 ? want : 1) : 16384);
   const size_t smem = (size_t)(g.T + 1) * 4;
-  const int mode = opt;
   DISPATCH_DT_MODE(launch_apply_t, lpr, grid, smem, st, a)
   return hipGetLastError();
 }

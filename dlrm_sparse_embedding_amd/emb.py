@@ -56,7 +56,8 @@ class emb_table_desc(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_int64), ("dim", ctypes.c_int32), ("col_slices", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("weights", ctypes.c_void_p * EMB_MAX_SLICES),
-                ("state", ctypes.c_void_p * EMB_MAX_SLICES)]
+                ("state", ctypes.c_void_p * EMB_MAX_SLICES),
+                ("master", ctypes.c_void_p * EMB_MAX_SLICES)]
 
 
 _lib = None
@@ -234,10 +235,11 @@ class TableSpec:
 
 
 class EmbeddingTables:
-    """Allocates this GPU's tables (and Adagrad state) as torch tensors,
-    registers them with emb_create_tables and forwards the calls."""
+    """Allocates this GPU's tables (and Adagrad state, and fp32 master weights
+    for low-precision tables if asked) as torch tensors, registers them with
+    emb_create_tables and forwards the calls."""
 
-    def __init__(self, specs, with_state: bool, device="cuda"):
+    def __init__(self, specs, with_state: bool, device="cuda", with_master: bool = False):
         specs = list(specs)
         self.specs = specs
         self.T = len(specs)
@@ -246,6 +248,7 @@ class EmbeddingTables:
         self.col_slices = specs[0].col_slices
         self.weights = []   # [t][s] tensors [rows, dim/col_slices]
         self.state = []     # [t][s] fp32 tensors or None
+        self.master = []    # [t][s] fp32 tensors or None
         descs = []
         for sp in specs:
             dsl = sp.dim // sp.col_slices
@@ -253,13 +256,17 @@ class EmbeddingTables:
                   for _ in range(sp.col_slices)]
             ss = ([torch.empty((sp.rows, dsl), dtype=torch.float32, device=device)
                    for _ in range(sp.col_slices)] if with_state else None)
+            ms = ([torch.empty((sp.rows, dsl), dtype=torch.float32, device=device)
+                   for _ in range(sp.col_slices)] if with_master else None)
             self.weights.append(ws)
             self.state.append(ss)
+            self.master.append(ms)
             d = emb_table_desc()
             d.rows, d.dim, d.col_slices, d.dtype, d.reserved = sp.rows, sp.dim, sp.col_slices, DTYPE_CODE[sp.dtype], 0
             for s in range(sp.col_slices):
                 d.weights[s] = ws[s].data_ptr()
                 d.state[s] = ss[s].data_ptr() if ss else None
+                d.master[s] = ms[s].data_ptr() if ms else None
             descs.append(d)
         self.ctx = emb_create_tables(descs)
         self.row_offset = emb_row_offsets(self.ctx, self.T)
@@ -329,3 +336,7 @@ class EmbeddingTables:
     def logical_state(self, t: int, rows) -> torch.Tensor:
         r = torch.as_tensor(rows, dtype=torch.int64, device=self.weights[t][0].device)
         return torch.cat([s.index_select(0, r) for s in self.state[t]], dim=1)
+
+    def logical_master(self, t: int, rows) -> torch.Tensor:
+        r = torch.as_tensor(rows, dtype=torch.int64, device=self.weights[t][0].device)
+        return torch.cat([m.index_select(0, r) for m in self.master[t]], dim=1)

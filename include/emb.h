@@ -91,7 +91,18 @@ extern "C" {
  *   weights[s]  device pointer of slice s, 16-byte aligned.
  *   state[s]    device fp32 Adagrad accumulator of slice s (same shape as
  *               the weight slice), or NULL for all s if Adagrad is not used.
- * All tables of one context must share dim, col_slices and dtype. */
+ *   master[s]   device fp32 master weights of slice s (same shape, 16-byte
+ *               aligned), or NULL for all s. Only for EMB_BF16 / EMB_F16:
+ *               the mixed-precision scheme of the "Merlin HugeCTR" GTC 2022
+ *               deck, slide "WEIGHT CONVERSION FOR MIXED PRECISION TRAINING"
+ *               (the optimizer keeps FP32 master weights; the weights the
+ *               lookups use are their low-precision cast). With a master,
+ *               the update reads the master (never weights[s]), steps it in
+ *               fp32, and writes the master and weights[s] = RNE(master) in
+ *               the same pass; the forward reads weights[s]. Without one,
+ *               weights[s] is the only copy.
+ * All tables of one context must share dim, col_slices and dtype, and all
+ * or none of them carry state, and all or none a master. */
 typedef struct emb_table_desc {
   int64_t rows;
   int32_t dim;
@@ -100,6 +111,7 @@ typedef struct emb_table_desc {
   int32_t reserved;             /* must be 0 */
   void*   weights[EMB_MAX_SLICES];
   float*  state[EMB_MAX_SLICES];
+  float*  master[EMB_MAX_SLICES];
 } emb_table_desc;
 
 typedef struct emb_ctx emb_ctx;

@@ -29,9 +29,9 @@ RTOL_SUM = 1e-5
 RTOL_W = {"f32": 1e-5, "bf16": 2e-2, "f16": 2e-2}
 
 
-def make_tables(cfg: W.Config) -> E.EmbeddingTables:
+def make_tables(cfg: W.Config, master: bool = False) -> E.EmbeddingTables:
     specs = [E.TableSpec(t.rows, t.dim, t.dtype, t.col_slices) for t in cfg.tables]
-    tabs = E.EmbeddingTables(specs, with_state=cfg.opt == "adagrad")
+    tabs = E.EmbeddingTables(specs, with_state=cfg.opt == "adagrad", with_master=master)
     tabs.init_uniform(cfg.init_seed)
     return tabs
 
@@ -132,9 +132,11 @@ def check_grad(g_gpu, g_ref, m_ref):
     assert not bad.any(), f"reduced grad: {int(bad.sum())} elements off, worst {err.max():.3e}"
 
 
-def check_update(cfg, w_gpu, G_gpu, w_old, G_old, g_ref, m_ref):
+def check_update(cfg, w_gpu, G_gpu, w_old, G_old, g_ref, m_ref, wdtype=None):
     """w_gpu/G_gpu: device results (fp32 view of stored values) for the
-    checked rows; w_old: stored values before the step."""
+    checked rows; w_old: stored values before the step. wdtype: the type the
+    checked weights are kept in (default the storage type; "f32" for an fp32
+    master)."""
     delta = RTOL_SUM * m_ref.astype(np.float32)
     g_lo = (g_ref - delta).astype(np.float32)
     g_hi = (g_ref + delta).astype(np.float32)
@@ -145,7 +147,7 @@ def check_update(cfg, w_gpu, G_gpu, w_old, G_old, g_ref, m_ref):
         wr, Gr = O.adagrad_step(w_old, G_old, g_ref, cfg.lr, cfg.eps)
         wa, Ga = O.adagrad_step(w_old, G_old, g_lo, cfg.lr, cfg.eps)
         wb, Gb = O.adagrad_step(w_old, G_old, g_hi, cfg.lr, cfg.eps)
-    tol = RTOL_W[cfg.dtype] * (np.abs(w_old).astype(np.float64) + np.abs(wr.astype(np.float64) - w_old))
+    tol = RTOL_W[wdtype or cfg.dtype] * (np.abs(w_old).astype(np.float64) + np.abs(wr.astype(np.float64) - w_old))
     lo = np.minimum(wa, wb).astype(np.float64) - tol
     hi = np.maximum(wa, wb).astype(np.float64) + tol
     wg = w_gpu.astype(np.float64)
@@ -180,25 +182,83 @@ def read_rows(tabs: E.EmbeddingTables, cfg, keys: np.ndarray):
     return w, G
 
 
-def stored_init(cfg, keys: np.ndarray):
+def read_master(tabs: E.EmbeddingTables, cfg, keys: np.ndarray):
+    """fp32 master rows of global keys."""
+    ro = cfg.row_offset()
+    t_of = np.searchsorted(ro, keys, side="right") - 1
+    m = np.zeros((len(keys), cfg.dim), np.float32)
+    for t in np.unique(t_of):
+        sel = np.nonzero(t_of == t)[0]
+        m[sel] = tabs.logical_master(int(t), keys[sel] - ro[t]).cpu().numpy()
+    return m
+
+
+def stored_init(cfg, keys: np.ndarray, rounded: bool = True):
+    """Initial values of global keys: as stored (rounded to the storage
+    type), or the fp32 values an fp32 master starts from."""
     ro = cfg.row_offset()
     t_of = np.searchsorted(ro, keys, side="right") - 1
     w = np.zeros((len(keys), cfg.dim), np.float32)
     for t in np.unique(t_of):
         sel = np.nonzero(t_of == t)[0]
-        w[sel] = O.to_storage(O.init_values(cfg.init_seed, int(t), keys[sel] - ro[t], cfg.dim), cfg.dtype)
+        v = O.init_values(cfg.init_seed, int(t), keys[sel] - ro[t], cfg.dim)
+        w[sel] = O.to_storage(v, cfg.dtype) if rounded else v
     return w
 
 
+def update_interval(cfg, w_lo, w_hi, G_lo, G_hi, g_ref, m_ref, wdtype=None):
+    """Propagates an interval of (w, G) through one oracle step with the
+    gradient known to within +-1e-5 * m_ref. The step is monotone in each of
+    w, G and g separately (increasing in w, decreasing in g, and in G
+    increasing or decreasing with the sign of g), so its extremes over the box
+    are at its corners; the interval is widened by the step's own rounding.
+    Used to chain several steps from oracle values only."""
+    delta = RTOL_SUM * m_ref.astype(np.float32)
+    gs = [(g_ref - delta).astype(np.float32), (g_ref + delta).astype(np.float32)]
+    rt = RTOL_W[wdtype or cfg.dtype]
+    ws = []
+    for w in (w_lo, w_hi):
+        for g in gs:
+            if cfg.opt == "sgd":
+                ws.append(O.sgd_step(w, g, cfg.lr))
+            else:
+                for G in (G_lo, G_hi):
+                    ws.append(O.adagrad_step(w, G, g, cfg.lr, cfg.eps)[0])
+    ws = np.stack(ws).astype(np.float64)
+    span = np.abs(ws - np.stack([w_lo] * len(ws)).astype(np.float64)).max(axis=0)
+    tol = rt * (np.abs(w_lo).astype(np.float64) + span)
+    lo, hi = ws.min(axis=0) - tol, ws.max(axis=0) + tol
+    if cfg.opt == "sgd":
+        return lo, hi, G_lo, G_hi
+    # G' = G + g*g rises with G but not with g: over a gradient band that
+    # holds 0 its least g*g is 0, else that of the band's end nearer 0
+    g_lo, g_hi = gs
+    sq_lo = np.where((g_lo <= 0) & (g_hi >= 0), np.float32(0), np.minimum(g_lo * g_lo, g_hi * g_hi))
+    sq_hi = np.maximum(g_lo * g_lo, g_hi * g_hi)
+    Gl = (np.asarray(G_lo, np.float32) + sq_lo.astype(np.float32)).astype(np.float64)
+    Gh = (np.asarray(G_hi, np.float32) + sq_hi.astype(np.float32)).astype(np.float64)
+    tG = 1e-5 * np.abs(Gh)
+    return lo, hi, Gl - tG, Gh + tG
+
+
+def check_interval(name, got, lo, hi):
+    g = np.asarray(got, np.float64)
+    bad = (g < lo) | (g > hi)
+    assert not bad.any(), (f"{name}: {int(bad.sum())} of {bad.size} off; e.g. got {g[bad][:3]} "
+                           f"want [{lo[bad][:3]}, {hi[bad][:3]}]")
+
+
 def run_step(cfg, batch, dY, path="fused", sample_bags=None, sample_keys=None, sample_untouched=2000,
-             seed=0, tabs=None):
+             seed=0, tabs=None, master=False):
     """Forward + backward + update on the GPU; every check against the oracle.
     sample_bags / sample_keys: None = check everything; else the number of
-    sampled samples / unique keys to check."""
+    sampled samples / unique keys to check. master: the tables carry fp32
+    master weights (the update steps the master; the stored copy must be its
+    RNE cast, bit for bit)."""
     rng = np.random.default_rng(seed)
     own = tabs is None
     if own:
-        tabs = make_tables(cfg)
+        tabs = make_tables(cfg, master=master)
     idx, off, dy = to_dev(batch, dY)
     B, N = cfg.batch, batch.N
     # ---- forward
@@ -232,13 +292,21 @@ def run_step(cfg, batch, dY, path="fused", sample_bags=None, sample_keys=None, s
         check_grad(g_gpu, g_ref, m_ref)
     # ---- update
     keys = u[sel]
-    w_old = stored_init(cfg, keys)
+    w_old = stored_init(cfg, keys, rounded=not master)
     G_old = np.zeros_like(w_old) if cfg.opt == "adagrad" else None
     tabs.update(cfg.opt, cfg.lr, cfg.eps, bufs, dY=dy)
     torch.cuda.synchronize()
     tabs.check_device_error()
     w_new, G_new = read_rows(tabs, cfg, keys)
-    check_update(cfg, w_new, G_new, w_old, G_old, g_ref, m_ref)
+    if master:
+        m_new = read_master(tabs, cfg, keys)
+        check_update(cfg, m_new, G_new, w_old, G_old, g_ref, m_ref, wdtype="f32")
+        # the stored copy is the RNE cast of the device's own master: one
+        # rounding decision, taken in the same precision on both sides
+        assert np.array_equal(w_new.view(np.uint32), O.to_storage(m_new, cfg.dtype).view(np.uint32)), \
+            "stored copy is not the RNE cast of the master"
+    else:
+        check_update(cfg, w_new, G_new, w_old, G_old, g_ref, m_ref)
     # ---- untouched rows stay bit-identical
     if sample_untouched:
         tot = cfg.total_rows
@@ -247,6 +315,9 @@ def run_step(cfg, batch, dY, path="fused", sample_bags=None, sample_keys=None, s
         if len(cand):
             w_u, G_u = read_rows(tabs, cfg, cand)
             assert np.array_equal(w_u.view(np.uint32), stored_init(cfg, cand).view(np.uint32)), "untouched row changed"
+            if master:
+                assert np.array_equal(read_master(tabs, cfg, cand).view(np.uint32),
+                                      stored_init(cfg, cand, rounded=False).view(np.uint32)), "untouched master changed"
             if G_u is not None:
                 assert np.all(G_u == 0), "untouched state changed"
     result = dict(U=U, keys=keys, w_new=w_new, G_new=G_new, bufs=bufs)

@@ -37,12 +37,18 @@ def test_header_constants_match_binding():
     assert consts["EMB_K_COUNT"] == len(E.KERNELS) == len(kids)
 
 
-def _desc(rows=100, dim=16, slices=1, dtype=E.EMB_F32, state=True):
+def _desc(rows=100, dim=16, slices=1, dtype=E.EMB_F32, state=True, master=False):
     d = E.emb_table_desc()
     d.rows, d.dim, d.col_slices, d.dtype, d.reserved = rows, dim, slices, dtype, 0
     for s in range(min(slices, E.EMB_MAX_SLICES)):
         d.weights[s] = FAKE + 0x1000 * s
         d.state[s] = (FAKE + 0x100000 + 0x1000 * s) if state else None
+        d.master[s] = (FAKE + 0x200000 + 0x1000 * s) if master else None
+    return d
+
+
+def _with(d, field, s, value):
+    getattr(d, field)[s] = value
     return d
 
 
@@ -64,6 +70,11 @@ def _create(descs):
     ([_desc(rows=1 << 31), _desc(rows=1 << 31)], E.EMB_E_INVAL),  # sum of rows >= 2^32 - 1
     ([_desc(state=True), _desc(state=False)], E.EMB_E_INVAL),
     ([_desc(dim=512)], E.EMB_E_INVAL),                     # > 1024-byte rows
+    ([_desc(master=True)], E.EMB_E_INVAL),                 # fp32 master on an fp32 table
+    ([_desc(dtype=E.EMB_BF16, master=True), _desc(dtype=E.EMB_BF16)], E.EMB_E_INVAL),  # master: all or none
+    ([_with(_desc(dim=32, slices=2, dtype=E.EMB_F16, master=True), "master", 1, None)], E.EMB_E_INVAL),
+    ([_with(_desc(dtype=E.EMB_BF16, master=True), "master", 0, FAKE + 0x200008)], E.EMB_E_INVAL),  # unaligned
+    ([_with(_desc(), "weights", 1, FAKE + 0x4000)], E.EMB_E_INVAL),  # pointer beyond col_slices
 ])
 def test_create_rejects(descs, code):
     rc, ctx = _create(descs)
@@ -73,7 +84,8 @@ def test_create_rejects(descs, code):
 
 
 def test_create_accepts_16_byte_slice_rows():
-    for d in (_desc(dim=8, dtype=E.EMB_BF16), _desc(dim=4), _desc(dim=128, slices=4, dtype=E.EMB_F16)):
+    for d in (_desc(dim=8, dtype=E.EMB_BF16), _desc(dim=4), _desc(dim=128, slices=4, dtype=E.EMB_F16),
+              _desc(dim=128, slices=4, dtype=E.EMB_F16, master=True), _desc(dtype=E.EMB_BF16, master=True)):
         rc, ctx = _create([d])
         assert rc == E.EMB_OK
         E.emb_destroy_tables(ctx)

@@ -262,14 +262,13 @@ def test_malformed_offsets_flagged(case):
     tabs.close()
 
 
-def test_two_adagrad_steps():
-    cfg = W.make_config(2, batch=3000)
-    b1, b2 = W.make_batch(cfg, k=0), W.make_batch(cfg, k=1)
-    d1, d2 = W.make_dy(cfg, k=0), W.make_dy(cfg, k=1)
-    _say("two-steps cfg2")
-    tabs = P.make_tables(cfg)
-    state = {}   # key -> (w, G) oracle state of touched rows
-    for batch, dY in ((b1, d1), (b2, d2)):
+def _chained_steps(cfg, batches, dys, master=False):
+    """Several training steps on one set of tables. The expected rows come
+    from the oracle alone: each touched row's (w, G) is carried as an interval
+    from step to step (update_interval), never from the device's results."""
+    tabs = P.make_tables(cfg, master=master)
+    box = {}   # key -> (w_lo, w_hi, G_lo, G_hi) from the oracle chain
+    for batch, dY in zip(batches, dys):
         idx, off, dy = P.to_dev(batch, dY)
         bufs = tabs.backward_buffers(batch.N, cfg.batch, with_grad=False)
         tabs.backward(idx, off, cfg.batch, cfg.pool, dy, bufs)
@@ -277,16 +276,55 @@ def test_two_adagrad_steps():
         torch.cuda.synchronize()
         u, c, inv = P.oracle_dedup(cfg, batch)
         g, m = P.grad_bounds(cfg, batch, dY, inv, len(u))
-        w_old = P.stored_init(cfg, u)
-        G_old = np.zeros_like(w_old)
+        w0 = P.stored_init(cfg, u, rounded=not master).astype(np.float64)
+        w_lo, w_hi = w0.copy(), w0.copy()
+        G_lo, G_hi = np.zeros_like(w0), np.zeros_like(w0)
         for j, k in enumerate(u.tolist()):
-            if k in state:
-                w_old[j], G_old[j] = state[k]
+            if k in box:
+                w_lo[j], w_hi[j], G_lo[j], G_hi[j] = box[k]
+        f32 = lambda a: a.astype(np.float32)
+        lo, hi, Glo, Ghi = P.update_interval(cfg, f32(w_lo), f32(w_hi), f32(G_lo), f32(G_hi), g, m,
+                                             wdtype="f32" if master else None)
         w_new, G_new = P.read_rows(tabs, cfg, u)
-        P.check_update(cfg, w_new, G_new, w_old, G_old, g, m)
+        if master:
+            m_new = P.read_master(tabs, cfg, u)
+            P.check_interval("master", m_new, lo, hi)
+            assert np.array_equal(w_new.view(np.uint32), O.to_storage(m_new, cfg.dtype).view(np.uint32))
+        else:
+            P.check_interval("weights", w_new, lo, hi)
+        if cfg.opt == "adagrad":
+            P.check_interval("state", G_new, Glo, Ghi)
         for j, k in enumerate(u.tolist()):
-            state[k] = (w_new[j].copy(), G_new[j].copy())
+            box[k] = (lo[j], hi[j], Glo[j], Ghi[j])
     tabs.close()
+
+
+def test_two_adagrad_steps():
+    cfg = W.make_config(2, batch=3000)
+    _say("two-steps cfg2")
+    _chained_steps(cfg, [W.make_batch(cfg, k=0), W.make_batch(cfg, k=1)],
+                   [W.make_dy(cfg, k=0), W.make_dy(cfg, k=1)])
+
+
+@pytest.mark.parametrize("cfg_id,path", [(4, "fused"), (4, "materialized"), (5, "fused"), (5, "materialized")])
+def test_master_weights_step(cfg_id, path):
+    # bf16 (SGD, mean pooling) and fp16 (Adagrad, 4 column slices) tables with
+    # fp32 masters: master within the fp32 band, stored copy = RNE(master)
+    # the masters add 4 bytes per element: tables shrunk to 2M rows
+    cfg = W.make_config(cfg_id, rows=2_000_000, **REDUCED[cfg_id])
+    batch = W.make_batch(cfg, k=0)
+    dY = W.make_dy(cfg, k=0)
+    _say("master", cfg_id, path)
+    P.run_step(cfg, batch, dY, path=path, master=True)
+
+
+def test_master_weights_three_steps():
+    # fp16 Adagrad with fp32 masters over three steps: the masters follow the
+    # oracle's fp32 chain (a step taken from the rounded copy would leave it)
+    cfg = W.make_config(5, batch=512, rows=2_000_000)
+    _say("master three steps cfg5")
+    _chained_steps(cfg, [W.make_batch(cfg, k=k) for k in range(3)], [W.make_dy(cfg, k=k) for k in range(3)],
+                   master=True)
 
 
 def test_dedup_ahead_on_second_stream_matches_serial():
