@@ -54,6 +54,11 @@ def parse():
     ap.add_argument("--reduce", choices=["fused", "atomic"], default="fused",
                     help="fused: sorted-segment reduction fused with the optimizer (the path); atomic: the "
                          "evidence variant, fp32 atomics into a materialised gradient, then the update")
+    ap.add_argument("--master", action="store_true",
+                    help="bf16/fp16 tables trained from fp32 master weights (the update steps the master "
+                         "and writes the master and its RNE copy in one pass)")
+    ap.add_argument("--rows", type=int, default=0,
+                    help="cap the rows of every table (0 = the workload's own sizes)")
     ap.add_argument("--ceiling", action="store_true",
                     help="only time plain library kernels (copy, read-only sum, fill) over 4 GiB: the "
                          "practical HBM ceiling the path's kernels are compared with")
@@ -132,7 +137,10 @@ def main() -> int:
     from dlrm_sparse_embedding_amd import emb as E
     from dlrm_sparse_embedding_amd import workloads as W
 
-    cfg = W.make_config(args.config)
+    cfg = W.make_config(args.config, rows=args.rows or None)
+    if args.master and cfg.dtype == "f32":
+        print("bench.py: --master needs a bf16/fp16 workload (configs 4, 5)", file=sys.stderr)
+        return 2
     if args.uniform_keys:
         cfg = replace(cfg, zipf_s=None)
     T, B, D = cfg.T, cfg.batch, cfg.dim
@@ -141,7 +149,7 @@ def main() -> int:
 
     torch.cuda.set_device(0)
     specs = [E.TableSpec(t.rows, t.dim, t.dtype, t.col_slices) for t in cfg.tables]
-    tabs = E.EmbeddingTables(specs, with_state=cfg.opt == "adagrad")
+    tabs = E.EmbeddingTables(specs, with_state=cfg.opt == "adagrad", with_master=args.master)
     tabs.init_uniform(cfg.init_seed)
     print(f"[bench] tables ready: {T} x {cfg.tables[0].rows} x {D} {cfg.dtype}", file=sys.stderr, flush=True)
 
@@ -234,10 +242,13 @@ def main() -> int:
     # algorithmic bytes per step (SURVEY-style formula, actual N and U)
     ib = 4 if host_batches[0].indices.dtype == np.int32 else 8
     state_b = D * 4 if cfg.opt == "adagrad" else 0
+    # weight bytes per unique row: stored row read + written, or with a master
+    # the fp32 master read + written and the low-precision copy written
+    wrow_b = 2 * D * 4 + rowbytes if args.master else 2 * rowbytes
     steps_N = [dev[i % len(dev)][2] for i in range(K)]
     steps_U = [U_of[i % len(dev)] for i in range(K)]
     fwd_bytes = sum(n * rowbytes + n * ib + (T * B + 1) * ib + B * T * D * 4 for n in steps_N)
-    bwd_bytes = sum(B * T * D * 4 + n * ib + (T * B + 1) * ib + u * (rowbytes + state_b) * 2 + u * 8 + n * 4
+    bwd_bytes = sum(B * T * D * 4 + n * ib + (T * B + 1) * ib + u * (wrow_b + 2 * state_b) + u * 8 + n * 4
                     for n, u in zip(steps_N, steps_U))
     lookups = sum(steps_N)
     if args.schedule == "overlap":
@@ -265,7 +276,7 @@ def main() -> int:
         "forward": Navg * rowbytes + Navg * ib + (T * B + 1) * ib + B * T * D * 4,
         # fused reduce + update: every bag's dY row once, each unique row's
         # weight (+ state) read and written once, the sorted bag ids
-        "reduce": B * T * D * 4 + Uavg * (rowbytes + state_b) * 2 + Navg * 4,
+        "reduce": B * T * D * 4 + Uavg * (wrow_b + 2 * state_b) + Navg * 4,
         "sort_scatter": Navg * 8 * 2,
         "sort_hist": Navg * 8,
         "keys": Navg * ib * 2 + Navg * (8 + 4),
@@ -310,9 +321,11 @@ def main() -> int:
         "dtype": "f32" if cfg.dtype == "f32" else f"{cfg.dtype}-storage/f32",
         "data": "synthetic",
         "config": {
-            "workload": (f"{T} {cfg.dtype} tables x {cfg.tables[0].rows} rows x {D}, batch {B}, "
+            "workload": (f"{T} {cfg.dtype} tables x {rows_desc(cfg)} rows x {D}"
+                         f"{f' ({cfg.tables[0].col_slices} column slices)' if cfg.tables[0].col_slices > 1 else ''}"
+                         f"{' + fp32 masters' if args.master else ''}, batch {B}, "
                          f"{'uniform' if cfg.zipf_s is None else f'Zipf({cfg.zipf_s})'} keys, "
-                         f"{cfg.pool} pooling, {cfg.opt}"),
+                         f"{hot_desc(cfg)}, {cfg.pool} pooling, {cfg.opt}"),
             "config_id": args.config,
             "global_batch": B,
             "lookups_per_step": int(round(Navg)),
@@ -336,6 +349,24 @@ def main() -> int:
     print(json.dumps(out), flush=True)
     tabs.close()
     return 0
+
+
+def rows_desc(cfg) -> str:
+    rr = [t.rows for t in cfg.tables]
+    if min(rr) == max(rr):
+        return str(rr[0])
+    return f"{min(rr)}..{max(rr)} ({sum(rr)} in total)"
+
+
+def hot_desc(cfg) -> str:
+    h = cfg.hotness
+    if all(x == 1 for x in h):
+        return "one lookup per bag"
+    if all(isinstance(x, int) for x in h):
+        if min(h) == max(h):
+            return f"{h[0]} lookups per bag"
+        return f"{min(h)}..{max(h)} lookups per bag by table (log-uniform)"
+    return "variable lookups per bag"
 
 
 def cpu_model() -> str:

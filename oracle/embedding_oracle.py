@@ -38,6 +38,15 @@ What is computed, and where the pages define it
   lookups read. Written out as: m' = the fp32 optimizer step of m, and the
   stored copy = round-to-nearest-even(m'). The stored copy is never read by
   the update.
+* Routing to shards -- EMBark (RecSys'24 article): tables are split into
+  shards (its 3D sharding tuple; model parallelism in the GTC 2022 deck,
+  slide "CHALLENGES OF EMBEDDING LAYER"), and reduction-based / unique-based
+  clusters send each distinct key, and its reduced gradient, once. Read here,
+  for one GPU's share, as the step before the exchange: each unique key gets
+  the shard that owns its (table, row) under a per-table rule (whole table on
+  one shard; rows dealt cyclically; rows in S contiguous blocks), and the
+  unique keys (with their reduced gradients) are grouped by destination
+  shard, keys ascending inside a group.
 * Untouched rows -- a dense step with g = 0 and G = 0 leaves w and G bit for
   bit unchanged, so only touched rows are computed.
 * Table contents -- synthetic: each element is a counter hash of (seed, table,
@@ -53,7 +62,8 @@ __all__ = [
     "splitmix64", "init_values", "bf16_bits_rne", "bf16_bits_to_f32", "f16_rne",
     "to_storage", "TouchedRows", "pooled_forward", "global_keys", "dedup",
     "bag_of_positions", "reduced_grad", "sgd_step", "adagrad_step",
-    "update_rows", "update_rows_master",
+    "update_rows", "update_rows_master", "SHARD_TABLE", "SHARD_ROW_CYCLIC", "SHARD_ROW_BLOCK",
+    "shard_of_keys", "pack_by_shard",
 ]
 
 _U64 = np.uint64
@@ -308,3 +318,58 @@ def update_rows_master(master: np.ndarray, G: np.ndarray | None, g: np.ndarray, 
     else:
         raise ValueError(opt)
     return m1, to_storage(m1, dtype), G1
+
+
+# ---------------------------------------------------------------------------
+# Routing unique keys (and reduced gradients) to their owning shards
+# ---------------------------------------------------------------------------
+
+SHARD_TABLE = 0        # every row of the table on shard `shard`
+SHARD_ROW_CYCLIC = 1   # row r on shard (r + shard) mod S
+SHARD_ROW_BLOCK = 2    # row r on shard floor(r / ceil(rows / S))
+
+
+def shard_of_keys(keys: np.ndarray, row_offset: np.ndarray, rules, S: int) -> np.ndarray:
+    """Owner shard of each global key. rules[t] = (kind, shard) for table t;
+    row_offset has T+1 entries (the last one is the total row count)."""
+    keys = np.asarray(keys, dtype=np.int64)
+    ro = np.asarray(row_offset, dtype=np.int64)
+    t = np.searchsorted(ro, keys, side="right") - 1
+    r = keys - ro[t]
+    dest = np.empty(len(keys), dtype=np.int64)
+    for tt in np.unique(t):
+        sel = t == tt
+        kind, shard = rules[int(tt)]
+        rows = int(ro[tt + 1] - ro[tt])
+        if kind == SHARD_TABLE:
+            dest[sel] = shard
+        elif kind == SHARD_ROW_CYCLIC:
+            dest[sel] = (r[sel] + shard) % S
+        elif kind == SHARD_ROW_BLOCK:
+            block = -(-rows // S)
+            dest[sel] = r[sel] // block
+        else:
+            raise ValueError(kind)
+    return dest
+
+
+def pack_by_shard(unique_keys: np.ndarray, row_offset: np.ndarray, rules, S: int,
+                  reduced_grad: np.ndarray | None = None):
+    """Group the unique keys by owner shard (a stable sort by destination, so
+    keys stay ascending inside each group). Keys at or past the total row
+    count (the invalid-index sentinel) are sent nowhere. Returns
+    (send_keys, send_offsets[S+1], slot_of_unique, send_grad): the keys of
+    shard s are send_keys[send_offsets[s]:send_offsets[s+1]], unique key u
+    sits at slot_of_unique[u] (-1 if sent nowhere), send_grad[slot] is its
+    reduced gradient row."""
+    u = np.asarray(unique_keys, dtype=np.int64)
+    total = int(np.asarray(row_offset)[-1])
+    valid = np.nonzero(u < total)[0]
+    dest = shard_of_keys(u[valid], row_offset, rules, S)
+    order = valid[np.argsort(dest, kind="stable")]
+    counts = np.bincount(dest, minlength=S)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    slot = np.full(len(u), -1, dtype=np.int64)
+    slot[order] = np.arange(len(order))
+    send_grad = None if reduced_grad is None else np.asarray(reduced_grad)[order]
+    return u[order], offsets, slot, send_grad

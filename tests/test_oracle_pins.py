@@ -548,3 +548,129 @@ def test_master_pin_catches_mistakes():
     assert not _master_pin_ok(steps_from_copy, "sgd", "bf16")
     assert not _master_pin_ok(truncating_copy, "adagrad", "bf16")
     assert not _master_pin_ok(sign_flip, "adagrad", "f16")
+
+
+# ---------------------------------------------------------------------------
+# Routing unique keys to shards
+# ---------------------------------------------------------------------------
+
+def _pack_brute(unique_keys, rows, rules, S, grad=None):
+    """Pure-Python loops: find each key's table by walking the tables, apply the
+    rule, append to that shard's list in key order, concatenate."""
+    buckets = [[] for _ in range(S)]
+    for u, k in enumerate(int(x) for x in unique_keys):
+        base = 0
+        t = None
+        for tt, n in enumerate(rows):
+            if k < base + n:
+                t = tt
+                break
+            base += n
+        if t is None:
+            continue                              # sentinel: sent nowhere
+        r = k - base
+        kind, shard = rules[t]
+        if kind == O.SHARD_TABLE:
+            d = shard
+        elif kind == O.SHARD_ROW_CYCLIC:
+            d = (r + shard) % S
+        else:
+            block = (rows[t] + S - 1) // S
+            d = r // block
+        buckets[d].append(u)
+    order = [u for b in buckets for u in b]
+    offsets = [0]
+    for b in buckets:
+        offsets.append(offsets[-1] + len(b))
+    slot = [-1] * len(unique_keys)
+    for i, u in enumerate(order):
+        slot[u] = i
+    keys = [int(unique_keys[u]) for u in order]
+    g = None if grad is None else np.asarray([grad[u] for u in order]).reshape(len(order), -1)
+    return keys, offsets, slot, g
+
+
+def _pack_case(seed, S, T=5):
+    rng = np.random.default_rng(seed)
+    rows = [int(x) for x in rng.integers(1, 60, T)]
+    ro = np.concatenate([[0], np.cumsum(rows)])
+    kinds = rng.integers(0, 3, T)
+    rules = [(int(k), int(rng.integers(0, S)) if k != O.SHARD_ROW_BLOCK else 0) for k in kinds]
+    n = int(rng.integers(0, ro[-1] + 1))
+    u = np.sort(rng.choice(int(ro[-1]), n, replace=False))
+    if rng.random() < 0.5:
+        u = np.concatenate([u, [ro[-1]]])         # the invalid-index sentinel sorts last
+    grad = rng.standard_normal((len(u), 4)).astype(np.float32)
+    return rows, ro, rules, u, grad
+
+
+def _pack_pin_ok(fn, seeds=range(40), Ss=(1, 2, 3, 7, 16)):
+    for seed in seeds:
+        for S in Ss:
+            rows, ro, rules, u, grad = _pack_case(seed, S)
+            k, off, slot, g = fn(u, ro, rules, S, grad)
+            bk, boff, bslot, bg = _pack_brute(u, rows, rules, S, grad)
+            if not (np.array_equal(np.asarray(k, np.int64), np.asarray(bk, np.int64))
+                    and np.array_equal(off, boff) and np.array_equal(slot, bslot)
+                    and np.array_equal(np.asarray(g).reshape(-1, 4), np.asarray(bg).reshape(-1, 4))):
+                return False
+    return True
+
+
+def test_pack_by_shard_bruteforce():
+    assert _pack_pin_ok(O.pack_by_shard)
+
+
+def test_pack_by_shard_invariants_and_special_cases():
+    rng = np.random.default_rng(3)
+    rows = [1000, 37, 5000, 1]
+    ro = np.concatenate([[0], np.cumsum(rows)])
+    u = np.sort(rng.choice(int(ro[-1]), 2500, replace=False))
+    for S in (1, 5, 64):
+        rules = [(O.SHARD_ROW_CYCLIC, 3), (O.SHARD_TABLE, S - 1), (O.SHARD_ROW_BLOCK, 0), (O.SHARD_TABLE, 0)]
+        k, off, slot, _ = O.pack_by_shard(u, ro, rules, S)
+        assert off[0] == 0 and off[-1] == len(u) and np.all(np.diff(off) >= 0)
+        assert np.array_equal(np.sort(k), u)                       # a permutation of the keys
+        assert np.array_equal(k[slot], u)                          # slot points at the key
+        for s in range(S):
+            assert np.all(np.diff(k[off[s]:off[s + 1]]) > 0)       # ascending inside a shard
+        d = O.shard_of_keys(k, ro, rules, S)
+        assert np.array_equal(d, np.repeat(np.arange(S), np.diff(off)))
+    # one shard, or every table on shard 0: the order is unchanged
+    for S, rules in ((1, [(O.SHARD_ROW_CYCLIC, 0)] * 4), (4, [(O.SHARD_TABLE, 0)] * 4)):
+        k, off, slot, _ = O.pack_by_shard(u, ro, rules, S)
+        assert np.array_equal(k, u) and np.array_equal(slot, np.arange(len(u)))
+    # row blocks with as many shards as rows: shard = row
+    k, off, slot, _ = O.pack_by_shard(np.array([0, 3, 4, 9]), np.array([0, 10]), [(O.SHARD_ROW_BLOCK, 0)], 10)
+    assert list(off) == [0, 1, 1, 1, 2, 3, 3, 3, 3, 3, 4]
+
+
+def test_pack_pin_catches_mistakes():
+    def floor_block(u, ro, rules, S, grad):               # block = rows // S (too small)
+        valid = np.nonzero(u < ro[-1])[0]
+        keys = u[valid]
+        t = np.searchsorted(ro, keys, side="right") - 1
+        d = O.shard_of_keys(keys, ro, rules, S)
+        for i, (key, tt) in enumerate(zip(keys, t)):
+            if rules[tt][0] == O.SHARD_ROW_BLOCK:
+                d[i] = min((key - ro[tt]) // max((ro[tt + 1] - ro[tt]) // S, 1), S - 1)
+        order = valid[np.argsort(d, kind="stable")]
+        off = np.concatenate([[0], np.cumsum(np.bincount(d, minlength=S))])
+        slot = np.full(len(u), -1)
+        slot[order] = np.arange(len(order))
+        return u[order], off, slot, grad[order]
+
+    def unstable(u, ro, rules, S, grad):                   # keys descending inside a shard
+        k, off, slot, g = O.pack_by_shard(u, ro, rules, S, grad)
+        k, g, slot = k.copy(), g.copy(), slot.copy()
+        for s in range(S):
+            a, b = off[s], off[s + 1]
+            k[a:b], g[a:b] = k[a:b][::-1], g[a:b][::-1]
+        return k, off, slot, g
+
+    def no_shift(u, ro, rules, S, grad):                   # cyclic rule ignores its shift
+        return O.pack_by_shard(u, ro, [(k, 0 if k == O.SHARD_ROW_CYCLIC else s) for k, s in rules], S, grad)
+
+    assert not _pack_pin_ok(floor_block)
+    assert not _pack_pin_ok(unstable)
+    assert not _pack_pin_ok(no_shift)
