@@ -84,6 +84,11 @@ struct emb_ctx {
   } dedup;
   // cap on forward blocks (0 = one block per work unit), see ensure_device
   int fwd_max_blocks = 0;
+  // shard map (emb_set_shard_map): host copy, device copy uploaded on first use
+  std::vector<emb_shard_rule> shard_rules;
+  int num_shards = 0;
+  void* dev_rules = nullptr;
+  bool rules_dirty = false;
   // timing
   bool timing = false;
   std::vector<TimedLaunch> pending;
@@ -312,6 +317,7 @@ void emb_destroy_tables(emb_ctx* ctx) {
     (void)hipEventDestroy(p.e1);
   }
   for (auto e : ctx->free_events) (void)hipEventDestroy(e);
+  if (ctx->dev_rules) (void)hipFree(ctx->dev_rules);
   delete ctx;
 }
 
@@ -591,6 +597,117 @@ int emb_backward_atomic_reduce(emb_ctx* ctx, const void* offsets, int32_t itype,
   KScope ks(ctx, EMB_K_ATOMIC, st);
   hipError_t e = launch_atomic_reduce(ctx->g, offsets, itype, N, B, pool, dY, inverse, num_unique, reduced_grad, st);
   if (e != hipSuccess) return hip_fail(e, "atomic reduce");
+  return ok();
+}
+
+int emb_set_shard_map(emb_ctx* ctx, const emb_shard_rule* rules, int32_t num_shards) {
+  if (!ctx || !rules) return fail(EMB_E_INVAL, "NULL argument");
+  if (num_shards < 1 || num_shards > EMB_MAX_SHARDS)
+    return fail(EMB_E_INVAL, "num_shards must be in 1..%d", EMB_MAX_SHARDS);
+  for (int t = 0; t < ctx->g.T; ++t) {
+    const emb_shard_rule& r = rules[t];
+    if (r.kind == EMB_SHARD_TABLE || r.kind == EMB_SHARD_ROW_CYCLIC) {
+      if (r.shard < 0 || r.shard >= num_shards) return fail(EMB_E_INVAL, "table %d: shard %d not in [0, %d)", t, r.shard, num_shards);
+    } else if (r.kind == EMB_SHARD_ROW_BLOCK) {
+      if (r.shard != 0) return fail(EMB_E_INVAL, "table %d: row-block rule takes shard 0", t);
+    } else {
+      return fail(EMB_E_INVAL, "table %d: unknown shard rule kind %d", t, r.kind);
+    }
+  }
+  ctx->shard_rules.assign(rules, rules + ctx->g.T);
+  ctx->num_shards = num_shards;
+  ctx->rules_dirty = true;
+  return ok();
+}
+
+int emb_pack_by_shard(emb_ctx* ctx, void* ws, const float* dY, uint32_t* send_keys, int32_t* send_offsets,
+                      int32_t* slot_of_unique, float* send_grad, void* hip_stream) {
+  if (!ctx) return fail(EMB_E_INVAL, "ctx is NULL");
+  if (ctx->num_shards < 1) return fail(EMB_E_STATE, "no shard map set");
+  if (!ctx->last.valid || ws != ctx->last.ws)
+    return fail(EMB_E_STATE, "ws is not the workspace of this context's last backward");
+  if ((dY == nullptr) != (send_grad == nullptr)) return fail(EMB_E_INVAL, "dY and send_grad are given together");
+  const long long N = ctx->last.N;
+  if (!send_offsets) return fail(EMB_E_INVAL, "send_offsets is NULL");
+  if (N > 0 && (!send_keys || !slot_of_unique)) return fail(EMB_E_INVAL, "send_keys/slot_of_unique is NULL");
+  if (dY && (!aligned(dY, 16) || !aligned(send_grad, 16)))
+    return fail(EMB_E_INVAL, "dY and send_grad must be 16-byte aligned");
+  int rc;
+  if ((rc = ensure_device(ctx))) return rc;
+  hipError_t e;
+  if (ctx->rules_dirty) {
+    const size_t bytes = sizeof(emb_shard_rule) * ctx->shard_rules.size();
+    if (!ctx->dev_rules) {
+      if ((e = hipMalloc(&ctx->dev_rules, bytes)) != hipSuccess) return hip_fail(e, "hipMalloc(shard map)");
+    }
+    if ((e = hipMemcpy(ctx->dev_rules, ctx->shard_rules.data(), bytes, hipMemcpyHostToDevice)) != hipSuccess)
+      return hip_fail(e, "hipMemcpy(shard map)");
+    ctx->rules_dirty = false;
+  }
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const int S = ctx->num_shards;
+  const WsLayout L = ws_layout(ctx->g, N, ctx->last.B);
+  char* w = static_cast<char*>(ws);
+  uint64_t* a = reinterpret_cast<uint64_t*>(w + L.keys_a);
+  uint64_t* b = reinterpret_cast<uint64_t*>(w + L.keys_b);
+  if (N > 0) {
+    {
+      KScope ks(ctx, EMB_K_PACK, st);
+      if ((e = launch_pack_dest(ctx->g, ctx->dc, static_cast<const int2*>(ctx->dev_rules), S, (int)N,
+                                ctx->last.unique_keys, ctx->last.num_unique, a, st)) != hipSuccess)
+        return hip_fail(e, "pack destinations");
+    }
+    // destinations 0..S (S = sent nowhere), sorted stably
+    int bits = 1;
+    while ((1 << bits) <= S) ++bits;
+    const int rb = radix_bits_for(bits);
+    uint32_t* ghist = reinterpret_cast<uint32_t*>(w + L.ghist);
+    uint32_t* dtot = reinterpret_cast<uint32_t*>(w + L.digit_tot);
+    for (int shift = 0; shift < bits; shift += rb) {
+      {
+        KScope ks(ctx, EMB_K_SORT_HIST, st);
+        if ((e = launch_sort_hist(rb, a, (int)N, shift, ghist, L.nblk_sort, st)) != hipSuccess)
+          return hip_fail(e, "pack sort histogram");
+      }
+      {
+        KScope ks(ctx, EMB_K_SORT_SCAN, st);
+        if ((e = launch_sort_scan(rb, ghist, L.nblk_sort, dtot, st)) != hipSuccess) return hip_fail(e, "pack sort scan");
+      }
+      {
+        KScope ks(ctx, EMB_K_SORT_SCATTER, st);
+        if ((e = launch_sort_scatter(rb, a, b, (int)N, shift, ghist, dtot, L.nblk_sort, st)) != hipSuccess)
+          return hip_fail(e, "pack sort scatter");
+      }
+      uint64_t* tmp = a;
+      a = b;
+      b = tmp;
+    }
+    {
+      KScope ks(ctx, EMB_K_PACK, st);
+      if ((e = launch_pack_place(a, ctx->last.unique_keys, ctx->last.num_unique, (int)N, S, send_keys,
+                                 slot_of_unique, st)) != hipSuccess)
+        return hip_fail(e, "pack placement");
+    }
+  }
+  {
+    KScope ks(ctx, EMB_K_PACK, st);
+    if ((e = launch_pack_offsets(a, (int)N, S, send_offsets, st)) != hipSuccess) return hip_fail(e, "pack offsets");
+  }
+  if (dY && N > 0) {
+    {
+      KScope ks(ctx, EMB_K_REDUCE, st);
+      if ((e = launch_reduce(ctx->g, ctx->dc, 0, (int)N, ctx->last.B, ctx->last.pool, dY, L, w,
+                             ctx->last.unique_keys, ctx->last.num_unique, send_grad, 0.f, 0.f, st,
+                             slot_of_unique)) != hipSuccess)
+        return hip_fail(e, "segment reduce into send slots");
+    }
+    {
+      KScope ks(ctx, EMB_K_COMBINE, st);
+      if ((e = launch_combine(ctx->g, ctx->dc, 0, (int)N, L, w, ctx->last.unique_keys, send_grad, 0.f, 0.f, st,
+                              slot_of_unique)) != hipSuccess)
+        return hip_fail(e, "segment combine into send slots");
+    }
+  }
   return ok();
 }
 

@@ -188,4 +188,16 @@ __device__ __forceinline__ uint32_t block_excl_scan_256(uint32_t v, uint32_t* ld
   return wpre + x - v;
 }
 
+// Table of a global key: the t with row_off[t] <= key < row_off[t+1], by
+// binary search over the row offsets (staged in LDS by the caller).
+__device__ __forceinline__ int table_of(const uint32_t* s_ro, int T, uint32_t key) {
+  int lo = 0, hi = T;  // s_ro[lo] <= key < s_ro[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_ro[mid] <= key) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
 }  // namespace emb

@@ -130,14 +130,25 @@ hipError_t launch_rle(const uint64_t* sorted, int N, const WsLayout& L, char* ws
                       hipStream_t st);
 hipError_t launch_set_empty(const WsLayout& L, char* ws, int32_t* num_unique, hipStream_t st);
 
-// mode: 0 = write reduced gradient, 1 = fused SGD, 2 = fused Adagrad
+// mode: 0 = write reduced gradient, 1 = fused SGD, 2 = fused Adagrad.
+// slot (mode 0, optional): segment u's gradient goes to row slot[u] of
+// grad_out (skipped if negative) instead of row u.
 hipError_t launch_reduce(const Geom& g, const DevCtx& dc, int mode, int N, int B, int pool,
                          const float* dY, const WsLayout& L, const char* ws,
                          const uint32_t* unique_keys, const int32_t* num_unique, float* grad_out,
-                         float lr, float eps, hipStream_t st);
+                         float lr, float eps, hipStream_t st, const int32_t* slot = nullptr);
 hipError_t launch_combine(const Geom& g, const DevCtx& dc, int mode, int N, const WsLayout& L,
                           const char* ws, const uint32_t* unique_keys, float* grad_out, float lr,
-                          float eps, hipStream_t st);
+                          float eps, hipStream_t st, const int32_t* slot = nullptr);
+
+// shard routing (k_pack.hip); rules: device [T] {kind, shard}
+hipError_t launch_pack_dest(const Geom& g, const DevCtx& dc, const int2* rules, int S, int N,
+                            const uint32_t* ukeys, const int32_t* num_unique, uint64_t* words,
+                            hipStream_t st);
+hipError_t launch_pack_place(const uint64_t* sorted, const uint32_t* ukeys, const int32_t* num_unique,
+                             int N, int S, uint32_t* send_keys, int32_t* slot, hipStream_t st);
+hipError_t launch_pack_offsets(const uint64_t* sorted, int N, int S, int32_t* send_offsets,
+                               hipStream_t st);
 // zero grad[0..U) and scatter-add every lookup's scaled dY row with fp32 atomics
 hipError_t launch_atomic_reduce(const Geom& g, const void* offsets, int itype, long long N, int B,
                                 int pool, const float* dY, const int32_t* inverse,

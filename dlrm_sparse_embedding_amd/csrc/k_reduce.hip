@@ -47,6 +47,7 @@ struct RedArgs {
   float* partial0;
   float* partial1;
   float* grad;  // reduced gradient out (mode 0) or in (apply)
+  const int32_t* slot;  // mode 0: row of grad for segment u (null = u; < 0 = none)
   const DevTable* tables;
   const uint32_t* row_off;
   int T, B, D, Dsl;
@@ -55,16 +56,6 @@ struct RedArgs {
   int ntiles, ntiles1;
   float lr, eps;
 };
-
-__device__ __forceinline__ int table_of(const uint32_t* s_ro, int T, uint32_t key) {
-  int lo = 0, hi = T;  // s_ro[lo] <= key < s_ro[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (s_ro[mid] <= key) lo = mid;
-    else hi = mid;
-  }
-  return lo;
-}
 
 // DT below is the update type code: storage type, | kMasterBit with a master.
 template <int DT>
@@ -122,8 +113,11 @@ template <int DT, int MODE>
 __device__ __forceinline__ void finish_row(const RedArgs& a, const uint32_t* s_ro, uint32_t key,
                                            int seg, int c0, const float* g) {
   if constexpr (MODE == 0) {
-    f4 o = {g[0], g[1], g[2], g[3]};
-    *reinterpret_cast<f4*>(a.grad + (size_t)seg * a.D + c0) = o;
+    const int dst = a.slot ? a.slot[seg] : seg;
+    if ((unsigned)dst < (unsigned)a.N) {
+      f4 o = {g[0], g[1], g[2], g[3]};
+      *reinterpret_cast<f4*>(a.grad + (size_t)dst * a.D + c0) = o;
+    }
   } else {
     const int t = table_of(s_ro, a.T, key);
     char* wp;
@@ -220,8 +214,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
       if constexpr (MODE == 0) {
         const int seg = a.chunk_seg[q];
         if ((unsigned)seg < (unsigned)a.N) {
-          f4 o = {acc[0], acc[1], acc[2], acc[3]};
-          *reinterpret_cast<f4*>(a.grad + (size_t)seg * a.D + c0) = o;
+          const int dst = a.slot ? a.slot[seg] : seg;
+          if ((unsigned)dst < (unsigned)a.N) {
+            f4 o = {acc[0], acc[1], acc[2], acc[3]};
+            *reinterpret_cast<f4*>(a.grad + (size_t)dst * a.D + c0) = o;
+          }
         }
       } else {
         row_update<DT, MODE>(wp, gp, mp, wv, Gv, acc, a.lr, a.eps);
@@ -369,6 +366,7 @@ static RedArgs make_args(const Geom& g, const DevCtx& dc, int N, const WsLayout&
   a.partial0 = const_cast<float*>(reinterpret_cast<const float*>(ws + L.partial0));
   a.partial1 = const_cast<float*>(reinterpret_cast<const float*>(ws + L.partial1));
   a.grad = nullptr;
+  a.slot = nullptr;
   a.tables = dc.tables;
   a.row_off = dc.row_off;
   a.T = g.T;
@@ -459,8 +457,9 @@ static void launch_chunks_pool(bool mean, int lpr, int grid, size_t smem, hipStr
 hipError_t launch_reduce(const Geom& g, const DevCtx& dc, int mode, int N, int B, int pool,
                          const float* dY, const WsLayout& L, const char* ws,
                          const uint32_t* unique_keys, const int32_t* num_unique, float* grad_out,
-                         float lr, float eps, hipStream_t st) {
+                         float lr, float eps, hipStream_t st, const int32_t* slot) {
   RedArgs a = make_args(g, dc, N, L, ws, unique_keys, lr, eps);
+  a.slot = slot;
   a.B = B;
   a.dY = dY;
   const bool mean = pool == EMB_POOL_MEAN;
@@ -480,8 +479,9 @@ hipError_t launch_reduce(const Geom& g, const DevCtx& dc, int mode, int N, int B
 
 hipError_t launch_combine(const Geom& g, const DevCtx& dc, int mode, int N, const WsLayout& L,
                           const char* ws, const uint32_t* unique_keys, float* grad_out, float lr,
-                          float eps, hipStream_t st) {
+                          float eps, hipStream_t st, const int32_t* slot) {
   RedArgs a = make_args(g, dc, N, L, ws, unique_keys, lr, eps);
+  a.slot = slot;
   a.grad = grad_out;
   const int lpr = lpr_b(g);
   const int sgw = 256 / lpr;

@@ -38,7 +38,7 @@ EMB_OPT_SGD, EMB_OPT_ADAGRAD = 0, 1
 EMB_MAX_SLICES = 4
 
 KERNELS = ["init", "forward", "keys", "sort_hist", "sort_scan", "sort_scatter", "rle", "reduce",
-           "combine", "apply", "atomic"]
+           "combine", "apply", "atomic", "pack"]
 
 DTYPE_CODE = {"f32": EMB_F32, "bf16": EMB_BF16, "f16": EMB_F16}
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
@@ -50,6 +50,17 @@ class EmbError(RuntimeError):
     def __init__(self, code: int, msg: str):
         super().__init__(f"emb error {code}: {msg}")
         self.code = code
+
+
+EMB_SHARD_TABLE = 0
+EMB_SHARD_ROW_CYCLIC = 1
+EMB_SHARD_ROW_BLOCK = 2
+EMB_MAX_SHARDS = 4096
+SHARD_KIND = {"table": EMB_SHARD_TABLE, "row_cyclic": EMB_SHARD_ROW_CYCLIC, "row_block": EMB_SHARD_ROW_BLOCK}
+
+
+class emb_shard_rule(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("shard", ctypes.c_int32)]
 
 
 class emb_table_desc(ctypes.Structure):
@@ -94,6 +105,10 @@ def lib() -> ctypes.CDLL:
     L.emb_backward_atomic_reduce.restype = ctypes.c_int
     L.emb_sparse_update.argtypes = [vp, i32, ctypes.c_float, ctypes.c_float, vp, vp, vp, vp]
     L.emb_sparse_update.restype = ctypes.c_int
+    L.emb_set_shard_map.argtypes = [vp, ctypes.POINTER(emb_shard_rule), i32]
+    L.emb_set_shard_map.restype = ctypes.c_int
+    L.emb_pack_by_shard.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
+    L.emb_pack_by_shard.restype = ctypes.c_int
     L.emb_last_error.argtypes = []
     L.emb_last_error.restype = ctypes.c_char_p
     L.emb_check_device_error.argtypes = [vp, vp]
@@ -217,6 +232,22 @@ def emb_set_kernel_timing(ctx: int, enable: bool) -> None:
     _check(lib().emb_set_kernel_timing(ctx, 1 if enable else 0))
 
 
+def emb_set_shard_map(ctx: int, rules, num_shards: int) -> None:
+    """rules: one (kind, shard) per table, kind an EMB_SHARD_* code or a
+    SHARD_KIND name."""
+    arr = (emb_shard_rule * len(rules))()
+    for t, (kind, shard) in enumerate(rules):
+        arr[t].kind = SHARD_KIND.get(kind, kind) if isinstance(kind, str) else int(kind)
+        arr[t].shard = int(shard)
+    _check(lib().emb_set_shard_map(ctx, arr, int(num_shards)))
+
+
+def emb_pack_by_shard(ctx: int, ws, dY, send_keys, send_offsets, slot_of_unique, send_grad,
+                      stream=None) -> None:
+    _check(lib().emb_pack_by_shard(ctx, _ptr(ws), _ptr(dY), _ptr(send_keys), _ptr(send_offsets),
+                                   _ptr(slot_of_unique), _ptr(send_grad), _stream(stream)))
+
+
 def emb_kernel_times(ctx: int) -> dict:
     ms = (ctypes.c_double * len(KERNELS))()
     n = (ctypes.c_int64 * len(KERNELS))()
@@ -336,6 +367,23 @@ class EmbeddingTables:
     def logical_state(self, t: int, rows) -> torch.Tensor:
         r = torch.as_tensor(rows, dtype=torch.int64, device=self.weights[t][0].device)
         return torch.cat([s.index_select(0, r) for s in self.state[t]], dim=1)
+
+    def set_shard_map(self, rules, num_shards: int) -> None:
+        emb_set_shard_map(self.ctx, rules, num_shards)
+
+    def pack_buffers(self, N: int, num_shards: int, with_grad: bool, device="cuda"):
+        cap = max(N, 1)
+        return dict(
+            send_keys=torch.empty(cap, dtype=torch.int32, device=device),   # uint32 bits
+            send_offsets=torch.empty(num_shards + 1, dtype=torch.int32, device=device),
+            slot_of_unique=torch.empty(cap, dtype=torch.int32, device=device),
+            send_grad=(torch.empty((cap, self.dim), dtype=torch.float32, device=device)
+                       if with_grad else None),
+        )
+
+    def pack(self, bufs, pbufs, dY=None, stream=None) -> None:
+        emb_pack_by_shard(self.ctx, bufs["ws"], dY, pbufs["send_keys"], pbufs["send_offsets"],
+                          pbufs["slot_of_unique"], pbufs["send_grad"] if dY is not None else None, stream)
 
     def logical_master(self, t: int, rows) -> torch.Tensor:
         r = torch.as_tensor(rows, dtype=torch.int64, device=self.weights[t][0].device)

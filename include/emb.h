@@ -217,6 +217,51 @@ int emb_backward_atomic_reduce(emb_ctx* ctx, const void* offsets, int32_t itype,
                                int32_t B, int32_t pool, const float* dY, const int32_t* inverse,
                                const int32_t* num_unique, float* reduced_grad, void* hip_stream);
 
+/* ---- routing to shards (the step before an embedding exchange) -------- */
+/* EMBark (RecSys'24 article, embedding clusters and 3D sharding): tables are
+ * split into shards owned by different GPUs, and the reduction-based (RB) and
+ * unique-based (UB) clusters send each distinct key, and its reduced
+ * gradient, once per step. The two calls below are that step for one GPU's
+ * share: they route the unique keys of the last backward to their owner
+ * shards and lay them out (and, for RB, the reduced gradients) grouped by
+ * destination, ready for an all-to-all. Nothing here talks to another GPU. */
+#define EMB_SHARD_TABLE       0   /* every row of the table on shard `shard` */
+#define EMB_SHARD_ROW_CYCLIC  1   /* row r on shard (r + shard) mod S */
+#define EMB_SHARD_ROW_BLOCK   2   /* row r on shard r / ceil(rows / S); shard = 0 */
+#define EMB_MAX_SHARDS        4096
+
+typedef struct emb_shard_rule {
+  int32_t kind;    /* EMB_SHARD_* */
+  int32_t shard;   /* see kind; 0 <= shard < S */
+} emb_shard_rule;
+
+/* Sets the owner rule of every table (rules[T], host memory, copied) and the
+ * shard count S (1..EMB_MAX_SHARDS). EMB_E_INVAL on a bad rule. The first
+ * emb_pack_by_shard after this call uploads the rules (8 bytes per table) to
+ * a device array the context owns, with a synchronous copy. */
+int emb_set_shard_map(emb_ctx* ctx, const emb_shard_rule* rules, int32_t num_shards);
+
+/* Groups the unique keys of this context's last backward (the call that
+ * filled `ws`, with N lookups) by owner shard: a stable sort by destination,
+ * so keys stay ascending inside a shard. Outputs (device, caller-owned):
+ *   send_keys[N]         the keys of shard s at
+ *                        [send_offsets[s], send_offsets[s+1])
+ *   send_offsets[S+1]    send_offsets[S] = number of keys sent
+ *   slot_of_unique[N]    unique key u sits at send_keys[slot_of_unique[u]];
+ *                        -1 for the invalid-index sentinel key (sent nowhere)
+ *   send_grad[N][dim]    RB only (dY != NULL): the reduced gradient of the key
+ *                        at each slot, reduced straight into its slot (the
+ *                        same values, bit for bit, as emb_backward_unique_reduce
+ *                        writes in unique-key order); NULL for keys only (UB).
+ * Entries past send_offsets[S] are unspecified. Uses the sort buffers of `ws`
+ * as scratch and leaves the segment data intact, so emb_sparse_update can still
+ * follow. EMB_E_STATE if ws is not the last backward's workspace or no shard
+ * map is set; EMB_E_INVAL on NULL / misaligned buffers (send_grad and dY are
+ * given together or not at all). */
+int emb_pack_by_shard(emb_ctx* ctx, void* ws, const float* dY, uint32_t* send_keys,
+                      int32_t* send_offsets, int32_t* slot_of_unique, float* send_grad,
+                      void* hip_stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* emb_last_error(void);
 
@@ -244,7 +289,8 @@ int emb_check_device_error(emb_ctx* ctx, void* hip_stream);
 #define EMB_K_COMBINE       8   /* long-segment combine (+ update) */
 #define EMB_K_APPLY         9   /* update from a materialised gradient */
 #define EMB_K_ATOMIC       10   /* atomic reduction (evidence variant) */
-#define EMB_K_COUNT        11
+#define EMB_K_PACK         11   /* shard routing: destinations, placement, offsets */
+#define EMB_K_COUNT        12
 
 /* enable != 0: from now on every kernel launch of this context is
  * bracketed by HIP events recorded on the launch stream. */

@@ -324,3 +324,12 @@ def run_step(cfg, batch, dY, path="fused", sample_bags=None, sample_keys=None, s
     if own:
         tabs.close()
     return result
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def custom_cfg(rows, dim=16, dtype="f32", slices=1, B=8, pool="sum", opt="adagrad"):
+    tabs = tuple(W.TableSpec(r, dim, dtype, slices) for r in rows)
+    return W.Config(99, "custom", tabs, B, pool, opt, 0.05, 1e-8, tuple(1 for _ in rows), None, init_seed=99)

@@ -145,3 +145,33 @@ def test_binding_raises_with_message():
     with pytest.raises(E.EmbError) as ei:
         E.emb_create_tables([_desc(dtype=9)])
     assert ei.value.code == E.EMB_E_DTYPE and "dtype" in str(ei.value)
+
+
+def test_shard_map_validation():
+    rc, ctx = _create([_desc(rows=1000), _desc(rows=5000)])
+    assert rc == E.EMB_OK
+    L = E.lib()
+    def setmap(rules, S):
+        arr = (E.emb_shard_rule * len(rules))()
+        for t, (k, s) in enumerate(rules):
+            arr[t].kind, arr[t].shard = k, s
+        return L.emb_set_shard_map(ctx, arr, S)
+    assert setmap([(E.EMB_SHARD_TABLE, 0), (E.EMB_SHARD_ROW_CYCLIC, 3)], 4) == E.EMB_OK
+    assert setmap([(E.EMB_SHARD_ROW_BLOCK, 0), (E.EMB_SHARD_ROW_BLOCK, 0)], E.EMB_MAX_SHARDS) == E.EMB_OK
+    assert setmap([(E.EMB_SHARD_TABLE, 4), (E.EMB_SHARD_TABLE, 0)], 4) == E.EMB_E_INVAL      # shard >= S
+    assert setmap([(E.EMB_SHARD_ROW_CYCLIC, -1), (E.EMB_SHARD_TABLE, 0)], 4) == E.EMB_E_INVAL
+    assert setmap([(E.EMB_SHARD_ROW_BLOCK, 1), (E.EMB_SHARD_TABLE, 0)], 4) == E.EMB_E_INVAL  # block takes 0
+    assert setmap([(7, 0), (E.EMB_SHARD_TABLE, 0)], 4) == E.EMB_E_INVAL                      # unknown kind
+    assert setmap([(E.EMB_SHARD_TABLE, 0)] * 2, 0) == E.EMB_E_INVAL
+    assert setmap([(E.EMB_SHARD_TABLE, 0)] * 2, E.EMB_MAX_SHARDS + 1) == E.EMB_E_INVAL
+    # packing needs a backward on this context first (no device work is started)
+    rc = L.emb_pack_by_shard(ctx, FAKE, None, FAKE, FAKE, FAKE, None, None)
+    assert rc == E.EMB_E_STATE
+    E.emb_destroy_tables(ctx)
+
+
+def test_pack_needs_shard_map():
+    rc, ctx = _create([_desc(rows=10)])
+    assert E.lib().emb_pack_by_shard(ctx, FAKE, None, FAKE, FAKE, FAKE, None, None) == E.EMB_E_STATE
+    assert "shard map" in E.lib().emb_last_error().decode()
+    E.emb_destroy_tables(ctx)
