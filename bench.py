@@ -57,6 +57,10 @@ def parse():
     ap.add_argument("--master", action="store_true",
                     help="bf16/fp16 tables trained from fp32 master weights (the update steps the master "
                          "and writes the master and its RNE copy in one pass)")
+    ap.add_argument("--pack", type=int, default=0, metavar="S",
+                    help="RB step for an S-shard layout instead of the local update: after the dedup, "
+                         "emb_pack_by_shard routes the unique keys to their owners (cyclic rows) and "
+                         "reduces their gradients straight into the send slots")
     ap.add_argument("--rows", type=int, default=0,
                     help="cap the rows of every table (0 = the workload's own sizes)")
     ap.add_argument("--ceiling", action="store_true",
@@ -162,6 +166,10 @@ def main() -> int:
     Y = torch.empty((B, T * D), dtype=torch.float32, device="cuda")
     nmax = max(b.N for b in host_batches)
     bufs = tabs.backward_buffers(nmax, B, with_grad=args.reduce == "atomic")
+    pbufs = None
+    if args.pack:
+        tabs.set_shard_map([("row_cyclic", t % args.pack) for t in range(T)], args.pack)
+        pbufs = tabs.pack_buffers(nmax, args.pack, with_grad=True)
     torch.cuda.synchronize()
     print(f"[bench] {len(dev)} batches on device, N = {[b.N for b in host_batches]}", file=sys.stderr, flush=True)
 
@@ -196,7 +204,10 @@ def main() -> int:
             tabs.forward(idx, off, B, cfg.pool, out=Y)
         if evs:
             evs[1].record(main)
-        if args.reduce == "fused":
+        if args.pack:
+            tabs.backward(idx, off, B, cfg.pool, dy, bufs)   # skips the dedup done ahead
+            tabs.pack(bufs, pbufs, dY=dy)
+        elif args.reduce == "fused":
             tabs.backward(idx, off, B, cfg.pool, dy, bufs)   # skips the dedup done ahead
             tabs.update(cfg.opt, cfg.lr, cfg.eps, bufs, dY=dy)
         else:
@@ -248,7 +259,10 @@ def main() -> int:
     steps_N = [dev[i % len(dev)][2] for i in range(K)]
     steps_U = [U_of[i % len(dev)] for i in range(K)]
     fwd_bytes = sum(n * rowbytes + n * ib + (T * B + 1) * ib + B * T * D * 4 for n in steps_N)
-    bwd_bytes = sum(B * T * D * 4 + n * ib + (T * B + 1) * ib + u * (wrow_b + 2 * state_b) + u * 8 + n * 4
+    # per unique row: the update's weight (+ state) traffic, or in the RB step
+    # its reduced gradient row written to the send buffer (+ key and slot)
+    urow_b = D * 4 + 8 if args.pack else wrow_b + 2 * state_b
+    bwd_bytes = sum(B * T * D * 4 + n * ib + (T * B + 1) * ib + u * urow_b + u * 8 + n * 4
                     for n, u in zip(steps_N, steps_U))
     lookups = sum(steps_N)
     if args.schedule == "overlap":
@@ -276,7 +290,7 @@ def main() -> int:
         "forward": Navg * rowbytes + Navg * ib + (T * B + 1) * ib + B * T * D * 4,
         # fused reduce + update: every bag's dY row once, each unique row's
         # weight (+ state) read and written once, the sorted bag ids
-        "reduce": B * T * D * 4 + Uavg * (wrow_b + 2 * state_b) + Navg * 4,
+        "reduce": B * T * D * 4 + Uavg * (D * 4 if args.pack else wrow_b + 2 * state_b) + Navg * 4,
         "sort_scatter": Navg * 8 * 2,
         "sort_hist": Navg * 8,
         "keys": Navg * ib * 2 + Navg * (8 + 4),
@@ -313,7 +327,7 @@ def main() -> int:
         "ms_per_step": round(ms_step, 4),
         "ms_per_step_p10_p50_p90": [pct(10), pct(50), pct(90)],
         "schedule": args.schedule,
-        "reduce": args.reduce,
+        "reduce": args.reduce if not args.pack else f"pack to {args.pack} shards (RB)",
         f"ms_per_step_{other}": round(other_ms / K, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -332,9 +346,10 @@ def main() -> int:
             "unique_per_step": int(round(Uavg)),
             "batches_cycled": len(dev),
         },
-        "phases": ("fwd = forward with the dedup on a second stream alongside it; bwd_update = segmented "
-                   "reduce + fused optimizer" if args.schedule == "overlap" else
-                   "fwd = forward; bwd_update = dedup + segmented reduce + fused optimizer"),
+        "phases": ("fwd = forward with the dedup on a second stream alongside it; bwd_update = " if args.schedule == "overlap"
+                   else "fwd = forward; bwd_update = dedup + ") + (
+                   f"routing to {args.pack} shards + reduce into the send slots (RB)" if args.pack
+                   else "segmented reduce + fused optimizer"),
         "fwd": {"ms": round(fwd_ms / K, 4), "lookups_per_s": round(lookups / (fwd_ms * 1e-3), 1),
                 "alg_GBps": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9, 1),
                 "alg_bytes_per_step": int(fwd_bytes / K)},
