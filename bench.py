@@ -61,6 +61,9 @@ def parse():
                     help="RB step for an S-shard layout instead of the local update: after the dedup, "
                          "emb_pack_by_shard routes the unique keys to their owners (cyclic rows) and "
                          "reduces their gradients straight into the send slots")
+    ap.add_argument("--unique-forward", action="store_true",
+                    help="unique-first forward: dedup first, gather each unique row once, pool from the "
+                         "compact rows (emb_forward_pooled_unique); implies the serial schedule")
     ap.add_argument("--rows", type=int, default=0,
                     help="cap the rows of every table (0 = the workload's own sizes)")
     ap.add_argument("--ceiling", action="store_true",
@@ -166,6 +169,7 @@ def main() -> int:
     Y = torch.empty((B, T * D), dtype=torch.float32, device="cuda")
     nmax = max(b.N for b in host_batches)
     bufs = tabs.backward_buffers(nmax, B, with_grad=args.reduce == "atomic")
+    rows_buf = tabs.unique_rows_buffer(nmax) if args.unique_forward else None
     pbufs = None
     if args.pack:
         tabs.set_shard_map([("row_cyclic", t % args.pack) for t in range(T)], args.pack)
@@ -193,7 +197,10 @@ def main() -> int:
         idx, off, n = dev[i % len(dev)]
         if evs:
             evs[0].record(main)
-        if sched == "overlap":
+        if args.unique_forward:
+            tabs.dedup(idx, off, B, cfg.pool, bufs)
+            tabs.forward_unique(idx, off, B, cfg.pool, bufs, rows_buf, out=Y)
+        elif sched == "overlap":
             side.wait_event(ev_free)
             with torch.cuda.stream(side):
                 tabs.dedup(idx, off, B, cfg.pool, bufs)
@@ -265,7 +272,7 @@ def main() -> int:
     bwd_bytes = sum(B * T * D * 4 + n * ib + (T * B + 1) * ib + u * urow_b + u * 8 + n * 4
                     for n, u in zip(steps_N, steps_U))
     lookups = sum(steps_N)
-    if args.schedule == "overlap":
+    if args.schedule == "overlap" or args.unique_forward:
         # the dedup's own I/O (indices, offsets, unique keys + counts, inverse)
         # runs in the forward phase under this schedule
         dd = sum(n * ib + (T * B + 1) * ib + u * 8 + n * 4 for n, u in zip(steps_N, steps_U))
@@ -346,7 +353,9 @@ def main() -> int:
             "unique_per_step": int(round(Uavg)),
             "batches_cycled": len(dev),
         },
-        "phases": ("fwd = forward with the dedup on a second stream alongside it; bwd_update = " if args.schedule == "overlap"
+        "phases": ("fwd = dedup, then the unique-first forward (unique rows gathered once); bwd_update = "
+                   if args.unique_forward else
+                   "fwd = forward with the dedup on a second stream alongside it; bwd_update = " if args.schedule == "overlap"
                    else "fwd = forward; bwd_update = dedup + ") + (
                    f"routing to {args.pack} shards + reduce into the send slots (RB)" if args.pack
                    else "segmented reduce + fused optimizer"),

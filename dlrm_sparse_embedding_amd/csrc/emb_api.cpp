@@ -364,6 +364,42 @@ int emb_forward_pooled(emb_ctx* ctx, const void* indices, const void* offsets, i
   return ok();
 }
 
+int emb_forward_pooled_unique(emb_ctx* ctx, const void* indices, const void* offsets, int32_t itype, int64_t N,
+                              int32_t B, int32_t pool, const void* ws, void* rows_buf, size_t rows_buf_bytes,
+                              float* out, void* hip_stream) {
+  if (!ctx) return fail(EMB_E_INVAL, "ctx is NULL");
+  int rc = check_itype(itype);
+  if (rc) return rc;
+  if ((rc = check_pool(pool))) return rc;
+  if (B < 0 || N < 0) return fail(EMB_E_INVAL, "negative B or N");
+  if (N >= (1ll << 31)) return fail(EMB_E_INVAL, "N must be < 2^31");
+  if (B == 0) return N == 0 ? ok() : fail(EMB_E_INVAL, "B == 0 with N > 0");
+  if (!offsets || !out) return fail(EMB_E_INVAL, "offsets/out is NULL");
+  if (!aligned(out, 16)) return fail(EMB_E_INVAL, "out must be 16-byte aligned");
+  const auto& d = ctx->dedup;
+  if (!(d.valid && d.indices == indices && d.offsets == offsets && d.itype == itype && d.N == N && d.B == B &&
+        d.pool == pool && d.ws == ws))
+    return fail(EMB_E_STATE, "no dedup of these lookups was done ahead on this context (emb_backward_dedup)");
+  const size_t need = (size_t)N * ctx->g.D * dtype_bytes(ctx->g.dtype);
+  if (N > 0 && (!rows_buf || !aligned(rows_buf, 16))) return fail(EMB_E_INVAL, "rows_buf is NULL or misaligned");
+  if (rows_buf_bytes < need) return fail(EMB_E_WORKSPACE, "rows_buf of %zu bytes < %zu needed", rows_buf_bytes, need);
+  if ((rc = ensure_device(ctx))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  hipError_t e;
+  {
+    KScope ks(ctx, EMB_K_GATHER, st);
+    if ((e = launch_gather_unique(ctx->g, ctx->dc, d.unique_keys, d.num_unique, (int)N, rows_buf, st)) != hipSuccess)
+      return hip_fail(e, "gather unique rows");
+  }
+  {
+    KScope ks(ctx, EMB_K_FORWARD, st);
+    if ((e = launch_forward(ctx->g, ctx->dc, d.inverse, offsets, itype, N, B, pool, out, ctx->fwd_max_blocks, st,
+                            rows_buf, N)) != hipSuccess)
+      return hip_fail(e, "forward from unique rows");
+  }
+  return ok();
+}
+
 size_t emb_backward_workspace_bytes(const emb_ctx* ctx, int64_t N, int32_t B) {
   if (!ctx || N < 0 || B < 0 || N >= (1ll << 31)) return 0;
   return ws_layout(ctx->g, N, B).total;

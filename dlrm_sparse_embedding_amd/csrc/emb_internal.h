@@ -102,10 +102,15 @@ WsLayout ws_layout(const Geom& g, long long N, int B);
 hipError_t launch_init_slice(const Geom& g, const DevCtx& dc, int t, int s, int64_t rows, void* w,
                              float* state, float* master, uint64_t seed, hipStream_t st);
 
-// max_blocks > 0 caps the grid (the kernel strides over the rest)
+// max_blocks > 0 caps the grid (the kernel strides over the rest). flat
+// (optional): pool from a compact [flat_rows][D] buffer of the storage type
+// instead of the tables, with int32 indices into it (the unique-first forward).
 hipError_t launch_forward(const Geom& g, const DevCtx& dc, const void* indices, const void* offsets,
                           int itype, long long N, int B, int pool, float* out, int max_blocks,
-                          hipStream_t st);
+                          hipStream_t st, const void* flat = nullptr, long long flat_rows = 0);
+// rows[u] = logical row of unique key u (storage type), u < min(*num_unique, cap)
+hipError_t launch_gather_unique(const Geom& g, const DevCtx& dc, const uint32_t* ukeys,
+                                const int32_t* num_unique, int cap, void* rows, hipStream_t st);
 
 hipError_t launch_keys(const Geom& g, const DevCtx& dc, const void* indices, const void* offsets,
                        int itype, long long N, int B, int pool, const WsLayout& L, char* ws,

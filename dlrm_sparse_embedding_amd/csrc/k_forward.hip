@@ -20,6 +20,12 @@
 // are written with non-temporal stores so the L2 keeps Zipf-hot table rows.
 // The grid may be capped (grid-stride over the work) so that the dedup, run
 // on a second stream, keeps some wave slots while the forward streams.
+//
+// Unique-first variant (FLAT): after the step's keys are deduplicated, each
+// unique row is gathered once into a compact [U][D] buffer (k_gather_unique)
+// and the bags are pooled from it through the lookups' inverse indices -- the
+// unique-based side of EMBark's compression (RecSys'24 article, embedding
+// clusters) applied to the forward on one GPU's share.
 #include "emb_device.h"
 
 namespace emb {
@@ -38,12 +44,15 @@ struct FwdArgs {
   long long total_sg;
   int nblk;
   int mean;
+  const void* flat;    // FLAT: the compact rows, [flat_rows][D] of the storage type,
+                       // indexed by int32 `indices` (offsets stay of type IDX)
+  long long flat_rows;
 };
 
 // 8 waves/SIMD with 4 rows in flight per subgroup measured faster than 5
 // waves/SIMD with 8 rows (293 -> 277 us on the 26x4Mx128 one-hot workload).
 // Positions are 32-bit (N < 2^31 is validated) to stay within 64 VGPRs.
-template <int DT, typename IDX, int LPR>
+template <int DT, typename IDX, int LPR, bool FLAT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_forward(FwdArgs a) {
   constexpr int CPL = 16 / Stor<DT>::kBytes;  // columns per lane
   constexpr int SGW = 256 / LPR;              // subgroups per block
@@ -68,15 +77,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
     const int P0 = __shfl(my_off, 0, LPR);
     const int P1 = __shfl(my_off, nb, LPR);
 
-    const uint32_t ro = a.row_off[t];
-    const uint32_t rows_t = a.row_off[t + 1] - ro;
     const int c0 = lsg * CPL;
     const bool act = c0 < a.D;
-    const int s = act ? c0 / a.Dsl : 0;
-    const int cs = c0 - s * a.Dsl;
-    const char* wbase =
-        reinterpret_cast<const char*>(a.tables[t].w[s]) + (size_t)cs * Stor<DT>::kBytes;
-    const size_t rstride = (size_t)a.Dsl * Stor<DT>::kBytes;
+    long long rows_t;
+    const char* wbase;
+    size_t rstride;
+    if constexpr (FLAT) {
+      rows_t = a.flat_rows;
+      wbase = reinterpret_cast<const char*>(a.flat) + (size_t)c0 * Stor<DT>::kBytes;
+      rstride = (size_t)a.D * Stor<DT>::kBytes;
+    } else {
+      rows_t = (long long)(a.row_off[t + 1] - a.row_off[t]);
+      const int s = act ? c0 / a.Dsl : 0;
+      const int cs = c0 - s * a.Dsl;
+      wbase = reinterpret_cast<const char*>(a.tables[t].w[s]) + (size_t)cs * Stor<DT>::kBytes;
+      rstride = (size_t)a.Dsl * Stor<DT>::kBytes;
+    }
     const size_t ostride = (size_t)a.T * a.D;
     float* obase = a.out + (size_t)b0 * ostride + (size_t)t * a.D + c0;
 
@@ -113,8 +129,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
       for (int k = 0; k < U; ++k) {
         v[k] = u4{0u, 0u, 0u, 0u};
         if (p + k < P1) {
-          const long long r = ld_idx<IDX>(a.indices, p + k);
-          if (r >= 0 && r < (long long)rows_t) {
+          // FLAT reads the dedup's int32 inverse; offsets keep the caller's type
+          const long long r = FLAT ? (long long)reinterpret_cast<const int32_t*>(a.indices)[p + k]
+                                   : ld_idx<IDX>(a.indices, p + k);
+          if (r >= 0 && r < rows_t) {
             if (act) v[k] = *reinterpret_cast<const u4*>(wbase + (size_t)r * rstride);
           } else {
             bad = 1;
@@ -148,8 +166,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
   }
 }
 
-#define FWD_LAUNCH(DT, IDX, LPR)                                                        \
-  hipLaunchKernelGGL((k_forward<DT, IDX, LPR>), dim3(grid), dim3(256), 0, st, args); \
+#define FWD_LAUNCH(DT, IDX, LPR)                                                               \
+  if (args.flat)                                                                            \
+    hipLaunchKernelGGL((k_forward<DT, IDX, LPR, true>), dim3(grid), dim3(256), 0, st, args);  \
+  else                                                                                      \
+    hipLaunchKernelGGL((k_forward<DT, IDX, LPR, false>), dim3(grid), dim3(256), 0, st, args); \
   break;
 
 #define FWD_LPR_SWITCH(DT, IDX)                \
@@ -171,7 +192,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
 
 hipError_t launch_forward(const Geom& g, const DevCtx& dc, const void* indices, const void* offsets,
                           int itype, long long N, int B, int pool, float* out, int max_blocks,
-                          hipStream_t st) {
+                          hipStream_t st, const void* flat, long long flat_rows) {
   if (B == 0 || g.T == 0) return hipSuccess;
   const int cpl = 16 / (g.dtype == EMB_F32 ? 4 : 2);
   int lpr = next_pow2((g.D + cpl - 1) / cpl);
@@ -200,6 +221,8 @@ hipError_t launch_forward(const Geom& g, const DevCtx& dc, const void* indices, 
   const int sgw = 256 / lpr;
   args.nblk = (int)((args.total_sg + sgw - 1) / sgw);
   args.mean = pool == EMB_POOL_MEAN;
+  args.flat = flat;
+  args.flat_rows = flat_rows;
   const int grid = max_blocks > 0 && max_blocks < args.nblk ? max_blocks : args.nblk;
   switch (g.dtype) {
     case EMB_F32:
@@ -212,6 +235,83 @@ hipError_t launch_forward(const Geom& g, const DevCtx& dc, const void* indices, 
       FWD_IDX_SWITCH(EMB_F16)
       break;
   }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// unique rows -> compact buffer
+// ---------------------------------------------------------------------------
+
+// One subgroup of LPR lanes per unique key u < U: its logical row (all column
+// slices) is copied, in the storage type, to rows[u]; the invalid-index
+// sentinel key gets a zero row (such lookups pool to nothing, as in the
+// direct forward).
+template <int DT, int LPR>
+__global__ __launch_bounds__(256) void k_gather_unique(const DevTable* __restrict__ tables,
+                                                       const uint32_t* __restrict__ row_off,
+                                                       const uint32_t* __restrict__ ukeys,
+                                                       const int32_t* __restrict__ num_unique, int cap,
+                                                       int T, int D, int Dsl, uint32_t total_rows,
+                                                       void* __restrict__ rows) {
+  extern __shared__ uint32_t s_ro[];
+  for (int i = threadIdx.x; i <= T; i += 256) s_ro[i] = row_off[i];
+  __syncthreads();
+  constexpr int CPL = 16 / Stor<DT>::kBytes;
+  constexpr int SGW = 256 / LPR;
+  const int lsg = threadIdx.x & (LPR - 1);
+  const int c0 = lsg * CPL;
+  if (c0 >= D) return;
+  const int U = min(max(*num_unique, 0), cap);
+  const size_t rbytes = (size_t)D * Stor<DT>::kBytes;
+  for (long long u = (long long)blockIdx.x * SGW + threadIdx.x / LPR; u < U; u += (long long)gridDim.x * SGW) {
+    const uint32_t key = ukeys[u];
+    u4 v = {0u, 0u, 0u, 0u};
+    if (key < total_rows) {
+      const int t = table_of(s_ro, T, key);
+      const int s = c0 / Dsl;
+      const size_t e = (size_t)(key - s_ro[t]) * Dsl + (c0 - s * Dsl);
+      v = *reinterpret_cast<const u4*>(reinterpret_cast<const char*>(tables[t].w[s]) + e * Stor<DT>::kBytes);
+    }
+    *reinterpret_cast<u4*>(reinterpret_cast<char*>(rows) + (size_t)u * rbytes + (size_t)c0 * Stor<DT>::kBytes) = v;
+  }
+}
+
+hipError_t launch_gather_unique(const Geom& g, const DevCtx& dc, const uint32_t* ukeys,
+                                const int32_t* num_unique, int cap, void* rows, hipStream_t st) {
+  if (cap <= 0) return hipSuccess;
+  const int cpl = 16 / (g.dtype == EMB_F32 ? 4 : 2);
+  int lpr = next_pow2((g.D + cpl - 1) / cpl);
+  if (lpr < 2) lpr = 2;
+  const int sgw = 256 / lpr;
+  const long long want = ((long long)cap + sgw - 1) / sgw;
+  const int grid = (int)(want < 16384 ? want : 16384);
+  const size_t smem = (size_t)(g.T + 1) * 4;
+#define GU(DT, P)                                                                                       \
+  hipLaunchKernelGGL((k_gather_unique<DT, P>), dim3(grid), dim3(256), smem, st, dc.tables, dc.row_off, \
+                     ukeys, num_unique, cap, g.T, g.D, g.Dsl, g.total_rows, rows);                      \
+  break;
+#define GU_LPR(DT)             \
+  switch (lpr) {               \
+    case 2: GU(DT, 2)          \
+    case 4: GU(DT, 4)          \
+    case 8: GU(DT, 8)          \
+    case 16: GU(DT, 16)        \
+    case 32: GU(DT, 32)        \
+    default: GU(DT, 64)        \
+  }
+  switch (g.dtype) {
+    case EMB_F32:
+      GU_LPR(EMB_F32)
+      break;
+    case EMB_BF16:
+      GU_LPR(EMB_BF16)
+      break;
+    default:
+      GU_LPR(EMB_F16)
+      break;
+  }
+#undef GU_LPR
+#undef GU
   return hipGetLastError();
 }
 

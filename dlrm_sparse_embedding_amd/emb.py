@@ -38,7 +38,7 @@ EMB_OPT_SGD, EMB_OPT_ADAGRAD = 0, 1
 EMB_MAX_SLICES = 4
 
 KERNELS = ["init", "forward", "keys", "sort_hist", "sort_scan", "sort_scatter", "rle", "reduce",
-           "combine", "apply", "atomic", "pack"]
+           "combine", "apply", "atomic", "pack", "gather"]
 
 DTYPE_CODE = {"f32": EMB_F32, "bf16": EMB_BF16, "f16": EMB_F16}
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
@@ -105,6 +105,8 @@ def lib() -> ctypes.CDLL:
     L.emb_backward_atomic_reduce.restype = ctypes.c_int
     L.emb_sparse_update.argtypes = [vp, i32, ctypes.c_float, ctypes.c_float, vp, vp, vp, vp]
     L.emb_sparse_update.restype = ctypes.c_int
+    L.emb_forward_pooled_unique.argtypes = [vp, vp, vp, i32, i64, i32, i32, vp, vp, sz, vp, vp]
+    L.emb_forward_pooled_unique.restype = ctypes.c_int
     L.emb_set_shard_map.argtypes = [vp, ctypes.POINTER(emb_shard_rule), i32]
     L.emb_set_shard_map.restype = ctypes.c_int
     L.emb_pack_by_shard.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
@@ -230,6 +232,14 @@ def emb_check_device_error(ctx: int, stream=None) -> None:
 
 def emb_set_kernel_timing(ctx: int, enable: bool) -> None:
     _check(lib().emb_set_kernel_timing(ctx, 1 if enable else 0))
+
+
+def emb_forward_pooled_unique(ctx: int, indices, offsets, B: int, pool: str, ws, rows_buf, out,
+                              stream=None) -> None:
+    _check(lib().emb_forward_pooled_unique(
+        ctx, _ptr(indices), _ptr(offsets), _itype(indices), int(indices.numel()), int(B), POOL_CODE[pool],
+        _ptr(ws), _ptr(rows_buf), int(rows_buf.numel() * rows_buf.element_size()) if rows_buf is not None else 0,
+        _ptr(out), _stream(stream)))
 
 
 def emb_set_shard_map(ctx: int, rules, num_shards: int) -> None:
@@ -367,6 +377,17 @@ class EmbeddingTables:
     def logical_state(self, t: int, rows) -> torch.Tensor:
         r = torch.as_tensor(rows, dtype=torch.int64, device=self.weights[t][0].device)
         return torch.cat([s.index_select(0, r) for s in self.state[t]], dim=1)
+
+    def unique_rows_buffer(self, N: int, device="cuda") -> torch.Tensor:
+        """Capacity for emb_forward_pooled_unique: N rows of the storage type."""
+        return torch.empty((max(N, 1), self.dim), dtype=TORCH_DTYPE[self.dtype], device=device)
+
+    def forward_unique(self, indices, offsets, B: int, pool: str, bufs, rows_buf, out=None, stream=None):
+        """Unique-first forward; needs self.dedup(...) of the same lookups first."""
+        if out is None:
+            out = torch.empty((B, self.T * self.dim), dtype=torch.float32, device=indices.device)
+        emb_forward_pooled_unique(self.ctx, indices, offsets, B, pool, bufs["ws"], rows_buf, out, stream)
+        return out
 
     def set_shard_map(self, rules, num_shards: int) -> None:
         emb_set_shard_map(self.ctx, rules, num_shards)

@@ -148,6 +148,22 @@ int emb_forward_pooled(emb_ctx* ctx, const void* indices, const void* offsets,
                        int32_t itype, int64_t N, int32_t B, int32_t pool,
                        float* out, void* hip_stream);
 
+/* Unique-first pooled forward: the unique-based compression of the EMBark
+ * article (RecSys'24, embedding clusters) on the forward side. Needs the
+ * dedup of the same lookups done ahead by emb_backward_dedup on this context
+ * (same indices, offsets, itype, N, B, pool and ws); it reads that dedup's
+ * unique keys, count and inverse. Each unique row is gathered once into
+ * rows_buf (capacity N rows of dim elements of the storage type, 16-byte
+ * aligned, rows_buf_bytes >= N * dim * sizeof(storage)), then every bag is
+ * pooled from rows_buf through the inverse. out is bit-identical to
+ * emb_forward_pooled's (the same rows are added in the same order). The dedup
+ * stays valid for the backward that follows. EMB_E_STATE without a matching
+ * dedup, EMB_E_WORKSPACE if rows_buf is too small. */
+int emb_forward_pooled_unique(emb_ctx* ctx, const void* indices, const void* offsets,
+                              int32_t itype, int64_t N, int32_t B, int32_t pool, const void* ws,
+                              void* rows_buf, size_t rows_buf_bytes, float* out,
+                              void* hip_stream);
+
 /* Bytes of workspace emb_backward_unique_reduce needs for N lookups and
  * batch B (0 on invalid arguments). */
 size_t emb_backward_workspace_bytes(const emb_ctx* ctx, int64_t N, int32_t B);
@@ -290,7 +306,8 @@ int emb_check_device_error(emb_ctx* ctx, void* hip_stream);
 #define EMB_K_APPLY         9   /* update from a materialised gradient */
 #define EMB_K_ATOMIC       10   /* atomic reduction (evidence variant) */
 #define EMB_K_PACK         11   /* shard routing: destinations, placement, offsets */
-#define EMB_K_COUNT        12
+#define EMB_K_GATHER       12   /* unique rows into the compact buffer */
+#define EMB_K_COUNT        13
 
 /* enable != 0: from now on every kernel launch of this context is
  * bracketed by HIP events recorded on the launch stream. */

@@ -175,3 +175,10 @@ def test_pack_needs_shard_map():
     assert E.lib().emb_pack_by_shard(ctx, FAKE, None, FAKE, FAKE, FAKE, None, None) == E.EMB_E_STATE
     assert "shard map" in E.lib().emb_last_error().decode()
     E.emb_destroy_tables(ctx)
+
+
+def test_unique_forward_needs_dedup_ahead():
+    rc, ctx = _create([_desc(rows=10)])
+    rc = E.lib().emb_forward_pooled_unique(ctx, FAKE, FAKE, E.EMB_I32, 4, 4, 0, FAKE, FAKE, 1 << 20, FAKE, None)
+    assert rc == E.EMB_E_STATE
+    E.emb_destroy_tables(ctx)
