@@ -47,6 +47,15 @@ What is computed, and where the pages define it
   one shard; rows dealt cyclically; rows in S contiguous blocks), and the
   unique keys (with their reduced gradients) are grouped by destination
   shard, keys ascending inside a group.
+* Hash-keyed lookup -- GTC 2022 deck, slide "HUGECTR EMBEDDING LAYER" (a GPU
+  hash table lookup fused with the reduction and concatenation), and the
+  dynamic embedding of the Sparse Operation Kit 2.0 article: feature ids are
+  arbitrary 64-bit values, and each table maps them to its rows. Read here
+  as: an id a table has not seen gets, when insertion is on, the table's
+  next free row, ids taken in order of first appearance in the CSR; once a
+  table's rows are used up, new ids get no row (their lookups pool to
+  nothing) and stay known as row-less; with insertion off, unseen ids get no
+  row.
 * Untouched rows -- a dense step with g = 0 and G = 0 leaves w and G bit for
   bit unchanged, so only touched rows are computed.
 * Table contents -- synthetic: each element is a counter hash of (seed, table,
@@ -63,7 +72,7 @@ __all__ = [
     "to_storage", "TouchedRows", "pooled_forward", "global_keys", "dedup",
     "bag_of_positions", "reduced_grad", "sgd_step", "adagrad_step",
     "update_rows", "update_rows_master", "SHARD_TABLE", "SHARD_ROW_CYCLIC", "SHARD_ROW_BLOCK",
-    "shard_of_keys", "pack_by_shard",
+    "shard_of_keys", "pack_by_shard", "HashTables",
 ]
 
 _U64 = np.uint64
@@ -373,3 +382,37 @@ def pack_by_shard(unique_keys: np.ndarray, row_offset: np.ndarray, rules, S: int
     slot[order] = np.arange(len(order))
     send_grad = None if reduced_grad is None else np.asarray(reduced_grad)[order]
     return u[order], offsets, slot, send_grad
+
+
+# ---------------------------------------------------------------------------
+# Hash-keyed lookup: 64-bit ids -> rows, handed out on first sight
+# ---------------------------------------------------------------------------
+
+class HashTables:
+    """Per-table id -> row maps (plain dicts). rows[t] is table t's capacity.
+    A row of -1 marks an id that arrived when its table was full."""
+
+    def __init__(self, rows):
+        self.rows = [int(r) for r in rows]
+        self.maps = [dict() for _ in self.rows]
+        self.next_free = [0] * len(self.rows)
+
+    def translate(self, ids, offsets, T: int, B: int, insert: bool) -> np.ndarray:
+        """Rows of the N lookups (-1 = no row), walking the CSR in order."""
+        ids = np.asarray(ids, dtype=np.int64)
+        offsets = np.asarray(offsets, dtype=np.int64)
+        out = np.full(len(ids), -1, dtype=np.int64)
+        for t in range(T):
+            m = self.maps[t]
+            for p in range(int(offsets[t * B]), int(offsets[(t + 1) * B])):
+                x = int(ids[p])
+                if x in m:
+                    out[p] = m[x]
+                elif insert:
+                    if self.next_free[t] < self.rows[t]:
+                        m[x] = self.next_free[t]
+                        self.next_free[t] += 1
+                    else:
+                        m[x] = -1
+                    out[p] = m[x]
+        return out

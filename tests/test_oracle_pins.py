@@ -674,3 +674,111 @@ def test_pack_pin_catches_mistakes():
     assert not _pack_pin_ok(floor_block)
     assert not _pack_pin_ok(unstable)
     assert not _pack_pin_ok(no_shift)
+
+
+# ---------------------------------------------------------------------------
+# Hash-keyed lookup
+# ---------------------------------------------------------------------------
+
+def _translate_numpy(ids, offsets, T, B, rows, insert, state):
+    """An independent formulation for a fresh step: per table, the new ids
+    ranked by their first position (np.unique's first indices, sorted) get
+    next_free + rank while rows last. state = (maps, next_free) it updates."""
+    maps, nf = state
+    out = np.full(len(ids), -1, dtype=np.int64)
+    for t in range(T):
+        a, b = int(offsets[t * B]), int(offsets[(t + 1) * B])
+        seg = np.asarray(ids[a:b], dtype=np.int64)
+        if len(seg) == 0:
+            continue
+        known = np.array([x in maps[t] for x in seg.tolist()], dtype=bool)
+        if insert:
+            new_ids, first = np.unique(seg[~known], return_index=True)
+            pos = np.nonzero(~known)[0][first]
+            order = np.argsort(pos)
+            for rank, x in enumerate(new_ids[order].tolist()):
+                r = nf[t] + rank
+                maps[t][x] = r if r < rows[t] else -1
+            nf[t] = min(rows[t], nf[t] + len(new_ids))
+        out[a:b] = [maps[t].get(x, -1) for x in seg.tolist()]
+    return out
+
+
+def _hash_case(seed):
+    rng = np.random.default_rng(seed)
+    T, B = 3, int(rng.integers(1, 40))
+    rows = [int(x) for x in rng.integers(1, 30, T)]
+    lens = rng.integers(0, 5, T * B)
+    offsets = np.concatenate([[0], np.cumsum(lens)])
+    ids = rng.choice(np.array([-5, 7, 2**40 + 3, -2**62, 11, 12, 13, 99, 100, 2**63 - 1] + list(range(200, 240))),
+                     int(offsets[-1]))
+    return T, B, rows, ids, offsets
+
+
+def test_hash_translate_matches_numpy_formulation():
+    for seed in range(60):
+        T, B, rows, ids, offsets = _hash_case(seed)
+        ht = O.HashTables(rows)
+        state = ([dict() for _ in rows], [0] * T)
+        for step in range(3):                      # several steps on the same maps
+            insert = step != 1
+            a = ht.translate(ids, offsets, T, B, insert)
+            b = _translate_numpy(ids, offsets, T, B, rows, insert, state)
+            assert np.array_equal(a, b), (seed, step)
+            ids = np.roll(ids, 3)
+
+
+def test_hash_translate_invariants():
+    T, B, rows, ids, offsets = 2, 6, [3, 100], np.array([9, 9, 4, 5, 6, 4, 7, 1, 2, 1]), np.array(
+        [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 10, 10])
+    ht = O.HashTables(rows)
+    got = ht.translate(ids, offsets, T, B, True)
+    # table 0 (positions 0..5: 9 9 4 5 6 4): first sights 9, 4, 5 take rows 0..2, 6 finds it full
+    assert got[:6].tolist() == [0, 0, 1, 2, -1, 1]
+    assert got[6:].tolist() == [0, 1, 2, 1]          # table 1 counts from its own row 0
+    # lookup-only: an unseen id has no row, a known one keeps its row
+    got2 = ht.translate(np.array([6, 4, 3, 3, 7, 8, 8, 8, 8, 8]), offsets, T, B, False)
+    assert got2[:6].tolist() == [-1, 1, -1, -1, -1, -1] and got2[6] == -1
+    assert ht.next_free == [3, 3]
+
+
+def test_hash_pin_catches_mistakes():
+    class LastSight(O.HashTables):                  # ranks new ids by last appearance
+        def translate(self, ids, offsets, T, B, insert):
+            out = np.full(len(ids), -1, dtype=np.int64)
+            for t in range(T):
+                a, b = int(offsets[t * B]), int(offsets[(t + 1) * B])
+                for p in range(b - 1, a - 1, -1):
+                    x = int(ids[p])
+                    if x not in self.maps[t] and insert:
+                        self.maps[t][x] = self.next_free[t] if self.next_free[t] < self.rows[t] else -1
+                        self.next_free[t] = min(self.rows[t], self.next_free[t] + 1)
+                for p in range(a, b):
+                    out[p] = self.maps[t].get(int(ids[p]), -1)
+            return out
+
+    class SharedCounter(O.HashTables):              # one row counter for all tables
+        def translate(self, ids, offsets, T, B, insert):
+            out = np.full(len(ids), -1, dtype=np.int64)
+            nxt = 0
+            for t in range(T):
+                for p in range(int(offsets[t * B]), int(offsets[(t + 1) * B])):
+                    x = int(ids[p])
+                    if x not in self.maps[t] and insert:
+                        self.maps[t][x] = nxt if nxt < self.rows[t] else -1
+                        nxt += 1
+                    out[p] = self.maps[t].get(x, -1)
+            return out
+
+    def ok(cls):
+        for seed in range(30):
+            T, B, rows, ids, offsets = _hash_case(seed)
+            a = cls(rows).translate(ids, offsets, T, B, True)
+            b = _translate_numpy(ids, offsets, T, B, rows, True, ([dict() for _ in rows], [0] * T))
+            if not np.array_equal(a, b):
+                return False
+        return True
+
+    assert ok(O.HashTables)
+    assert not ok(LastSight)
+    assert not ok(SharedCounter)
