@@ -89,6 +89,10 @@ struct emb_ctx {
   int num_shards = 0;
   void* dev_rules = nullptr;
   bool rules_dirty = false;
+  // hash maps (emb_hash_attach)
+  void* dev_hmeta = nullptr;
+  HashView hv{};
+  bool hash_ready = false;
   // timing
   bool timing = false;
   std::vector<TimedLaunch> pending;
@@ -318,6 +322,7 @@ void emb_destroy_tables(emb_ctx* ctx) {
   }
   for (auto e : ctx->free_events) (void)hipEventDestroy(e);
   if (ctx->dev_rules) (void)hipFree(ctx->dev_rules);
+  if (ctx->dev_hmeta) (void)hipFree(ctx->dev_hmeta);
   delete ctx;
 }
 
@@ -636,6 +641,161 @@ int emb_backward_atomic_reduce(emb_ctx* ctx, const void* offsets, int32_t itype,
   return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+struct HashLayout {
+  std::vector<HashMeta> meta;
+  long long slots = 0;
+  size_t keys_off = 0, vals_off = 0, nf_off = 0, total = 0;
+};
+
+size_t a256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Map layout: 2^k >= 2 * rows slots per table (at least 64), keys | values |
+// per-table counters. total = 0 if the slots do not fit int32.
+HashLayout hash_layout(const emb_ctx* c) {
+  HashLayout h;
+  long long base = 0;
+  for (int t = 0; t < c->g.T; ++t) {
+    const long long rows = c->desc[t].rows;
+    long long cap = 64;
+    while (cap < 2 * rows) cap <<= 1;
+    if (rows >= 0x7fffffffll || base + cap >= (1ll << 31)) return HashLayout{};
+    h.meta.push_back(HashMeta{base, (uint32_t)(cap - 1), (int)rows});
+    base += cap;
+  }
+  h.slots = base;
+  h.keys_off = 0;
+  h.vals_off = a256((size_t)base * 8);
+  h.nf_off = a256(h.vals_off + (size_t)base * 4);
+  h.total = a256(h.nf_off + (size_t)c->g.T * 4);
+  return h;
+}
+
+struct HashWs {
+  size_t slot_of_pos = 0, pkeys = 0, paux = 0, pval = 0, blk = 0, rank_base = 0, total = 0;
+};
+
+HashWs hash_ws(const emb_ctx* c, long long N) {
+  HashWs w;
+  w.slot_of_pos = 0;
+  w.pkeys = a256((size_t)N * 4);
+  w.paux = a256(w.pkeys + (size_t)N * 16);
+  w.pval = a256(w.paux + (size_t)N * 8);
+  w.blk = a256(w.pval + (size_t)N * 8);
+  w.rank_base = a256(w.blk + (size_t)(N / 2048 + 2) * 4);
+  w.total = a256(w.rank_base + (size_t)(c->g.T + 1) * 4);
+  return w;
+}
+
+int check_lookup_args(emb_ctx* ctx, const void* ids, const void* offsets, int32_t itype, int64_t N, int32_t B) {
+  if (!ctx) return fail(EMB_E_INVAL, "ctx is NULL");
+  int rc = check_itype(itype);
+  if (rc) return rc;
+  if (B < 0 || N < 0) return fail(EMB_E_INVAL, "negative B or N");
+  if (N >= (1ll << 31)) return fail(EMB_E_INVAL, "N must be < 2^31");
+  if (B == 0 && N > 0) return fail(EMB_E_INVAL, "B == 0 with N > 0");
+  if (B > 0 && !offsets) return fail(EMB_E_INVAL, "offsets is NULL");
+  if (N > 0 && !ids) return fail(EMB_E_INVAL, "ids is NULL");
+  if (!ctx->hash_ready) return fail(EMB_E_STATE, "no hash map memory attached");
+  return EMB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t emb_hash_bytes(const emb_ctx* ctx) {
+  if (!ctx) return 0;
+  return hash_layout(ctx).total;
+}
+
+int emb_hash_attach(emb_ctx* ctx, void* mem, size_t bytes, void* hip_stream) {
+  if (!ctx) return fail(EMB_E_INVAL, "ctx is NULL");
+  const HashLayout h = hash_layout(ctx);
+  if (h.total == 0) return fail(EMB_E_INVAL, "tables too large for the hash maps' int32 slot indices");
+  if (!mem || !aligned(mem, 256)) return fail(EMB_E_INVAL, "map memory is NULL or not 256-byte aligned");
+  if (bytes < h.total) return fail(EMB_E_WORKSPACE, "map memory of %zu bytes < %zu needed", bytes, h.total);
+  int rc;
+  if ((rc = ensure_device(ctx))) return rc;
+  hipError_t e;
+  const size_t mbytes = sizeof(HashMeta) * h.meta.size();
+  if (!ctx->dev_hmeta) {
+    if ((e = hipMalloc(&ctx->dev_hmeta, mbytes)) != hipSuccess) return hip_fail(e, "hipMalloc(hash layout)");
+  }
+  if ((e = hipMemcpy(ctx->dev_hmeta, h.meta.data(), mbytes, hipMemcpyHostToDevice)) != hipSuccess)
+    return hip_fail(e, "hipMemcpy(hash layout)");
+  char* m = static_cast<char*>(mem);
+  HashView& v = ctx->hv;
+  v.meta = static_cast<const HashMeta*>(ctx->dev_hmeta);
+  v.keys = reinterpret_cast<unsigned long long*>(m + h.keys_off);
+  v.vals = reinterpret_cast<int*>(m + h.vals_off);
+  v.next_free = reinterpret_cast<int*>(m + h.nf_off);
+  v.slots = h.slots;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  KScope ks(ctx, EMB_K_HASH, st);
+  if ((e = launch_hash_clear(v, ctx->g.T, st)) != hipSuccess) return hip_fail(e, "hash map reset");
+  ctx->hash_ready = true;
+  return ok();
+}
+
+size_t emb_hash_workspace_bytes(const emb_ctx* ctx, int64_t N) {
+  if (!ctx || N < 0 || N >= (1ll << 31)) return 0;
+  return hash_ws(ctx, N).total;
+}
+
+int emb_hash_translate(emb_ctx* ctx, const int64_t* ids, const void* offsets, int32_t itype, int64_t N, int32_t B,
+                       int32_t insert, void* ws, size_t ws_bytes, void* rows_out, void* hip_stream) {
+  int rc = check_lookup_args(ctx, ids, offsets, itype, N, B);
+  if (rc) return rc;
+  if (N > 0 && !rows_out) return fail(EMB_E_INVAL, "rows_out is NULL");
+  const HashWs L = hash_ws(ctx, N);
+  if (N > 0 && (!ws || !aligned(ws, 256))) return fail(EMB_E_INVAL, "ws is NULL or not 256-byte aligned");
+  if (N > 0 && ws_bytes < L.total) return fail(EMB_E_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, L.total);
+  if ((rc = ensure_device(ctx))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  char* w = static_cast<char*>(ws);
+  KScope ks(ctx, EMB_K_HASH, st);
+  HashScratch hs;
+  hs.slot_of_pos = reinterpret_cast<int*>(w + L.slot_of_pos);
+  hs.pkeys = reinterpret_cast<unsigned long long*>(w + L.pkeys);
+  hs.paux = reinterpret_cast<int*>(w + L.paux);
+  hs.pval = reinterpret_cast<int*>(w + L.pval);
+  hs.blk = reinterpret_cast<uint32_t*>(w + L.blk);
+  hs.rank_base = reinterpret_cast<int*>(w + L.rank_base);
+  hipError_t e = launch_hash_translate(ctx->hv, ctx->dc, ctx->g.T, reinterpret_cast<const long long*>(ids), offsets,
+                                       itype, (int)N, B, insert != 0, hs, rows_out, st);
+  if (e != hipSuccess) return hip_fail(e, "hash translation");
+  return ok();
+}
+
+int emb_forward_pooled_hashed(emb_ctx* ctx, const int64_t* ids, const void* offsets, int32_t itype, int64_t N,
+                              int32_t B, int32_t pool, float* out, void* hip_stream) {
+  int rc = check_lookup_args(ctx, ids, offsets, itype, N, B);
+  if (rc) return rc;
+  if ((rc = check_pool(pool))) return rc;
+  if (B == 0) return ok();
+  if (!out || !aligned(out, 16)) return fail(EMB_E_INVAL, "out is NULL or not 16-byte aligned");
+  if ((rc = ensure_device(ctx))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  KScope ks(ctx, EMB_K_FORWARD, st);
+  hipError_t e = launch_forward(ctx->g, ctx->dc, ids, offsets, itype, N, B, pool, out, ctx->fwd_max_blocks, st,
+                                nullptr, 0, &ctx->hv);
+  if (e != hipSuccess) return hip_fail(e, "hashed forward");
+  return ok();
+}
+
+int emb_hash_rows_used(emb_ctx* ctx, int32_t* used, void* hip_stream) {
+  if (!ctx || !used) return fail(EMB_E_INVAL, "NULL argument");
+  if (!ctx->hash_ready) return fail(EMB_E_STATE, "no hash map memory attached");
+  hipError_t e = hipMemcpyAsync(used, ctx->hv.next_free, sizeof(int32_t) * ctx->g.T, hipMemcpyDeviceToDevice,
+                                static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(rows used)");
+  return ok();
+}
+
 int emb_set_shard_map(emb_ctx* ctx, const emb_shard_rule* rules, int32_t num_shards) {
   if (!ctx || !rules) return fail(EMB_E_INVAL, "NULL argument");
   if (num_shards < 1 || num_shards > EMB_MAX_SHARDS)
@@ -765,8 +925,10 @@ int emb_check_device_error(emb_ctx* ctx, void* hip_stream) {
                                              "break the CSR contract"
                                            : "a kernel saw an index outside [0, rows)");
     }
-    return fail(EMB_E_INVAL, "offsets break the CSR contract (offsets[0] = 0, non-decreasing, "
-                             "offsets[T*B] = N)");
+    if (flag & 2)
+      return fail(EMB_E_INVAL, "offsets break the CSR contract (offsets[0] = 0, non-decreasing, "
+                               "offsets[T*B] = N)");
+    return fail(EMB_E_INVAL, "id translation saw the reserved id INT64_MIN");
   }
   return ok();
 }

@@ -200,4 +200,35 @@ __device__ __forceinline__ int table_of(const uint32_t* s_ro, int T, uint32_t ke
   return lo;
 }
 
+// ---- hash maps of the hash-keyed lookup (k_hash.hip, k_forward.hip) ----
+constexpr long long kEmpty = (long long)0x8000000000000000ull;  // free slot; not a valid id
+
+// SplitMix64's output mixer (Steele, Lea & Flood, OOPSLA 2014).
+__device__ __forceinline__ uint64_t mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// Finds id in one table's map by linear probing from its mixed hash; with
+// `insert`, claims the first free slot on the way with a 64-bit CAS (equal
+// ids racing for one slot all end up on it). Returns the slot index, or -1
+// (absent without insert; no free slot with it).
+__device__ __forceinline__ long long find_slot(const HashMeta& m, unsigned long long* keys, long long id,
+                                               bool insert) {
+  uint32_t i = (uint32_t)mix64((uint64_t)id) & m.mask;
+  for (uint32_t step = 0; step <= m.mask; ++step) {
+    const long long slot = m.base + i;
+    const long long k = (long long)__hip_atomic_load(keys + slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (k == id) return slot;
+    if (k == kEmpty) {
+      if (!insert) return -1;
+      const unsigned long long old = atomicCAS(keys + slot, (unsigned long long)kEmpty, (unsigned long long)id);
+      if ((long long)old == kEmpty || (long long)old == id) return slot;
+    }
+    i = (i + 1) & m.mask;
+  }
+  return -1;
+}
+
 }  // namespace emb

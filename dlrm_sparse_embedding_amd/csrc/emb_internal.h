@@ -20,6 +20,33 @@ struct DevTable {
   float* m[EMB_MAX_SLICES];
 };
 
+// Hash map of one table (hash-keyed lookup): slots [base, base + mask + 1)
+// of the context's key / value / scratch arrays; rows = the table's rows.
+struct HashMeta {
+  long long base;
+  uint32_t mask;
+  int rows;
+};
+
+// Device view of the attached hash maps (caller memory).
+struct HashView {
+  const HashMeta* meta;       // [T] (context-owned device copy)
+  unsigned long long* keys;   // [slots] id, or the free marker
+  int* vals;                  // [slots] row of the id
+  int* next_free;             // [T] rows handed out so far
+  long long slots;
+};
+
+// Workspace of one translation of N lookups.
+struct HashScratch {
+  int* slot_of_pos;           // [N]
+  unsigned long long* pkeys;  // [2N] pending map (new ids of the step)
+  int* paux;                  // [2N]
+  int* pval;                  // [2N]
+  uint32_t* blk;              // [N / 2048 + 2]
+  int* rank_base;             // [T + 1]
+};
+
 // Update-kernel type code: the storage type, or'ed with kMasterBit when the
 // table is stepped from an fp32 master and the storage holds its RNE copy.
 constexpr int kMasterBit = 8;
@@ -107,7 +134,8 @@ hipError_t launch_init_slice(const Geom& g, const DevCtx& dc, int t, int s, int6
 // instead of the tables, with int32 indices into it (the unique-first forward).
 hipError_t launch_forward(const Geom& g, const DevCtx& dc, const void* indices, const void* offsets,
                           int itype, long long N, int B, int pool, float* out, int max_blocks,
-                          hipStream_t st, const void* flat = nullptr, long long flat_rows = 0);
+                          hipStream_t st, const void* flat = nullptr, long long flat_rows = 0,
+                          const HashView* hash = nullptr);
 // rows[u] = logical row of unique key u (storage type), u < min(*num_unique, cap)
 hipError_t launch_gather_unique(const Geom& g, const DevCtx& dc, const uint32_t* ukeys,
                                 const int32_t* num_unique, int cap, void* rows, hipStream_t st);
@@ -145,6 +173,13 @@ hipError_t launch_reduce(const Geom& g, const DevCtx& dc, int mode, int N, int B
 hipError_t launch_combine(const Geom& g, const DevCtx& dc, int mode, int N, const WsLayout& L,
                           const char* ws, const uint32_t* unique_keys, float* grad_out, float lr,
                           float eps, hipStream_t st, const int32_t* slot = nullptr);
+
+// hash-keyed lookup (k_hash.hip)
+hipError_t launch_hash_clear(const HashView& h, int T, hipStream_t st);
+// rows_out has the integer type `itype`
+hipError_t launch_hash_translate(const HashView& h, const DevCtx& dc, int T, const long long* ids,
+                                 const void* offsets, int itype, int N, int B, bool insert, const HashScratch& w,
+                                 void* rows_out, hipStream_t st);
 
 // shard routing (k_pack.hip); rules: device [T] {kind, shard}
 hipError_t launch_pack_dest(const Geom& g, const DevCtx& dc, const int2* rules, int S, int N,

@@ -44,15 +44,21 @@ struct FwdArgs {
   long long total_sg;
   int nblk;
   int mean;
-  const void* flat;    // FLAT: the compact rows, [flat_rows][D] of the storage type,
+  const void* flat;    // SRC 1: the compact rows, [flat_rows][D] of the storage type,
                        // indexed by int32 `indices` (offsets stay of type IDX)
   long long flat_rows;
+  const HashMeta* hmeta;        // SRC 2: `indices` are int64 ids looked up in
+  unsigned long long* hkeys;    // the tables' hash maps (an id without a row
+  const int* hvals;             // pools to nothing)
 };
 
 // 8 waves/SIMD with 4 rows in flight per subgroup measured faster than 5
 // waves/SIMD with 8 rows (293 -> 277 us on the 26x4Mx128 one-hot workload).
 // Positions are 32-bit (N < 2^31 is validated) to stay within 64 VGPRs.
-template <int DT, typename IDX, int LPR, bool FLAT>
+// SRC: 0 = rows of the tables by index, 1 = compact unique rows by inverse,
+// 2 = rows of the tables by hashed id (lookup only: the HugeCTR embedding
+// layer's hash table lookup fused with the pooling).
+template <int DT, typename IDX, int LPR, int SRC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_forward(FwdArgs a) {
   constexpr int CPL = 16 / Stor<DT>::kBytes;  // columns per lane
   constexpr int SGW = 256 / LPR;              // subgroups per block
@@ -82,7 +88,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
     long long rows_t;
     const char* wbase;
     size_t rstride;
-    if constexpr (FLAT) {
+    if constexpr (SRC == 1) {
       rows_t = a.flat_rows;
       wbase = reinterpret_cast<const char*>(a.flat) + (size_t)c0 * Stor<DT>::kBytes;
       rstride = (size_t)a.D * Stor<DT>::kBytes;
@@ -93,6 +99,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
       wbase = reinterpret_cast<const char*>(a.tables[t].w[s]) + (size_t)cs * Stor<DT>::kBytes;
       rstride = (size_t)a.Dsl * Stor<DT>::kBytes;
     }
+    HashMeta hm{};
+    if constexpr (SRC == 2) hm = a.hmeta[t];
     const size_t ostride = (size_t)a.T * a.D;
     float* obase = a.out + (size_t)b0 * ostride + (size_t)t * a.D + c0;
 
@@ -129,12 +137,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
       for (int k = 0; k < U; ++k) {
         v[k] = u4{0u, 0u, 0u, 0u};
         if (p + k < P1) {
-          // FLAT reads the dedup's int32 inverse; offsets keep the caller's type
-          const long long r = FLAT ? (long long)reinterpret_cast<const int32_t*>(a.indices)[p + k]
-                                   : ld_idx<IDX>(a.indices, p + k);
+          // SRC 1 reads the dedup's int32 inverse, SRC 2 int64 ids; offsets
+          // keep the caller's type
+          long long r;
+          if constexpr (SRC == 1) {
+            r = reinterpret_cast<const int32_t*>(a.indices)[p + k];
+          } else if constexpr (SRC == 2) {
+            const long long id = reinterpret_cast<const long long*>(a.indices)[p + k];
+            const long long slot = id == kEmpty ? -1 : find_slot(hm, a.hkeys, id, false);
+            r = slot >= 0 ? a.hvals[slot] : -1;
+          } else {
+            r = ld_idx<IDX>(a.indices, p + k);
+          }
           if (r >= 0 && r < rows_t) {
             if (act) v[k] = *reinterpret_cast<const u4*>(wbase + (size_t)r * rstride);
-          } else {
+          } else if constexpr (SRC != 2) {
             bad = 1;
           }
         }
@@ -166,11 +183,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
   }
 }
 
-#define FWD_LAUNCH(DT, IDX, LPR)                                                               \
-  if (args.flat)                                                                            \
-    hipLaunchKernelGGL((k_forward<DT, IDX, LPR, true>), dim3(grid), dim3(256), 0, st, args);  \
-  else                                                                                      \
-    hipLaunchKernelGGL((k_forward<DT, IDX, LPR, false>), dim3(grid), dim3(256), 0, st, args); \
+#define FWD_LAUNCH(DT, IDX, LPR)                                                          \
+  if (args.flat)                                                                       \
+    hipLaunchKernelGGL((k_forward<DT, IDX, LPR, 1>), dim3(grid), dim3(256), 0, st, args); \
+  else if (args.hmeta)                                                                 \
+    hipLaunchKernelGGL((k_forward<DT, IDX, LPR, 2>), dim3(grid), dim3(256), 0, st, args); \
+  else                                                                                 \
+    hipLaunchKernelGGL((k_forward<DT, IDX, LPR, 0>), dim3(grid), dim3(256), 0, st, args); \
   break;
 
 #define FWD_LPR_SWITCH(DT, IDX)                \
@@ -192,7 +211,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
 
 hipError_t launch_forward(const Geom& g, const DevCtx& dc, const void* indices, const void* offsets,
                           int itype, long long N, int B, int pool, float* out, int max_blocks,
-                          hipStream_t st, const void* flat, long long flat_rows) {
+                          hipStream_t st, const void* flat, long long flat_rows, const HashView* hash) {
   if (B == 0 || g.T == 0) return hipSuccess;
   const int cpl = 16 / (g.dtype == EMB_F32 ? 4 : 2);
   int lpr = next_pow2((g.D + cpl - 1) / cpl);
@@ -223,6 +242,9 @@ hipError_t launch_forward(const Geom& g, const DevCtx& dc, const void* indices, 
   args.mean = pool == EMB_POOL_MEAN;
   args.flat = flat;
   args.flat_rows = flat_rows;
+  args.hmeta = hash ? hash->meta : nullptr;
+  args.hkeys = hash ? hash->keys : nullptr;
+  args.hvals = hash ? hash->vals : nullptr;
   const int grid = max_blocks > 0 && max_blocks < args.nblk ? max_blocks : args.nblk;
   switch (g.dtype) {
     case EMB_F32:

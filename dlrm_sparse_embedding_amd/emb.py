@@ -38,7 +38,7 @@ EMB_OPT_SGD, EMB_OPT_ADAGRAD = 0, 1
 EMB_MAX_SLICES = 4
 
 KERNELS = ["init", "forward", "keys", "sort_hist", "sort_scan", "sort_scatter", "rle", "reduce",
-           "combine", "apply", "atomic", "pack", "gather"]
+           "combine", "apply", "atomic", "pack", "gather", "hash"]
 
 DTYPE_CODE = {"f32": EMB_F32, "bf16": EMB_BF16, "f16": EMB_F16}
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
@@ -107,6 +107,18 @@ def lib() -> ctypes.CDLL:
     L.emb_sparse_update.restype = ctypes.c_int
     L.emb_forward_pooled_unique.argtypes = [vp, vp, vp, i32, i64, i32, i32, vp, vp, sz, vp, vp]
     L.emb_forward_pooled_unique.restype = ctypes.c_int
+    L.emb_hash_bytes.argtypes = [vp]
+    L.emb_hash_bytes.restype = sz
+    L.emb_hash_attach.argtypes = [vp, vp, sz, vp]
+    L.emb_hash_attach.restype = ctypes.c_int
+    L.emb_hash_workspace_bytes.argtypes = [vp, i64]
+    L.emb_hash_workspace_bytes.restype = sz
+    L.emb_hash_translate.argtypes = [vp, vp, vp, i32, i64, i32, i32, vp, sz, vp, vp]
+    L.emb_hash_translate.restype = ctypes.c_int
+    L.emb_forward_pooled_hashed.argtypes = [vp, vp, vp, i32, i64, i32, i32, vp, vp]
+    L.emb_forward_pooled_hashed.restype = ctypes.c_int
+    L.emb_hash_rows_used.argtypes = [vp, vp, vp]
+    L.emb_hash_rows_used.restype = ctypes.c_int
     L.emb_set_shard_map.argtypes = [vp, ctypes.POINTER(emb_shard_rule), i32]
     L.emb_set_shard_map.restype = ctypes.c_int
     L.emb_pack_by_shard.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
@@ -240,6 +252,40 @@ def emb_forward_pooled_unique(ctx: int, indices, offsets, B: int, pool: str, ws,
         ctx, _ptr(indices), _ptr(offsets), _itype(indices), int(indices.numel()), int(B), POOL_CODE[pool],
         _ptr(ws), _ptr(rows_buf), int(rows_buf.numel() * rows_buf.element_size()) if rows_buf is not None else 0,
         _ptr(out), _stream(stream)))
+
+
+def emb_hash_bytes(ctx: int) -> int:
+    return int(lib().emb_hash_bytes(ctx))
+
+
+def emb_hash_attach(ctx: int, mem, stream=None) -> None:
+    _check(lib().emb_hash_attach(ctx, _ptr(mem), int(mem.numel() * mem.element_size()), _stream(stream)))
+
+
+def emb_hash_workspace_bytes(ctx: int, N: int) -> int:
+    return int(lib().emb_hash_workspace_bytes(ctx, int(N)))
+
+
+def emb_hash_translate(ctx: int, ids, offsets, B: int, insert: bool, ws, rows_out, stream=None) -> None:
+    """ids: int64 [N]; rows_out: [N] of the offsets' integer type."""
+    if ids.dtype != torch.int64:
+        raise ValueError("ids must be int64")
+    if rows_out.dtype != offsets.dtype:
+        raise ValueError("rows_out must have the offsets' integer type")
+    _check(lib().emb_hash_translate(ctx, _ptr(ids), _ptr(offsets), _itype(offsets), int(ids.numel()), int(B),
+                                    1 if insert else 0, _ptr(ws), int(ws.numel() * ws.element_size()),
+                                    _ptr(rows_out), _stream(stream)))
+
+
+def emb_forward_pooled_hashed(ctx: int, ids, offsets, B: int, pool: str, out, stream=None) -> None:
+    if ids.dtype != torch.int64:
+        raise ValueError("ids must be int64")
+    _check(lib().emb_forward_pooled_hashed(ctx, _ptr(ids), _ptr(offsets), _itype(offsets), int(ids.numel()),
+                                           int(B), POOL_CODE[pool], _ptr(out), _stream(stream)))
+
+
+def emb_hash_rows_used(ctx: int, used, stream=None) -> None:
+    _check(lib().emb_hash_rows_used(ctx, _ptr(used), _stream(stream)))
 
 
 def emb_set_shard_map(ctx: int, rules, num_shards: int) -> None:
@@ -388,6 +434,29 @@ class EmbeddingTables:
             out = torch.empty((B, self.T * self.dim), dtype=torch.float32, device=indices.device)
         emb_forward_pooled_unique(self.ctx, indices, offsets, B, pool, bufs["ws"], rows_buf, out, stream)
         return out
+
+    def hash_attach(self, device="cuda", stream=None) -> None:
+        """Allocates the id -> row maps of every table and empties them."""
+        self.hash_mem = torch.empty(emb_hash_bytes(self.ctx), dtype=torch.uint8, device=device)
+        emb_hash_attach(self.ctx, self.hash_mem, stream)
+
+    def hash_translate(self, ids, offsets, B: int, insert: bool, stream=None):
+        rows = torch.empty(max(ids.numel(), 1), dtype=offsets.dtype, device=ids.device)[:ids.numel()]
+        ws = torch.empty(max(emb_hash_workspace_bytes(self.ctx, ids.numel()), 256), dtype=torch.uint8,
+                         device=ids.device)
+        emb_hash_translate(self.ctx, ids, offsets, B, insert, ws, rows, stream)
+        return rows
+
+    def forward_hashed(self, ids, offsets, B: int, pool: str, out=None, stream=None):
+        if out is None:
+            out = torch.empty((B, self.T * self.dim), dtype=torch.float32, device=ids.device)
+        emb_forward_pooled_hashed(self.ctx, ids, offsets, B, pool, out, stream)
+        return out
+
+    def hash_rows_used(self, stream=None):
+        used = torch.empty(self.T, dtype=torch.int32, device=self.weights[0][0].device)
+        emb_hash_rows_used(self.ctx, used, stream)
+        return used
 
     def set_shard_map(self, rules, num_shards: int) -> None:
         emb_set_shard_map(self.ctx, rules, num_shards)

@@ -278,6 +278,55 @@ int emb_pack_by_shard(emb_ctx* ctx, void* ws, const float* dY, uint32_t* send_ke
                       int32_t* send_offsets, int32_t* slot_of_unique, float* send_grad,
                       void* hip_stream);
 
+/* ---- hash-keyed lookup (feature ids -> rows) ----------------------------- */
+/* "Merlin HugeCTR" GTC 2022 deck, slide "HUGECTR EMBEDDING LAYER": a GPU
+ * hash table lookup fused with the pooling; the dynamic embedding of the
+ * Sparse Operation Kit 2.0 article. Lookups carry arbitrary int64 ids (every
+ * value but INT64_MIN, which marks a free slot); each table keeps a device
+ * hash map from id to one of its rows. With insertion, an id a table has not
+ * seen gets the table's next free row, ids taken in order of first appearance
+ * in the CSR (so the id -> row mapping is deterministic); once a table's rows
+ * are used up, new ids get no row (rows are never freed). The maps live in
+ * caller memory: one region of emb_hash_bytes bytes, 2^k slots per table (at
+ * least twice its rows, 12 bytes per slot) plus a counter per table; only ids
+ * holding a row are stored. */
+
+/* Bytes of map memory for this context's tables (0 if the slots would not
+ * fit int32 indices or a table has 2^31 - 1 rows or more). */
+size_t emb_hash_bytes(const emb_ctx* ctx);
+
+/* Attaches the map memory (device, 256-byte aligned, >= emb_hash_bytes) and
+ * empties every map on hip_stream. Uploads the per-table map layout (16 bytes
+ * per table) to a device array the context owns, with a synchronous copy. */
+int emb_hash_attach(emb_ctx* ctx, void* mem, size_t bytes, void* hip_stream);
+
+/* Scratch bytes emb_hash_translate needs for N lookups. */
+size_t emb_hash_workspace_bytes(const emb_ctx* ctx, int64_t N);
+
+/* ids[N] (int64) -> rows_out[N] (row within the table of each lookup's bag,
+ * -1 for an id without a row), rows_out of the integer type of offsets
+ * (itype), so that rows_out and offsets feed emb_forward_pooled and the
+ * backward directly (a -1 row counts as an out-of-range index there).
+ * insert != 0 hands out rows to new ids as described above; insert == 0 only
+ * looks up. offsets as for emb_forward_pooled; ws holds the step's pending
+ * map of new ids (emb_hash_workspace_bytes: about 36 bytes per lookup).
+ * Raises bit 4 of the device flag (EMB_E_INVAL from emb_check_device_error)
+ * for an id equal to INT64_MIN. EMB_E_STATE if no map memory is attached. */
+int emb_hash_translate(emb_ctx* ctx, const int64_t* ids, const void* offsets, int32_t itype,
+                       int64_t N, int32_t B, int32_t insert, void* ws, size_t ws_bytes,
+                       void* rows_out, void* hip_stream);
+
+/* Fused hash lookup + pooled forward (lookup only, no insertion): as
+ * emb_forward_pooled with each lookup's row found in its table's map; an id
+ * without a row contributes nothing (no error). EMB_E_STATE if no map memory
+ * is attached. */
+int emb_forward_pooled_hashed(emb_ctx* ctx, const int64_t* ids, const void* offsets, int32_t itype,
+                              int64_t N, int32_t B, int32_t pool, float* out, void* hip_stream);
+
+/* Copies the number of rows handed out per table (int32[T], device) into
+ * used, on hip_stream. */
+int emb_hash_rows_used(emb_ctx* ctx, int32_t* used, void* hip_stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* emb_last_error(void);
 
@@ -285,7 +334,8 @@ const char* emb_last_error(void);
  * this context flagged since the last check: EMB_E_BOUNDS if one saw an
  * index outside [0, rows_t); else EMB_E_INVAL if the backward's key build
  * saw offsets that break the CSR contract above (offsets[0] != 0, a
- * decreasing step, or offsets[T*B] != N); else EMB_OK. Malformed offsets
+ * decreasing step, or offsets[T*B] != N), or the id translation saw the
+ * reserved id INT64_MIN; else EMB_OK. Malformed offsets
  * never make a kernel access memory outside the caller's buffers: every
  * kernel clamps offsets into [0, N], and the key build still gives every
  * position in [0, N) an in-range key or the never-applied sentinel, but the
@@ -307,7 +357,8 @@ int emb_check_device_error(emb_ctx* ctx, void* hip_stream);
 #define EMB_K_ATOMIC       10   /* atomic reduction (evidence variant) */
 #define EMB_K_PACK         11   /* shard routing: destinations, placement, offsets */
 #define EMB_K_GATHER       12   /* unique rows into the compact buffer */
-#define EMB_K_COUNT        13
+#define EMB_K_HASH         13   /* id -> row translation (and map reset) */
+#define EMB_K_COUNT        14
 
 /* enable != 0: from now on every kernel launch of this context is
  * bracketed by HIP events recorded on the launch stream. */

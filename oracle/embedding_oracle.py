@@ -54,8 +54,8 @@ What is computed, and where the pages define it
   as: an id a table has not seen gets, when insertion is on, the table's
   next free row, ids taken in order of first appearance in the CSR; once a
   table's rows are used up, new ids get no row (their lookups pool to
-  nothing) and stay known as row-less; with insertion off, unseen ids get no
-  row.
+  nothing; rows are never freed, so such an id never gets one); with
+  insertion off, unseen ids get no row.
 * Untouched rows -- a dense step with g = 0 and G = 0 leaves w and G bit for
   bit unchanged, so only touched rows are computed.
 * Table contents -- synthetic: each element is a counter hash of (seed, table,
@@ -389,8 +389,7 @@ def pack_by_shard(unique_keys: np.ndarray, row_offset: np.ndarray, rules, S: int
 # ---------------------------------------------------------------------------
 
 class HashTables:
-    """Per-table id -> row maps (plain dicts). rows[t] is table t's capacity.
-    A row of -1 marks an id that arrived when its table was full."""
+    """Per-table id -> row maps (plain dicts). rows[t] is table t's capacity."""
 
     def __init__(self, rows):
         self.rows = [int(r) for r in rows]
@@ -408,11 +407,8 @@ class HashTables:
                 x = int(ids[p])
                 if x in m:
                     out[p] = m[x]
-                elif insert:
-                    if self.next_free[t] < self.rows[t]:
-                        m[x] = self.next_free[t]
-                        self.next_free[t] += 1
-                    else:
-                        m[x] = -1
+                elif insert and self.next_free[t] < self.rows[t]:
+                    m[x] = self.next_free[t]
+                    self.next_free[t] += 1
                     out[p] = m[x]
         return out

@@ -1,0 +1,145 @@
+"""GPU parity of the hash-keyed lookup (emb_hash_translate and
+emb_forward_pooled_hashed) against the oracle's HashTables: the rows handed
+out to 64-bit ids are compared bit for bit over several steps (insertion and
+lookup-only, tables filling up), and the fused hashed forward against the
+plain forward on the translated rows."""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from dlrm_sparse_embedding_amd import emb as E
+from dlrm_sparse_embedding_amd import workloads as W
+
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _free_gpu():
+    yield
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _ids_batch(rng, rows, B, hot, universe, index_dtype, fit=False):
+    """Bags of `hot` lookups whose ids are scattered 64-bit values drawn with
+    Zipf-like repeats from a universe of `universe` distinct ids per table
+    (at most the table's rows with fit=True, so every id gets a row)."""
+    T = len(rows)
+    lens = [rng.integers(0, 2 * hot + 1, B) for _ in range(T)]
+    ids = []
+    for t in range(T):
+        u = min(universe, rows[t]) if fit else universe
+        ranks = np.minimum(rng.zipf(1.2, int(lens[t].sum())), u) - 1
+        # a fixed scramble of (table, rank) into the whole int64 range
+        x = (ranks.astype(np.uint64) * np.uint64(0x9E3779B97F4A7C15)) ^ np.uint64((t * 0x632BE59BD9B4E019 + 7) % 2**64)
+        ids.append(x.view(np.int64))
+    batch = W.make_batch_from_lengths(lens, [np.zeros(int(l.sum()), np.int64) for l in lens], B,
+                                      index_dtype=index_dtype)
+    return batch, np.concatenate(ids)
+
+
+@pytest.mark.parametrize("index_dtype", [np.int32, np.int64])
+def test_translate_matches_oracle_over_steps(index_dtype):
+    rng = np.random.default_rng(8)
+    rows = [50, 1000, 7, 20000]          # tables 0 and 2 fill up
+    cfg = P.custom_cfg(rows, dim=16, B=512)
+    P.say("hash translate", index_dtype.__name__)
+    tabs = P.make_tables(cfg)
+    tabs.hash_attach()
+    ht = O.HashTables(rows)
+    for step, insert in enumerate([True, True, False, True]):
+        batch, ids = _ids_batch(rng, rows, cfg.batch, 3, 5000, index_dtype)
+        d_ids = torch.from_numpy(ids).cuda()
+        d_off = torch.from_numpy(batch.offsets).cuda()
+        got = tabs.hash_translate(d_ids, d_off, cfg.batch, insert).cpu().numpy().astype(np.int64)
+        ref = ht.translate(ids, batch.offsets, cfg.T, cfg.batch, insert)
+        assert np.array_equal(got, ref), (step, int((got != ref).sum()))
+        assert tabs.hash_rows_used().cpu().tolist() == ht.next_free
+    tabs.check_device_error()
+    tabs.close()
+
+
+def test_translate_large_then_train_step():
+    # a 26-table step at batch 8192: translate with insertion, then the
+    # training step on the translated rows, checked against the oracle
+    rng = np.random.default_rng(3)
+    cfg = W.make_config(2, batch=8192)
+    rows = [t.rows for t in cfg.tables]
+    P.say("hash translate + step cfg2")
+    tabs = P.make_tables(cfg)
+    tabs.hash_attach()
+    ht = O.HashTables(rows)
+    batch, ids = _ids_batch(rng, rows, cfg.batch, 1, 200000, np.int32, fit=True)
+    got = tabs.hash_translate(torch.from_numpy(ids).cuda(), torch.from_numpy(batch.offsets).cuda(),
+                              cfg.batch, True).cpu().numpy()
+    ref = ht.translate(ids, batch.offsets, cfg.T, cfg.batch, True)
+    assert np.array_equal(got.astype(np.int64), ref)
+    assert (ref >= 0).all()
+    # the oracle's rows are the batch of an ordinary step (table starts at 0)
+    step_batch = W.Batch(ref.astype(np.int32), batch.offsets, batch.lengths, cfg.T, cfg.batch)
+    dY = W.make_dy(cfg, k=0)
+    P.run_step(cfg, step_batch, dY, tabs=tabs, sample_untouched=0)
+    tabs.close()
+
+
+@pytest.mark.parametrize("pool", ["sum", "mean"])
+def test_fused_hashed_forward_equals_forward_on_rows(pool):
+    rng = np.random.default_rng(5)
+    rows = [300, 40, 5000]
+    cfg = P.custom_cfg(rows, dim=64, dtype="bf16", B=700, pool=pool)
+    P.say("hashed forward", pool)
+    tabs = P.make_tables(cfg)
+    tabs.hash_attach()
+    batch, ids = _ids_batch(rng, rows, cfg.batch, 4, 800, np.int64)
+    d_ids = torch.from_numpy(ids).cuda()
+    d_off = torch.from_numpy(batch.offsets).cuda()
+    tabs.hash_translate(d_ids, d_off, cfg.batch, True)        # table 1 fills up: some ids get no row
+    # new ids the maps have never seen, mixed in: they pool to nothing
+    ids2 = ids.copy()
+    ids2[::7] = rng.integers(-2**62, 2**62, len(ids2[::7]))
+    d_ids2 = torch.from_numpy(ids2).cuda()
+    rows2 = tabs.hash_translate(d_ids2, d_off, cfg.batch, False)
+    Yh = tabs.forward_hashed(d_ids2, d_off, cfg.batch, pool)
+    Yr = tabs.forward(rows2, d_off, cfg.batch, pool)
+    torch.cuda.synchronize()
+    a, b = Yh.cpu().numpy(), Yr.cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    with pytest.raises(E.EmbError):
+        tabs.check_device_error()            # the plain forward saw rows of -1
+    # the oracle's own rows agree, and (sum pooling) so do the pooled values,
+    # row-less lookups dropped; mean divides by the whole bag and is covered
+    # by the bit equality with the plain forward above
+    ht = O.HashTables(rows)
+    ht.translate(ids, batch.offsets, cfg.T, cfg.batch, True)
+    ref_rows = ht.translate(ids2, batch.offsets, cfg.T, cfg.batch, False)
+    assert np.array_equal(rows2.cpu().numpy().astype(np.int64), ref_rows)
+    if pool == "sum":
+        keep = ref_rows >= 0
+        bag = np.repeat(np.arange(cfg.T * cfg.batch), np.diff(batch.offsets))
+        sub_lens = np.bincount(bag[keep], minlength=cfg.T * cfg.batch).reshape(cfg.T, cfg.batch)
+        kept = ref_rows[keep]
+        cut = np.concatenate([[0], np.cumsum(sub_lens.sum(axis=1))])
+        sub = W.make_batch_from_lengths(list(sub_lens), [kept[cut[t]:cut[t + 1]] for t in range(cfg.T)], cfg.batch)
+        P.check_forward(a, cfg, sub, P.oracle_tables(cfg, sub))
+    tabs.close()
+
+
+def test_reserved_id_flagged():
+    cfg = P.custom_cfg([10], dim=16, B=4)
+    P.say("hash reserved id")
+    tabs = P.make_tables(cfg)
+    tabs.hash_attach()
+    ids = torch.tensor([5, -2**63, 5, 6], dtype=torch.int64, device="cuda")
+    off = torch.tensor([0, 1, 2, 3, 4], dtype=torch.int32, device="cuda")
+    rows = tabs.hash_translate(ids, off, 4, True).cpu().tolist()
+    assert rows == [0, -1, 0, 1]
+    with pytest.raises(E.EmbError) as ei:
+        tabs.check_device_error()
+    assert ei.value.code == E.EMB_E_INVAL
+    tabs.close()

@@ -698,7 +698,8 @@ def _translate_numpy(ids, offsets, T, B, rows, insert, state):
             order = np.argsort(pos)
             for rank, x in enumerate(new_ids[order].tolist()):
                 r = nf[t] + rank
-                maps[t][x] = r if r < rows[t] else -1
+                if r < rows[t]:
+                    maps[t][x] = r
             nf[t] = min(rows[t], nf[t] + len(new_ids))
         out[a:b] = [maps[t].get(x, -1) for x in seg.tolist()]
     return out
@@ -750,9 +751,9 @@ def test_hash_pin_catches_mistakes():
                 a, b = int(offsets[t * B]), int(offsets[(t + 1) * B])
                 for p in range(b - 1, a - 1, -1):
                     x = int(ids[p])
-                    if x not in self.maps[t] and insert:
-                        self.maps[t][x] = self.next_free[t] if self.next_free[t] < self.rows[t] else -1
-                        self.next_free[t] = min(self.rows[t], self.next_free[t] + 1)
+                    if x not in self.maps[t] and insert and self.next_free[t] < self.rows[t]:
+                        self.maps[t][x] = self.next_free[t]
+                        self.next_free[t] += 1
                 for p in range(a, b):
                     out[p] = self.maps[t].get(int(ids[p]), -1)
             return out
@@ -764,8 +765,8 @@ def test_hash_pin_catches_mistakes():
             for t in range(T):
                 for p in range(int(offsets[t * B]), int(offsets[(t + 1) * B])):
                     x = int(ids[p])
-                    if x not in self.maps[t] and insert:
-                        self.maps[t][x] = nxt if nxt < self.rows[t] else -1
+                    if x not in self.maps[t] and insert and nxt < self.rows[t]:
+                        self.maps[t][x] = nxt
                         nxt += 1
                     out[p] = self.maps[t].get(x, -1)
             return out
