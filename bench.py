@@ -64,6 +64,9 @@ def parse():
     ap.add_argument("--unique-forward", action="store_true",
                     help="unique-first forward: dedup first, gather each unique row once, pool from the "
                          "compact rows (emb_forward_pooled_unique); implies the serial schedule")
+    ap.add_argument("--hashed", action="store_true",
+                    help="lookups carry 64-bit ids: every step first translates them to rows through the "
+                         "tables' hash maps (emb_hash_translate with insertion), then runs the step on the rows")
     ap.add_argument("--rows", type=int, default=0,
                     help="cap the rows of every table (0 = the workload's own sizes)")
     ap.add_argument("--ceiling", action="store_true",
@@ -164,6 +167,25 @@ def main() -> int:
     dev = []
     for b in host_batches:
         dev.append((torch.from_numpy(b.indices).cuda(), torch.from_numpy(b.offsets).cuda(), b.N))
+    if args.hashed:
+        # ids: a fixed scramble of (table, row) over the whole int64 range; the
+        # maps hand rows out by first appearance, so rows differ from the ids'
+        # source rows but the step's work is the same
+        ids_dev, rows_dev = [], []
+        for b in host_batches:
+            t_of = np.repeat(np.arange(T), np.diff(b.offsets[::B].astype(np.int64)))
+            x = (b.indices.astype(np.uint64) * np.uint64(0x9E3779B97F4A7C15)) ^ (
+                t_of.astype(np.uint64) * np.uint64(0xD1B54A32D192ED03))
+            ids_dev.append(torch.from_numpy(x.view(np.int64)).cuda())
+        tabs.hash_attach()
+        hws = torch.empty(E.emb_hash_workspace_bytes(tabs.ctx, max(b.N for b in host_batches)),
+                          dtype=torch.uint8, device="cuda")
+        for k, b in enumerate(host_batches):
+            rows_dev.append(torch.empty(b.N, dtype=dev[k][1].dtype, device="cuda"))
+            E.emb_hash_translate(tabs.ctx, ids_dev[k], dev[k][1], B, True, hws, rows_dev[k])
+        dev = [(rows_dev[k], dev[k][1], dev[k][2]) for k in range(len(dev))]
+        torch.cuda.synchronize()
+        tabs.check_device_error()
     dY_host = W.make_dy(cfg)
     dy = torch.from_numpy(dY_host).cuda()
     Y = torch.empty((B, T * D), dtype=torch.float32, device="cuda")
@@ -189,6 +211,7 @@ def main() -> int:
     side = torch.cuda.Stream()          # default priority
     ev_free = torch.cuda.Event()        # ws / dedup outputs free again (previous update done)
     ev_dd = torch.cuda.Event()          # dedup done
+    ev_tr = torch.cuda.Event()          # id translation done (hashed ids)
     ev_free.record(main)
 
     def step(i, sched, evs=None):
@@ -197,11 +220,16 @@ def main() -> int:
         idx, off, n = dev[i % len(dev)]
         if evs:
             evs[0].record(main)
+        if args.hashed:
+            E.emb_hash_translate(tabs.ctx, ids_dev[i % len(dev)], off, B, True, hws, idx)
+            ev_tr.record(main)
         if args.unique_forward:
             tabs.dedup(idx, off, B, cfg.pool, bufs)
             tabs.forward_unique(idx, off, B, cfg.pool, bufs, rows_buf, out=Y)
         elif sched == "overlap":
             side.wait_event(ev_free)
+            if args.hashed:
+                side.wait_event(ev_tr)
             with torch.cuda.stream(side):
                 tabs.dedup(idx, off, B, cfg.pool, bufs)
             ev_dd.record(side)
@@ -279,6 +307,22 @@ def main() -> int:
         fwd_bytes += dd
         bwd_bytes -= dd
 
+    # hashed ids: the fused lookup-only forward (hash probe + gather + pooling
+    # in one kernel) against the plain forward on translated rows
+    hashed_fwd = None
+    if args.hashed:
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        e0.record(main)
+        for i in range(K):
+            tabs.forward_hashed(ids_dev[i % len(dev)], dev[i % len(dev)][1], B, cfg.pool, out=Y)
+        e1.record(main)
+        for i in range(K):
+            tabs.forward(dev[i % len(dev)][0], dev[i % len(dev)][1], B, cfg.pool, out=Y)
+        e2.record(main)
+        torch.cuda.synchronize()
+        hashed_fwd = {"fused_hashed_forward_ms": round(e0.elapsed_time(e1) / K, 4),
+                      "forward_on_rows_ms": round(e1.elapsed_time(e2) / K, 4)}
+
     # per-kernel times (HIP events around each launch, on the launch stream)
     E.emb_set_kernel_timing(tabs.ctx, True)
     for i in range(K):
@@ -353,7 +397,8 @@ def main() -> int:
             "unique_per_step": int(round(Uavg)),
             "batches_cycled": len(dev),
         },
-        "phases": ("fwd = dedup, then the unique-first forward (unique rows gathered once); bwd_update = "
+        "phases": ("fwd includes the id -> row translation; " if args.hashed else "") + (
+                   "fwd = dedup, then the unique-first forward (unique rows gathered once); bwd_update = "
                    if args.unique_forward else
                    "fwd = forward with the dedup on a second stream alongside it; bwd_update = " if args.schedule == "overlap"
                    else "fwd = forward; bwd_update = dedup + ") + (
@@ -370,6 +415,8 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if hashed_fwd:
+        out["hashed"] = hashed_fwd
     print(json.dumps(out), flush=True)
     tabs.close()
     return 0

@@ -58,8 +58,10 @@ struct FwdArgs {
 // SRC: 0 = rows of the tables by index, 1 = compact unique rows by inverse,
 // 2 = rows of the tables by hashed id (lookup only: the HugeCTR embedding
 // layer's hash table lookup fused with the pooling).
+// The hashed source keeps the probes of 4 lookups in flight too and needs
+// more registers: it runs at 6 waves/SIMD instead of 8.
 template <int DT, typename IDX, int LPR, int SRC>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_forward(FwdArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SRC == 2 ? 6 : 8, SRC == 2 ? 6 : 8))) void k_forward(FwdArgs a) {
   constexpr int CPL = 16 / Stor<DT>::kBytes;  // columns per lane
   constexpr int SGW = 256 / LPR;              // subgroups per block
   constexpr int U = 4;                        // rows in flight per subgroup
@@ -132,6 +134,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
     };
 
     for (int p = P0; p < P1; p += U) {
+      // SRC 2: the U lookups' map probes are issued together -- ids, then the
+      // home slots' keys, then the rows of the hits -- and only an id not in
+      // its home slot walks the probe sequence
+      long long hr[U];
+      if constexpr (SRC == 2) {
+        long long id[U];
+        unsigned long long k0[U];
+        long long s0[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k)
+          id[k] = p + k < P1 ? reinterpret_cast<const long long*>(a.indices)[p + k] : kEmpty;
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+          s0[k] = hm.base + (uint32_t)(mix64((uint64_t)id[k]) & hm.mask);
+          k0[k] = id[k] != kEmpty ? a.hkeys[s0[k]] : (unsigned long long)kEmpty;
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+          hr[k] = -1;
+          if ((long long)k0[k] == id[k] && id[k] != kEmpty) {
+            hr[k] = a.hvals[s0[k]];
+          } else if ((long long)k0[k] != kEmpty) {
+            const long long slot = find_slot(hm, a.hkeys, id[k], false);
+            if (slot >= 0) hr[k] = a.hvals[slot];
+          }
+        }
+      }
       u4 v[U];
 #pragma unroll
       for (int k = 0; k < U; ++k) {
@@ -143,9 +172,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
           if constexpr (SRC == 1) {
             r = reinterpret_cast<const int32_t*>(a.indices)[p + k];
           } else if constexpr (SRC == 2) {
-            const long long id = reinterpret_cast<const long long*>(a.indices)[p + k];
-            const long long slot = id == kEmpty ? -1 : find_slot(hm, a.hkeys, id, false);
-            r = slot >= 0 ? a.hvals[slot] : -1;
+            r = hr[k];
           } else {
             r = ld_idx<IDX>(a.indices, p + k);
           }
