@@ -2,9 +2,13 @@
 """Benchmark of the pooled-embedding training step on one MI355X.
 
 A step is one pass of the whole path over one batch: pooled forward
-(emb_forward_pooled), key dedup + segmented reduction (emb_backward_unique_reduce)
-and the fused sparse Adagrad/SGD update (emb_sparse_update). Inputs (tables,
-indices, offsets, upstream gradient) are resident in HBM before timing starts.
+(emb_forward_pooled), key dedup + segmented reduction (emb_backward_dedup /
+emb_backward_unique_reduce) and the fused sparse Adagrad/SGD update
+(emb_sparse_update). Inputs (tables, indices, offsets, upstream gradient) are
+resident in HBM before timing starts. By default the steps are software-
+pipelined: the next batch's dedup (which needs only its indices) runs on a
+second stream, into a second workspace, while the current step's forward and
+update run; K timed steps do exactly K dedups, forwards and updates.
 
 Default workload: 26 fp32 tables x 4,000,000 rows x 128 (53 GB of weights +
 53 GB of Adagrad state), batch 65536, one lookup per bag, Zipf(1.05) keys, sum
@@ -48,9 +52,11 @@ def parse():
                     help="the oracle runs on successive cycled batches until this much CPU time is spent")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--uniform-keys", action="store_true", help="control run: uniform keys instead of Zipf")
-    ap.add_argument("--schedule", choices=["overlap", "serial"], default="overlap",
+    ap.add_argument("--schedule", choices=["overlap", "serial", "pipeline"], default="pipeline",
                     help="overlap: the key dedup (emb_backward_dedup) runs on a second stream "
-                         "concurrently with the forward; serial: one stream, dedup inside the backward")
+                         "concurrently with the forward; serial: one stream, dedup inside the backward; "
+                         "pipeline: the dedup of the next batch runs on a second stream (with its own "
+                         "workspace) alongside the current step's forward and update")
     ap.add_argument("--reduce", choices=["fused", "atomic"], default="fused",
                     help="fused: sorted-segment reduction fused with the optimizer (the path); atomic: the "
                          "evidence variant, fp32 atomics into a materialised gradient, then the update")
@@ -147,6 +153,12 @@ def main() -> int:
     from dlrm_sparse_embedding_amd import emb as E
     from dlrm_sparse_embedding_amd import workloads as W
 
+    if args.schedule == "pipeline" and (args.pack or args.reduce != "fused" or args.hashed or args.unique_forward):
+        # the variants run with the schedule given explicitly, else serial
+        if "--schedule" in sys.argv:
+            print("bench.py: --schedule pipeline runs the plain training step only", file=sys.stderr)
+            return 2
+        args.schedule = "serial"
     cfg = W.make_config(args.config, rows=args.rows or None)
     if args.master and cfg.dtype == "f32":
         print("bench.py: --master needs a bf16/fp16 workload (configs 4, 5)", file=sys.stderr)
@@ -207,6 +219,11 @@ def main() -> int:
         torch.cuda.synchronize()
         U_of.append(int(bufs["num_unique"].item()))
 
+    # the pipeline schedule alternates two workspaces / dedup outputs
+    bufs2 = [bufs, tabs.backward_buffers(nmax, B, with_grad=args.reduce == "atomic")]
+    ev_free2 = [torch.cuda.Event(), torch.cuda.Event()]   # buffer set j free (its update done)
+    ev_dd2 = [torch.cuda.Event(), torch.cuda.Event()]     # dedup into buffer set j done
+
     main = torch.cuda.current_stream()
     side = torch.cuda.Stream()          # default priority
     ev_free = torch.cuda.Event()        # ws / dedup outputs free again (previous update done)
@@ -214,12 +231,38 @@ def main() -> int:
     ev_tr = torch.cuda.Event()          # id translation done (hashed ids)
     ev_free.record(main)
 
-    def step(i, sched, evs=None):
+    def issue_dedup(i):
+        """Pipeline schedule: the dedup of batch i on the side stream into
+        buffer set i % 2, once that set's previous update is done."""
+        j = i % 2
+        idx, off, _ = dev[i % len(dev)]
+        side.wait_event(ev_free2[j])
+        with torch.cuda.stream(side):
+            tabs.dedup(idx, off, B, cfg.pool, bufs2[j])
+        ev_dd2[j].record(side)
+
+    def step(i, sched, evs=None, last=False):
         """One training step; evs = three timing events (start, after forward
-        [+ dedup], end) recorded on the main stream."""
+        [+ dedup], end) recorded on the main stream. Under the pipeline
+        schedule the step's dedup was issued ahead (by the previous step or the
+        prologue) and this step issues the next batch's unless it is the last."""
         idx, off, n = dev[i % len(dev)]
         if evs:
             evs[0].record(main)
+        if sched == "pipeline":
+            j = i % 2
+            tabs.forward(idx, off, B, cfg.pool, out=Y)
+            if evs:
+                evs[1].record(main)
+            main.wait_event(ev_dd2[j])
+            tabs.backward(idx, off, B, cfg.pool, dy, bufs2[j])   # skips the dedup done ahead
+            tabs.update(cfg.opt, cfg.lr, cfg.eps, bufs2[j], dY=dy)
+            ev_free2[j].record(main)
+            if not last:
+                issue_dedup(i + 1)
+            if evs:
+                evs[2].record(main)
+            return
         if args.hashed:
             E.emb_hash_translate(tabs.ctx, ids_dev[i % len(dev)], off, B, True, hws, idx)
             ev_tr.record(main)
@@ -254,9 +297,17 @@ def main() -> int:
         if evs:
             evs[2].record(main)
 
+    def run(sched, K, ev=None):
+        if sched == "pipeline":
+            # the prologue dedup starts after everything before it on main
+            ev_free2[0].record(main)
+            ev_free2[1].record(main)
+            issue_dedup(0)
+        for i in range(K):
+            step(i, sched, ev[i] if ev else None, last=i == K - 1)
+
     def timed(sched, K):
-        for i in range(args.warmup):
-            step(i, sched)
+        run(sched, args.warmup)
         torch.cuda.synchronize()
         tabs.check_device_error()
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
@@ -265,8 +316,7 @@ def main() -> int:
         torch.cuda.synchronize()
         wall0 = time.perf_counter()
         t0.record(main)
-        for i in range(K):
-            step(i, sched, ev[i])
+        run(sched, K, ev)
         t1.record(main)
         torch.cuda.synchronize()
         wall = time.perf_counter() - wall0
@@ -278,7 +328,7 @@ def main() -> int:
         return total, fwd, bwd, per_step
 
     K = args.steps
-    other = "serial" if args.schedule == "overlap" else "overlap"
+    other = "serial" if args.schedule != "serial" else "overlap"
     total_ms, fwd_ms, bwd_ms, per_step = timed(args.schedule, K)
     other_ms, _, _, _ = timed(other, K)
 
@@ -300,7 +350,7 @@ def main() -> int:
     bwd_bytes = sum(B * T * D * 4 + n * ib + (T * B + 1) * ib + u * urow_b + u * 8 + n * 4
                     for n, u in zip(steps_N, steps_U))
     lookups = sum(steps_N)
-    if args.schedule == "overlap" or args.unique_forward:
+    if args.schedule in ("overlap", "pipeline") or args.unique_forward:
         # the dedup's own I/O (indices, offsets, unique keys + counts, inverse)
         # runs in the forward phase under this schedule
         dd = sum(n * ib + (T * B + 1) * ib + u * 8 + n * 4 for n, u in zip(steps_N, steps_U))
@@ -325,8 +375,7 @@ def main() -> int:
 
     # per-kernel times (HIP events around each launch, on the launch stream)
     E.emb_set_kernel_timing(tabs.ctx, True)
-    for i in range(K):
-        step(i, args.schedule)
+    run(args.schedule, K)
     torch.cuda.synchronize()
     ktimes = E.emb_kernel_times(tabs.ctx)
     E.emb_set_kernel_timing(tabs.ctx, False)
@@ -400,6 +449,8 @@ def main() -> int:
         "phases": ("fwd includes the id -> row translation; " if args.hashed else "") + (
                    "fwd = dedup, then the unique-first forward (unique rows gathered once); bwd_update = "
                    if args.unique_forward else
+                   "fwd = forward (the next batch's dedup runs on a second stream alongside the forward and "
+                   "the update); bwd_update = " if args.schedule == "pipeline" else
                    "fwd = forward with the dedup on a second stream alongside it; bwd_update = " if args.schedule == "overlap"
                    else "fwd = forward; bwd_update = dedup + ") + (
                    f"routing to {args.pack} shards + reduce into the send slots (RB)" if args.pack

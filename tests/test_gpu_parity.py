@@ -327,6 +327,51 @@ def test_master_weights_three_steps():
                    master=True)
 
 
+def test_pipelined_dedup_matches_serial():
+    # three steps where the next batch's dedup runs on a side stream, into a
+    # second workspace, while the current step's forward and update run --
+    # the pattern of bench.py's pipeline schedule -- against three serial steps
+    cfg = W.make_config(2, batch=4096)
+    batches = [W.make_batch(cfg, k=k) for k in range(3)]
+    dys = [W.make_dy(cfg, k=k) for k in range(3)]
+    u = np.unique(np.concatenate([P.oracle_dedup(cfg, b)[0] for b in batches]))
+    _say("pipelined dedup cfg2")
+    results = []
+    for pipelined in (False, True):
+        tabs = P.make_tables(cfg)
+        dev = [P.to_dev(b, d) for b, d in zip(batches, dys)]
+        bufs = [tabs.backward_buffers(max(b.N for b in batches), cfg.batch, with_grad=False) for _ in range(2)]
+        main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+        free = [torch.cuda.Event(), torch.cuda.Event()]
+        done = [torch.cuda.Event(), torch.cuda.Event()]
+        free[0].record(main)
+        free[1].record(main)
+
+        def ahead(i):
+            side.wait_event(free[i % 2])
+            with torch.cuda.stream(side):
+                tabs.dedup(dev[i][0], dev[i][1], cfg.batch, cfg.pool, bufs[i % 2])
+            done[i % 2].record(side)
+
+        if pipelined:
+            ahead(0)
+        for i in range(3):
+            idx, off, dy = dev[i]
+            tabs.forward(idx, off, cfg.batch, cfg.pool)
+            if pipelined:
+                main.wait_event(done[i % 2])
+            tabs.backward(idx, off, cfg.batch, cfg.pool, dy, bufs[i % 2])
+            tabs.update(cfg.opt, cfg.lr, cfg.eps, bufs[i % 2], dY=dy)
+            free[i % 2].record(main)
+            if pipelined and i < 2:
+                ahead(i + 1)
+        torch.cuda.synchronize()
+        results.append(P.read_rows(tabs, cfg, u))
+        tabs.close()
+    assert np.array_equal(results[0][0].view(np.uint32), results[1][0].view(np.uint32))
+    assert np.array_equal(results[0][1].view(np.uint32), results[1][1].view(np.uint32))
+
+
 def test_dedup_ahead_on_second_stream_matches_serial():
     # emb_backward_dedup on a side stream, concurrent with the forward, then
     # the backward (which skips its dedup) and the fused update: bit-identical
