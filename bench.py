@@ -75,6 +75,9 @@ def parse():
                          "tables' hash maps (emb_hash_translate with insertion), then runs the step on the rows")
     ap.add_argument("--rows", type=int, default=0,
                     help="cap the rows of every table (0 = the workload's own sizes)")
+    ap.add_argument("--single-schedule", action="store_true",
+                    help="time only --schedule (no comparison schedule, no isolated-kernel pass), so a "
+                         "profiler trace of the run holds that schedule's launches alone")
     ap.add_argument("--ceiling", action="store_true",
                     help="only time plain library kernels (copy, read-only sum, fill) over 4 GiB: the "
                          "practical HBM ceiling the path's kernels are compared with")
@@ -330,7 +333,7 @@ def main() -> int:
     K = args.steps
     other = "serial" if args.schedule != "serial" else "overlap"
     total_ms, fwd_ms, bwd_ms, per_step = timed(args.schedule, K)
-    other_ms, _, _, _ = timed(other, K)
+    other_ms = None if args.single_schedule else timed(other, K)[0]
 
     def pct(q):
         return round(float(np.percentile(np.asarray(per_step), q)), 4)
@@ -374,13 +377,16 @@ def main() -> int:
                       "forward_on_rows_ms": round(e1.elapsed_time(e2) / K, 4)}
 
     # per-kernel times (HIP events around each launch, on the launch stream)
-    E.emb_set_kernel_timing(tabs.ctx, True)
-    run(args.schedule, K)
-    torch.cuda.synchronize()
-    ktimes = E.emb_kernel_times(tabs.ctx)
-    E.emb_set_kernel_timing(tabs.ctx, False)
-    kavg_us = {k: (ms / n * 1e3 if n else 0.0) for k, (ms, n) in ktimes.items()}
-    ktot = {k: ms for k, (ms, n) in ktimes.items()}
+    def kernel_times(sched):
+        E.emb_set_kernel_timing(tabs.ctx, True)
+        run(sched, K)
+        torch.cuda.synchronize()
+        kt = E.emb_kernel_times(tabs.ctx)
+        E.emb_set_kernel_timing(tabs.ctx, False)
+        return ({k: (ms / n * 1e3 if n else 0.0) for k, (ms, n) in kt.items()},
+                {k: ms for k, (ms, n) in kt.items()})
+
+    kavg_us, ktot = kernel_times(args.schedule)
     dominant = max((k for k in ktot if k != "init"), key=lambda k: ktot[k])
 
     # algorithmic bytes of one launch of the dominant kernel
@@ -399,17 +405,28 @@ def main() -> int:
         "atomic": B * T * D * 4 + Navg * D * 4 * 2 + Navg * 4,
     }
     alg = per_launch.get(dominant)
-    roofline = None
-    if alg is not None and kavg_us[dominant] > 0:
-        achieved = alg / (kavg_us[dominant] * 1e-6) / 1e9
+
+    def roofline_of(avg_us):
+        if alg is None or avg_us <= 0:
+            return None
+        achieved = alg / (avg_us * 1e-6) / 1e9
         wtag = f"cfg{args.config}" + ("_uniform" if args.uniform_keys else "")
         src = {"forward": "k_forward.hip", "reduce": "k_reduce.hip", "sort_scatter": "k_keys_sort.hip",
                "sort_hist": "k_keys_sort.hip", "keys": "k_keys_sort.hip", "atomic": "k_atomic.hip"}[dominant]
-        traffic = measured_traffic(dominant, wtag)
-        roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                    "traffic": traffic, "alg_bytes_per_launch": int(alg),
-                    "avg_launch_us": round(kavg_us[dominant], 2), "source": src}
+        return {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": measured_traffic(dominant, wtag), "alg_bytes_per_launch": int(alg),
+                "avg_launch_us": round(avg_us, 2), "source": src}
+
+    # live: launch durations under the timed schedule (with the pipeline the
+    # dominant kernel shares the GPU with the next batch's dedup)
+    roofline = roofline_of(kavg_us[dominant])
+    roofline_alone = None
+    if args.schedule != "serial" and not args.single_schedule:
+        kavg_serial, _ = kernel_times("serial")
+        roofline_alone = roofline_of(kavg_serial.get(dominant, 0.0))
+        if roofline_alone:
+            roofline_alone["schedule"] = "serial (the kernel alone on the GPU)"
 
     # CPU oracle on a bounded sample of batch 0
     cpu = None
@@ -428,7 +445,7 @@ def main() -> int:
         "ms_per_step_p10_p50_p90": [pct(10), pct(50), pct(90)],
         "schedule": args.schedule,
         "reduce": args.reduce if not args.pack else f"pack to {args.pack} shards (RB)",
-        f"ms_per_step_{other}": round(other_ms / K, 4),
+        f"ms_per_step_{other}": round(other_ms / K, 4) if other_ms is not None else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -464,6 +481,7 @@ def main() -> int:
         "kernels_avg_us": {k: round(v, 2) for k, v in kavg_us.items() if v > 0},
         "kernels_ms_per_step": {k: round(v / K, 4) for k, v in ktot.items() if v > 0},
         "roofline": roofline,
+        "roofline_alone": roofline_alone,
         "cpu_baseline": cpu,
     }
     if hashed_fwd:
