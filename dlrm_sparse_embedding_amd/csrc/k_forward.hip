@@ -69,7 +69,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SRC == 2 ? 
   const int N = (int)a.N;
   // grid-stride over logical blocks: the grid may be capped below the work so
   // that kernels on another stream (the dedup) keep wave slots
-  for (int blk = blockIdx.x; blk < a.nblk; blk += gridDim.x) {
+  // With the full grid (padded to a multiple of 8) blocks are remapped so that
+  // each XCD walks its own contiguous eighth of the bag runs: at any time an
+  // XCD's L2 holds the hot rows of one table rather than every XCD holding
+  // the same few tables' (HBM reads of the 26x4Mx128 one-hot forward: 468 ->
+  // 384 MB per launch).
+  const int blk_first =
+      (gridDim.x & 7) == 0 && (int)gridDim.x >= a.nblk ? xcd_remap(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+  for (int blk = blk_first; blk < a.nblk; blk += gridDim.x) {
     const long long sg = (long long)blk * SGW + threadIdx.x / LPR;
     if (sg >= a.total_sg) break;
 
@@ -272,7 +279,7 @@ hipError_t launch_forward(const Geom& g, const DevCtx& dc, const void* indices, 
   args.hmeta = hash ? hash->meta : nullptr;
   args.hkeys = hash ? hash->keys : nullptr;
   args.hvals = hash ? hash->vals : nullptr;
-  const int grid = max_blocks > 0 && max_blocks < args.nblk ? max_blocks : args.nblk;
+  const int grid = max_blocks > 0 && max_blocks < args.nblk ? max_blocks : round_up8(args.nblk);
   switch (g.dtype) {
     case EMB_F32:
       FWD_IDX_SWITCH(EMB_F32)
