@@ -144,8 +144,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
   for (int i = threadIdx.x; i <= a.T; i += 256) s_ro[i] = a.row_off[i];
   __syncthreads();
   // dY rows in flight: the largest count that fits 64 VGPRs without spills at
-  // 8 waves/SIMD (spills cost scratch traffic in HBM: measured ~270 MB/launch)
-  constexpr int U = (MODE == 2 && MEAN) ? 4 : 6;
+  // 8 waves/SIMD (spills cost scratch traffic in HBM: measured ~270 MB/launch);
+  // Adagrad with mean pooling or a 16-bit / master row holds more live values
+  constexpr int U = (MODE == 2 && (MEAN || (DT & 7) != EMB_F32 || (DT & kMasterBit))) ? 4 : 6;
   constexpr int SGW = 256 / LPR;
   const int lsg = threadIdx.x & (LPR - 1);
   const int c0 = lsg * 4;
