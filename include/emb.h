@@ -13,21 +13,30 @@
  *     bound, tables are sharded across GPUs (one GPU's share is what this
  *     library holds);
  *     slide "WEIGHT CONVERSION FOR MIXED PRECISION TRAINING": the optimizer
- *     computes in FP32.
+ *     computes in FP32 (optionally on FP32 master weights whose
+ *     low-precision cast the lookups read).
  *   - NVIDIA Merlin blog, HugeCTR section: the features of one slot are
  *     each turned into an embedding vector and reduced to a single vector.
- *   - EMBark (RecSys'24 news article, section on embedding clusters):
- *     reduction-based and unique-based compression of embedding traffic,
- *     applied here locally as key dedup + per-key gradient reduction.
+ *   - EMBark (RecSys'24 news article, sections on embedding clusters and 3D
+ *     sharding): reduction-based and unique-based compression of embedding
+ *     traffic, applied here locally as key dedup + per-key gradient
+ *     reduction, and as the routing of unique keys to owner shards.
+ *   - Sparse Operation Kit 2.0 article (Merlin TensorFlow plugin): dynamic
+ *     embedding, i.e. ids mapped to rows as they arrive (the hash-keyed
+ *     lookup below).
  *
  * Conventions for every call
  *   - All tensors are caller-owned device memory (allocated e.g. by
- *     PyTorch). The library never frees caller memory and never allocates
- *     more than a small per-context descriptor block (lazily, on first use).
+ *     PyTorch). The library never frees caller memory. It allocates only
+ *     small per-context device arrays: the descriptor block (tables, row
+ *     offsets, error flag; lazily, on first use), and when those features
+ *     are used the shard rules (8 bytes per table) and the hash-map layout
+ *     (16 bytes per table).
  *   - Every call that takes `hip_stream` is asynchronous on that stream
  *     (a hipStream_t passed as void*; NULL = the null stream) and performs
- *     no host synchronisation, except emb_check_device_error and
- *     emb_kernel_times.
+ *     no host synchronisation, except emb_check_device_error,
+ *     emb_kernel_times, and the one-time uploads named at
+ *     emb_set_shard_map and emb_hash_attach.
  *   - Return value: EMB_OK (0) or a negative EMB_E_* code; then
  *     emb_last_error() returns a message (per thread). No C++ exception
  *     crosses this interface. Argument validation happens before any HIP
@@ -134,7 +143,8 @@ int emb_row_offsets(const emb_ctx* ctx, int64_t* row_offset);
  * (t, r, c) becomes w = fp32(v) * fp32(0.1f * 2^-24) with
  * v = (splitmix64(seed ^ (t << 40) ^ (r*dim + c)) >> 40) - 2^23, i.e.
  * U(-0.05, 0.05), rounded to the storage type with round-to-nearest-even;
- * Adagrad state (if present) is set to 0. SplitMix64 as published by
+ * fp32 masters (if present) get w itself, so the stored copy is their RNE
+ * cast; Adagrad state (if present) is set to 0. SplitMix64 as published by
  * Steele, Lea & Flood (OOPSLA 2014). */
 int emb_init_uniform(emb_ctx* ctx, uint64_t seed, void* hip_stream);
 
@@ -183,7 +193,8 @@ size_t emb_backward_workspace_bytes(const emb_ctx* ctx, int64_t N, int32_t B);
  * carries the sorted segments to emb_sparse_update; it, offsets and dY
  * must stay valid and unchanged until that call. A lookup with an
  * out-of-range index gets the key sum(rows) (which sorts last and is never
- * applied by the update) and raises the device error flag.
+ * applied by the update) and raises the device error flag; offsets that
+ * break the CSR contract raise it too (see emb_check_device_error).
  * N must be < 2^31. */
 int emb_backward_unique_reduce(emb_ctx* ctx, const void* indices, const void* offsets,
                                int32_t itype, int64_t N, int32_t B, int32_t pool,
@@ -211,7 +222,9 @@ int emb_backward_dedup(emb_ctx* ctx, const void* indices, const void* offsets, i
  *   SGD:     w <- w - (lr*g)
  *   Adagrad: G <- G + g*g;  w <- w - (lr*g) / (sqrt(G) + eps)
  * in fp32 with each operation rounded separately in this order, then w
- * rounded to the storage type with round-to-nearest-even. g is
+ * rounded to the storage type with round-to-nearest-even. With fp32
+ * masters, w is the master (the stored copy is not read) and the master and
+ * its RNE cast are both written in the same pass. g is
  * reduced_grad[u] if reduced_grad is not NULL (the buffer the backward
  * filled), else it is reduced from dY inside the update kernel (fused
  * path, no materialised gradient). Rows no lookup touched are not read or
