@@ -102,10 +102,14 @@ struct emb_ctx {
 namespace {
 
 int ensure_device(emb_ctx* c) {
-  if (c->dev_block) return EMB_OK;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (c->dev_block) {
+    if (dev != c->device)
+      return fail(EMB_E_INVAL, "the context lives on device %d but device %d is current", c->device, dev);
+    return EMB_OK;
+  }
   const int T = c->g.T;
   const size_t tab_bytes = sizeof(DevTable) * (size_t)T;
   const size_t ro_off = (tab_bytes + 255) & ~size_t(255);
@@ -171,9 +175,12 @@ struct KScope {
     }
   }
   ~KScope() {
-    if (c->timing && e0 && e1) {
+    if (e0 && e1) {
       (void)hipEventRecord(e1, st);
       c->pending.push_back({kid, e0, e1});
+    } else {  // an event could not be created: time nothing, keep the other one
+      if (e0) c->free_events.push_back(e0);
+      if (e1) c->free_events.push_back(e1);
     }
   }
 };

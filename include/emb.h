@@ -32,6 +32,9 @@
  *     offsets, error flag; lazily, on first use), and when those features
  *     are used the shard rules (8 bytes per table) and the hash-map layout
  *     (16 bytes per table).
+ *   - A context belongs to the HIP device that is current at its first
+ *     device call (its descriptor block lives there); later calls with
+ *     another device current fail with EMB_E_INVAL.
  *   - Every call that takes `hip_stream` is asynchronous on that stream
  *     (a hipStream_t passed as void*; NULL = the null stream) and performs
  *     no host synchronisation, except emb_check_device_error,
