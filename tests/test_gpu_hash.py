@@ -143,3 +143,23 @@ def test_reserved_id_flagged():
         tabs.check_device_error()
     assert ei.value.code == E.EMB_E_INVAL
     tabs.close()
+
+
+@pytest.mark.slow
+def test_translate_full_size():
+    # 1.7 M lookups of 26 tables with 4 M rows each: every row handed out
+    # equals the oracle's, over two steps with insertion
+    rng = np.random.default_rng(12)
+    cfg = W.make_config(3)
+    rows = [t.rows for t in cfg.tables]
+    P.say("hash translate full cfg3")
+    tabs = P.make_tables(cfg)
+    tabs.hash_attach()
+    ht = O.HashTables(rows)
+    for step in range(2):
+        batch, ids = _ids_batch(rng, rows, cfg.batch, 1, 4_000_000, np.int32, fit=True)
+        got = tabs.hash_translate(torch.from_numpy(ids).cuda(), torch.from_numpy(batch.offsets).cuda(),
+                                  cfg.batch, True).cpu().numpy().astype(np.int64)
+        ref = ht.translate(ids, batch.offsets, cfg.T, cfg.batch, True)
+        assert np.array_equal(got, ref), (step, int((got != ref).sum()))
+    tabs.close()

@@ -146,3 +146,35 @@ def test_update_after_pack_is_unchanged():
         tabs.close()
     assert np.array_equal(results[0][0].view(np.uint32), results[1][0].view(np.uint32))
     assert np.array_equal(results[0][1].view(np.uint32), results[1][1].view(np.uint32))
+
+
+@pytest.mark.slow
+def test_pack_full_size():
+    # the 26 x 4M x 128 workload at batch 65536: 636 k unique keys routed to 64
+    # shards, every key, offset and slot checked, the RB gradients bit-equal
+    # to the unique-order reduction
+    cfg = W.make_config(3)
+    batch = W.make_batch(cfg, k=1)
+    dY = W.make_dy(cfg, k=1)
+    rules = _rules(lambda t: t % 3, cfg.T, 64)
+    P.say("pack full cfg3 N", batch.N)
+    tabs = P.make_tables(cfg)
+    idx, off, dy = P.to_dev(batch, dY)
+    bufs = tabs.backward_buffers(batch.N, cfg.batch, with_grad=True)
+    tabs.backward(idx, off, cfg.batch, cfg.pool, dy, bufs)
+    tabs.set_shard_map(rules, 64)
+    pb = tabs.pack_buffers(batch.N, 64, with_grad=True)
+    tabs.pack(bufs, pb, dY=dy)
+    torch.cuda.synchronize()
+    u, _, _ = P.oracle_dedup(cfg, batch)
+    U = int(bufs["num_unique"].item())
+    assert U == len(u)
+    ok, ooff, oslot, _ = O.pack_by_shard(u, cfg.row_offset(), rules, 64)
+    assert np.array_equal(pb["send_offsets"].cpu().numpy().astype(np.int64), ooff)
+    assert np.array_equal(pb["send_keys"][:U].cpu().numpy().view(np.uint32).astype(np.int64), ok)
+    assert np.array_equal(pb["slot_of_unique"][:U].cpu().numpy().astype(np.int64), oslot)
+    sg = pb["send_grad"][:U]
+    rg = bufs["reduced_grad"][:U]
+    slot = torch.from_numpy(oslot).cuda()
+    assert torch.equal(sg[slot].view(torch.int32), rg.view(torch.int32))
+    tabs.close()

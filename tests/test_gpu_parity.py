@@ -87,6 +87,17 @@ def test_config_full_sampled(cfg_id):
     P.run_step(cfg, batch, dY, path="fused", sample_bags=512, sample_keys=3000)
 
 
+@pytest.mark.slow
+def test_master_weights_full_sampled():
+    # the 100 x 1M x 128 bf16 workload (mean pooling, SGD) with fp32 masters at
+    # its full batch: 25.6 GB of bf16 rows + 51.2 GB of masters
+    cfg = W.make_config(4)
+    batch = W.make_batch(cfg)
+    dY = W.make_dy(cfg)
+    _say(f"cfg4 full with masters N={batch.N}")
+    P.run_step(cfg, batch, dY, path="fused", sample_bags=256, sample_keys=3000, master=True)
+
+
 # ---------------------------------------------------------------------------
 # exactness: integer upstream gradients make every fp32 sum exact, so the
 # fused sparse update must equal the oracle bit for bit

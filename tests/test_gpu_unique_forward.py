@@ -94,3 +94,14 @@ def test_backward_after_unique_forward():
     ref = P.run_step(cfg, batch, dY, sample_untouched=0)
     assert np.array_equal(w1.view(np.uint32), ref["w_new"].view(np.uint32))
     assert np.array_equal(G1.view(np.uint32), ref["G_new"].view(np.uint32))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("cfg_id", [3, 5])
+def test_unique_forward_full_size(cfg_id):
+    cfg = W.make_config(cfg_id)
+    batch = W.make_batch(cfg, k=2)
+    P.say("unique forward full", cfg_id, "N", batch.N)
+    tabs, _, _, Y0, Y1 = _both(cfg, batch, None)
+    _same(Y0, Y1)
+    tabs.close()
