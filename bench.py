@@ -338,7 +338,7 @@ def main() -> int:
     def pct(q):
         return round(float(np.percentile(np.asarray(per_step), q)), 4)
 
-    # algorithmic bytes per step (SURVEY-style formula, actual N and U)
+    # algorithmic bytes per step (what the method must move, from the actual N and U)
     ib = 4 if host_batches[0].indices.dtype == np.int32 else 8
     state_b = D * 4 if cfg.opt == "adagrad" else 0
     # weight bytes per unique row: stored row read + written, or with a master

@@ -6,7 +6,7 @@ shares no code, header, table or constant with the HIP path; the only thing
 both sides consume in common is the seeded input generator
 (``dlrm_sparse_embedding_amd.workloads``), which holds none of this arithmetic.
 
-What is computed, and where the pages define it
+What is computed, and where the sources define it
 -----------------------------------------------
 * Pooled forward -- "Merlin HugeCTR: GPU-accelerated recommender system
   training and inference" (GTC 2022 deck), slide "COMMON EMBEDDING PRIMITIVES":

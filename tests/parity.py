@@ -2,8 +2,8 @@
 path through the C ABI and compare it with the CPU oracle on the same seeded
 inputs.
 
-Tolerances (derived from the arithmetic, rtol from the benchmark spec's
-relative tolerance: 1e-5 for fp32, 2e-2 for 16-bit storage):
+Tolerances (derived from the arithmetic; relative tolerance 1e-5 for fp32 and
+2e-2 for 16-bit storage):
   pooled output  |Y - Y_ref| <= 1e-5 * M,  M = the same pooling of |W| (the
                  recursive-summation bound (L-1) * 2^-24 * M stays below it for
                  L <= 100; every stored value is exact in fp32);
