@@ -98,8 +98,10 @@ __global__ __launch_bounds__(256) void k_keys(KeysArgs a) {
         else
           flag |= 1;
       }
-      a.keys[p] = ((uint64_t)key << 32) | (uint32_t)p;
-      a.bag_of_pos[p] = (int32_t)(g0 + j);
+      // non-temporal: the dedup's streams should not evict the rows of the
+      // forward / update that may run beside it on another stream
+      __builtin_nontemporal_store(((uint64_t)key << 32) | (uint32_t)p, a.keys + p);
+      __builtin_nontemporal_store((int32_t)(g0 + j), a.bag_of_pos + p);
     }
   }
   if (flag) atomicOr(a.err, flag);
@@ -314,7 +316,7 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const uint64_t* __restrict
     const uint64_t x = s_stage[j];
     const uint32_t d = digit_of<RB>(x, shift);
     const size_t dst = (size_t)s_gbase[d] + (uint32_t)(j - (int)s_bexcl[d]);
-    if (dst < (size_t)N) out[dst] = x;
+    if (dst < (size_t)N) __builtin_nontemporal_store(x, out + dst);  // see k_keys
   }
 }
 

@@ -202,8 +202,9 @@ __global__ __launch_bounds__(256) void k_rle_write(RleArgs a) {
     const int32_t seg_start = (int32_t)max(pm, im[k]) - 1;
     const uint32_t key = key_of(item[k]);
     const uint32_t pos = (uint32_t)item[k];
-    if (pos < (uint32_t)a.N) a.inverse[pos] = seg;
-    a.sorted_bag[i] = bag[k];
+    // non-temporal: keep the L2 for the forward / update beside the dedup
+    if (pos < (uint32_t)a.N) __builtin_nontemporal_store(seg, a.inverse + pos);
+    __builtin_nontemporal_store(bag[k], a.sorted_bag + i);
     if (fl & (1u << k)) {
       a.unique_keys[seg] = key;
       a.seg_off[seg] = (int32_t)i;
