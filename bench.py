@@ -387,7 +387,6 @@ def main() -> int:
                 {k: ms for k, (ms, n) in kt.items()})
 
     kavg_us, ktot = kernel_times(args.schedule)
-    dominant = max((k for k in ktot if k != "init"), key=lambda k: ktot[k])
 
     # algorithmic bytes of one launch of the dominant kernel
     Navg = lookups / K
@@ -404,6 +403,9 @@ def main() -> int:
         # read-modify-write of its unique row (D*4 each way), inverse reads
         "atomic": B * T * D * 4 + Navg * D * 4 * 2 + Navg * 4,
     }
+    # the kernel family with the most time per step among those the roofline
+    # has a byte count for (on the real workloads: the fused update)
+    dominant = max((k for k in ktot if k in per_launch and ktot[k] > 0), key=lambda k: ktot[k])
     alg = per_launch.get(dominant)
 
     def roofline_of(avg_us):
