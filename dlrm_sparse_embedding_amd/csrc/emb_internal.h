@@ -80,6 +80,8 @@ inline int next_pow2(int x) {
   return p;
 }
 inline int round_up8(int x) { return (x + 7) & ~7; }
+// Column blocks of a row of D fp32 columns at 4 columns per lane, lpr lanes.
+inline unsigned col_blocks(int D, int lpr) { return (unsigned)((D + 4 * lpr - 1) / (4 * lpr)); }
 
 // Geometry common to every table of a context.
 struct Geom {

@@ -36,7 +36,7 @@ struct AtomArgs {
 template <typename IDX, int LPR, bool MEAN>
 __global__ __launch_bounds__(256) void k_atomic_scatter(AtomArgs a) {
   constexpr int SGW = 256 / LPR;
-  const int c0 = (threadIdx.x & (LPR - 1)) * 4;
+  const int c0 = (int)blockIdx.y * 4 * LPR + (threadIdx.x & (LPR - 1)) * 4;  // column block: blockIdx.y
   const bool act = c0 < a.D;
   const int U = min(*a.num_unique, (int)a.N);
   const long long bags = (long long)a.T * a.B;
@@ -71,13 +71,14 @@ hipError_t launch_atomic_reduce(const Geom& g, const void* offsets, int itype, l
   AtomArgs a{offsets, dY, inverse, num_unique, grad, N, g.T, B, g.D};
   int lpr = next_pow2((g.D + 3) / 4);
   if (lpr < 2) lpr = 2;
+  if (lpr > 64) lpr = 64;  // wider rows take col_blocks() blocks along y
   const int sgw = 256 / lpr;
   const long long bags = (long long)g.T * B;
   const int grid = (int)std::min<long long>((bags + sgw - 1) / sgw, 16384);
   const bool mean = pool == EMB_POOL_MEAN;
 #define L_AT(IDX, P)                                                                           \
-  if (mean) hipLaunchKernelGGL((k_atomic_scatter<IDX, P, true>), dim3(grid), dim3(256), 0, st, a); \
-  else hipLaunchKernelGGL((k_atomic_scatter<IDX, P, false>), dim3(grid), dim3(256), 0, st, a);
+  if (mean) hipLaunchKernelGGL((k_atomic_scatter<IDX, P, true>), dim3(grid, col_blocks(g.D, P)), dim3(256), 0, st, a); \
+  else hipLaunchKernelGGL((k_atomic_scatter<IDX, P, false>), dim3(grid, col_blocks(g.D, P)), dim3(256), 0, st, a);
 #define L_AT_LPR(IDX)                   \
   switch (lpr) {                        \
     case 2: L_AT(IDX, 2) break;         \

@@ -149,7 +149,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
   constexpr int U = (MODE == 2 && (MEAN || (DT & 7) != EMB_F32 || (DT & kMasterBit))) ? 4 : 6;
   constexpr int SGW = 256 / LPR;
   const int lsg = threadIdx.x & (LPR - 1);
-  const int c0 = lsg * 4;
+  // blockIdx.y picks the column block: rows wider than 4*LPR columns
+  // (16-bit rows of more than 256) are spread over gridDim.y blocks
+  const int c0 = (int)blockIdx.y * 4 * LPR + lsg * 4;
   const bool act = c0 < a.D;
   const uint32_t dys = (uint32_t)(a.T * a.D);
   const int nsg = gridDim.x * SGW;
@@ -265,7 +267,7 @@ __global__ __launch_bounds__(256) void k_level1(RedArgs a) {
   constexpr int SGW = 256 / LPR;
   const int J = blockIdx.x * SGW + threadIdx.x / LPR;
   if (J >= a.ntiles1) return;
-  const int c0 = (threadIdx.x & (LPR - 1)) * 4;
+  const int c0 = (int)blockIdx.y * 4 * LPR + (threadIdx.x & (LPR - 1)) * 4;  // column block: blockIdx.y
   const bool act = c0 < a.D;
   const int jf = J * kL1Tiles;
   const int jl = min(jf + kL1Tiles - 1, a.ntiles - 1);
@@ -304,7 +306,7 @@ __global__ __launch_bounds__(256) void k_combine(RedArgs a) {
   __syncthreads();
   const int j = blockIdx.x * SGW + threadIdx.x / LPR;
   if (j >= a.ntiles) return;
-  const int c0 = (threadIdx.x & (LPR - 1)) * 4;
+  const int c0 = (int)blockIdx.y * 4 * LPR + (threadIdx.x & (LPR - 1)) * 4;  // column block: blockIdx.y
   const bool act = c0 < a.D;
   const int u = a.tile_last_seg[j];
   if (u < 0 || u >= a.N) return;
@@ -333,7 +335,7 @@ __global__ __launch_bounds__(256) void k_apply(RedArgs a) {
   __syncthreads();
   constexpr int SGW = 256 / LPR;
   const int lsg = threadIdx.x & (LPR - 1);
-  const int c0 = lsg * 4;
+  const int c0 = (int)blockIdx.y * 4 * LPR + lsg * 4;  // column block: blockIdx.y
   if (c0 >= a.D) return;
   const int U = min(*a.num_unique, a.N);
   for (long long u = (long long)blockIdx.x * SGW + threadIdx.x / LPR; u < U;
@@ -383,9 +385,11 @@ static RedArgs make_args(const Geom& g, const DevCtx& dc, int N, const WsLayout&
   return a;
 }
 
+// Lanes per row for the fp32-gradient kernels: 4 columns per lane, at most a
+// wave; wider rows take col_blocks() blocks along the grid's y axis.
 static int lpr_b(const Geom& g) {
   int l = next_pow2((g.D + 3) / 4);
-  return l < 2 ? 2 : l;
+  return l < 2 ? 2 : (l > 64 ? 64 : l);
 }
 
 #define LPR_SWITCH(LAUNCH)          \
@@ -400,21 +404,21 @@ static int lpr_b(const Geom& g) {
 
 template <int DT, int MODE, bool MEAN>
 static void launch_chunks_t(int lpr, int grid, size_t smem, hipStream_t st, const RedArgs& a) {
-#define L_CH(P) hipLaunchKernelGGL((k_chunks<DT, P, MODE, MEAN>), dim3(grid), dim3(256), smem, st, a);
+#define L_CH(P) hipLaunchKernelGGL((k_chunks<DT, P, MODE, MEAN>), dim3(grid, col_blocks(a.D, P)), dim3(256), smem, st, a);
   LPR_SWITCH(L_CH)
 #undef L_CH
 }
 
 template <int DT, int MODE>
 static void launch_combine_t(int lpr, int grid, size_t smem, hipStream_t st, const RedArgs& a) {
-#define L_CO(P) hipLaunchKernelGGL((k_combine<DT, P, MODE>), dim3(grid), dim3(256), smem, st, a);
+#define L_CO(P) hipLaunchKernelGGL((k_combine<DT, P, MODE>), dim3(grid, col_blocks(a.D, P)), dim3(256), smem, st, a);
   LPR_SWITCH(L_CO)
 #undef L_CO
 }
 
 template <int DT, int MODE>
 static void launch_apply_t(int lpr, int grid, size_t smem, hipStream_t st, const RedArgs& a) {
-#define L_AP(P) hipLaunchKernelGGL((k_apply<DT, P, MODE>), dim3(grid), dim3(256), smem, st, a);
+#define L_AP(P) hipLaunchKernelGGL((k_apply<DT, P, MODE>), dim3(grid, col_blocks(a.D, P)), dim3(256), smem, st, a);
   LPR_SWITCH(L_AP)
 #undef L_AP
 }
@@ -488,7 +492,7 @@ hipError_t launch_combine(const Geom& g, const DevCtx& dc, int mode, int N, cons
   const int sgw = 256 / lpr;
   if (L.ntiles1 > 1) {
     const int grid1 = ceil_div(L.ntiles1, sgw);
-#define L_L1(P) hipLaunchKernelGGL((k_level1<P>), dim3(grid1), dim3(256), 0, st, a);
+#define L_L1(P) hipLaunchKernelGGL((k_level1<P>), dim3(grid1, col_blocks(a.D, P)), dim3(256), 0, st, a);
     LPR_SWITCH(L_L1)
 #undef L_L1
   }
