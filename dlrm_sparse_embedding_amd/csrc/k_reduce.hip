@@ -138,7 +138,9 @@ __device__ __forceinline__ int slot_of(int so, int j, int tile) {
   return (j == so / tile && so % tile != 0) ? 2 * j + 1 : 2 * j;
 }
 
-template <int DT, int LPR, int MODE, bool MEAN>
+// REP: the batch may hold a key more than once in one bag (more lookups than
+// bags), so a segment can repeat a bag; see the multiplicity loop below.
+template <int DT, int LPR, int MODE, bool MEAN, bool REP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_chunks(RedArgs a) {
   extern __shared__ uint32_t s_ro[];
   for (int i = threadIdx.x; i <= a.T; i += 256) s_ro[i] = a.row_off[i];
@@ -146,7 +148,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
   // dY rows in flight: the largest count that fits 64 VGPRs without spills at
   // 8 waves/SIMD (spills cost scratch traffic in HBM: measured ~270 MB/launch);
   // Adagrad with mean pooling or a 16-bit / master row holds more live values
-  constexpr int U = (MODE == 2 && (MEAN || (DT & 7) != EMB_F32 || (DT & kMasterBit))) ? 4 : 6;
+  constexpr int U0 = (MODE == 2 && (MEAN || (DT & 7) != EMB_F32 || (DT & kMasterBit))) ? 4 : 6;
+  constexpr int U = REP ? U0 - 1 : U0;  // the multiplicities take registers too
   constexpr int SGW = 256 / LPR;
   const int lsg = threadIdx.x & (LPR - 1);
   // blockIdx.y picks the column block: rows wider than 4*LPR columns
@@ -193,22 +196,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
       int bg[U];
 #pragma unroll
       for (int k = 0; k < U; ++k) bg[k] = i + k < ce ? (i + k == cb ? bag0 : a.sorted_bag[i + k]) : -1;
+      // A segment's positions are ascending, so repeats of one bag (a key
+      // looked up several times in one multi-hot bag) sit next to each
+      // other. Only a run's first entry loads its dY row; the run adds it
+      // with its multiplicity (3 bits per entry in `mul`), a one-hot batch
+      // adds every row once, as a plain sum would.
+      uint32_t mul = 0111111u;  // one per entry: no repeats
+      if constexpr (REP) {
+        mul = 0;
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int k = U - 1; k >= 0; --k) {
+          ++cnt;
+          if (!(k > 0 && bg[k] >= 0 && bg[k] == bg[k - 1])) {
+            mul |= cnt << (3 * k);
+            cnt = 0;
+          }
+        }
+      }
       f4 v[U];
 #pragma unroll
       for (int k = 0; k < U; ++k) {
         v[k] = f4{0.f, 0.f, 0.f, 0.f};
         const unsigned b = (unsigned)(bg[k] - bagt);
-        if (bg[k] >= 0 && b < (unsigned)a.B && act) {
+        if (bg[k] >= 0 && b < (unsigned)a.B && act && ((mul >> (3 * k)) & 7u)) {
           v[k] = *reinterpret_cast<const f4*>(a.dY + (b * dys + dyt));
           if constexpr (MEAN) v[k] *= a.inv_len[bg[k]];
         }
       }
 #pragma unroll
       for (int k = 0; k < U; ++k) {
-        acc[0] += v[k].x;
-        acc[1] += v[k].y;
-        acc[2] += v[k].z;
-        acc[3] += v[k].w;
+        const float m = (float)((mul >> (3 * k)) & 7u);
+        acc[0] = fmaf(m, v[k].x, acc[0]);
+        acc[1] = fmaf(m, v[k].y, acc[1]);
+        acc[2] = fmaf(m, v[k].z, acc[2]);
+        acc[3] = fmaf(m, v[k].w, acc[3]);
       }
     }
 
@@ -402,9 +424,9 @@ static int lpr_b(const Geom& g) {
     default: LAUNCH(64) break;      \
   }
 
-template <int DT, int MODE, bool MEAN>
+template <int DT, int MODE, bool MEAN, bool REP>
 static void launch_chunks_t(int lpr, int grid, size_t smem, hipStream_t st, const RedArgs& a) {
-#define L_CH(P) hipLaunchKernelGGL((k_chunks<DT, P, MODE, MEAN>), dim3(grid, col_blocks(a.D, P)), dim3(256), smem, st, a);
+#define L_CH(P) hipLaunchKernelGGL((k_chunks<DT, P, MODE, MEAN, REP>), dim3(grid, col_blocks(a.D, P)), dim3(256), smem, st, a);
   LPR_SWITCH(L_CH)
 #undef L_CH
 }
@@ -454,9 +476,15 @@ static void launch_apply_t(int lpr, int grid, size_t smem, hipStream_t st, const
   }
 
 template <int DT, int MODE>
-static void launch_chunks_pool(bool mean, int lpr, int grid, size_t smem, hipStream_t st, const RedArgs& a) {
-  if (mean) launch_chunks_t<DT, MODE, true>(lpr, grid, smem, st, a);
-  else launch_chunks_t<DT, MODE, false>(lpr, grid, smem, st, a);
+static void launch_chunks_pool(bool mean, bool rep, int lpr, int grid, size_t smem, hipStream_t st,
+                               const RedArgs& a) {
+  if (rep) {
+    if (mean) launch_chunks_t<DT, MODE, true, true>(lpr, grid, smem, st, a);
+    else launch_chunks_t<DT, MODE, false, true>(lpr, grid, smem, st, a);
+  } else {
+    if (mean) launch_chunks_t<DT, MODE, true, false>(lpr, grid, smem, st, a);
+    else launch_chunks_t<DT, MODE, false, false>(lpr, grid, smem, st, a);
+  }
 }
 
 hipError_t launch_reduce(const Geom& g, const DevCtx& dc, int mode, int N, int B, int pool,
@@ -478,7 +506,10 @@ hipError_t launch_reduce(const Geom& g, const DevCtx& dc, int mode, int N, int B
   const long long want = (upper + sgw - 1) / sgw;
   const int grid = (int)(want < 16384 ? (want > 0 ? want : 1) : 16384);
   const size_t smem = (size_t)(g.T + 1) * 4;
-  DISPATCH_DT_MODE(launch_chunks_pool, mean, lpr, grid, smem, st, a)
+  // with no more lookups than bags a repeat is rare (it needs an empty bag
+  // elsewhere); the plain loop is then the faster one, and both are exact
+  const bool rep = (long long)N > (long long)g.T * B;
+  DISPATCH_DT_MODE(launch_chunks_pool, mean, rep, lpr, grid, smem, st, a)
   return hipGetLastError();
 }
 
