@@ -593,6 +593,7 @@ int emb_sparse_update(emb_ctx* ctx, int32_t opt, float lr, float eps, const void
   const long long N = ctx->last.N;
   if (N > 0 && !reduced_grad && !dY) return fail(EMB_E_INVAL, "dY is NULL (needed by the fused path)");
   if (dY && !aligned(dY, 16)) return fail(EMB_E_INVAL, "dY must be 16-byte aligned");
+  if (reduced_grad && !aligned(reduced_grad, 16)) return fail(EMB_E_INVAL, "reduced_grad must be 16-byte aligned");
   if (N == 0) return ok();
   int rc;
   if ((rc = ensure_device(ctx))) return rc;

@@ -248,6 +248,8 @@ def emb_set_kernel_timing(ctx: int, enable: bool) -> None:
 
 def emb_forward_pooled_unique(ctx: int, indices, offsets, B: int, pool: str, ws, rows_buf, out,
                               stream=None) -> None:
+    if offsets.dtype != indices.dtype:
+        raise ValueError("indices and offsets must share one integer type")
     _check(lib().emb_forward_pooled_unique(
         ctx, _ptr(indices), _ptr(offsets), _itype(indices), int(indices.numel()), int(B), POOL_CODE[pool],
         _ptr(ws), _ptr(rows_buf), int(rows_buf.numel() * rows_buf.element_size()) if rows_buf is not None else 0,

@@ -232,7 +232,8 @@ int emb_backward_dedup(emb_ctx* ctx, const void* indices, const void* offsets, i
  * filled), else it is reduced from dY inside the update kernel (fused
  * path, no materialised gradient). Rows no lookup touched are not read or
  * written. EMB_E_STATE if ws is not the workspace of this context's last
- * backward; EMB_E_INVAL for Adagrad on tables without state. */
+ * backward; EMB_E_INVAL for Adagrad on tables without state, for a NULL
+ * dY on the fused path, or for dY / reduced_grad not 16-byte aligned. */
 int emb_sparse_update(emb_ctx* ctx, int32_t opt, float lr, float eps,
                       const void* ws, const float* dY, const float* reduced_grad,
                       void* hip_stream);
