@@ -140,7 +140,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SRC == 2 ? 
       for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
     };
 
+    // SRC 0 / 1: the run's row indices are read LPR at a time, one per lane
+    // of the subgroup, validated there, and handed out by lane shuffles, so
+    // a row load waits on one round trip instead of an index load and then
+    // its own. kNoRow marks an index outside the table (it adds nothing).
+    // (Subgroups of fewer than U lanes read each index in every lane.)
+    constexpr uint32_t kNoRow = 0xffffffffu;
+    constexpr bool kLaneIdx = SRC != 2 && LPR >= U;
+    uint32_t myrow = kNoRow;
+    int blk_end = P0;  // lookups [P0, blk_end) have had their indices read
     for (int p = P0; p < P1; p += U) {
+      if constexpr (kLaneIdx) {
+        if (p >= blk_end) {  // uniform over the subgroup
+          const int q = p + lsg;
+          myrow = kNoRow;
+          if (q < P1) {
+            long long r;
+            if constexpr (SRC == 1) r = reinterpret_cast<const int32_t*>(a.indices)[q];
+            else r = ld_idx<IDX>(a.indices, q);
+            if (r >= 0 && r < rows_t) myrow = (uint32_t)r;
+            else bad = 1;
+          }
+          blk_end = p + LPR;
+        }
+      }
       // SRC 2: the U lookups' map probes are issued together -- ids, then the
       // home slots' keys, then the rows of the hits -- and only an id not in
       // its home slot walks the probe sequence
@@ -172,22 +195,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SRC == 2 ? 
 #pragma unroll
       for (int k = 0; k < U; ++k) {
         v[k] = u4{0u, 0u, 0u, 0u};
-        if (p + k < P1) {
-          // SRC 1 reads the dedup's int32 inverse, SRC 2 int64 ids; offsets
-          // keep the caller's type
-          long long r;
-          if constexpr (SRC == 1) {
-            r = reinterpret_cast<const int32_t*>(a.indices)[p + k];
-          } else if constexpr (SRC == 2) {
-            r = hr[k];
-          } else {
-            r = ld_idx<IDX>(a.indices, p + k);
+        if constexpr (SRC == 2) {
+          const long long r = hr[k];
+          if (p + k < P1 && r >= 0 && r < rows_t && act)
+            v[k] = *reinterpret_cast<const u4*>(wbase + (size_t)r * rstride);
+        } else if constexpr (!kLaneIdx) {
+          if (p + k < P1) {
+            long long r;
+            if constexpr (SRC == 1) r = reinterpret_cast<const int32_t*>(a.indices)[p + k];
+            else r = ld_idx<IDX>(a.indices, p + k);
+            if (r >= 0 && r < rows_t) {
+              if (act) v[k] = *reinterpret_cast<const u4*>(wbase + (size_t)r * rstride);
+            } else {
+              bad = 1;
+            }
           }
-          if (r >= 0 && r < rows_t) {
-            if (act) v[k] = *reinterpret_cast<const u4*>(wbase + (size_t)r * rstride);
-          } else if constexpr (SRC != 2) {
-            bad = 1;
-          }
+        } else {
+          // lookup p + k's row sits in lane (p + k - first of its block); U
+          // divides LPR, so a group never straddles two blocks
+          const uint32_t r = (uint32_t)__shfl((int)myrow, (p + k - (blk_end - LPR)) & (LPR - 1), LPR);
+          if (p + k < P1 && r != kNoRow && act)
+            v[k] = *reinterpret_cast<const u4*>(wbase + (size_t)r * rstride);
         }
       }
 #pragma unroll
@@ -213,7 +241,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SRC == 2 ? 
       cur_start = cur_end;
       cur_end = __shfl(my_off, min(cur + 1, nb), LPR);
     }
-    if (bad && lsg == 0) atomicOr(a.err, 1);
+    if (bad) atomicOr(a.err, 1);
   }
 }
 
