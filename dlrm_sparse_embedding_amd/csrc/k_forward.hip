@@ -58,10 +58,13 @@ struct FwdArgs {
 // SRC: 0 = rows of the tables by index, 1 = compact unique rows by inverse,
 // 2 = rows of the tables by hashed id (lookup only: the HugeCTR embedding
 // layer's hash table lookup fused with the pooling).
-// The hashed source keeps the probes of 4 lookups in flight too and needs
-// more registers: it runs at 6 waves/SIMD instead of 8.
+// The hashed source needs more registers where a lane probes for 4 lookups
+// (subgroups of 2 lanes) or widens 16-bit rows: 6 waves/SIMD there (no
+// spills), 8 everywhere else.
 template <int DT, typename IDX, int LPR, int SRC>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SRC == 2 ? 6 : 8, SRC == 2 ? 6 : 8))) void k_forward(FwdArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
+    SRC == 2 && (LPR < 4 || DT != EMB_F32) ? 6 : 8, SRC == 2 && (LPR < 4 || DT != EMB_F32) ? 6 : 8))) void
+k_forward(FwdArgs a) {
   constexpr int CPL = 16 / Stor<DT>::kBytes;  // columns per lane
   constexpr int SGW = 256 / LPR;              // subgroups per block
   constexpr int U = 4;                        // rows in flight per subgroup
@@ -144,9 +147,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SRC == 2 ? 
     // of the subgroup, validated there, and handed out by lane shuffles, so
     // a row load waits on one round trip instead of an index load and then
     // its own. kNoRow marks an index outside the table (it adds nothing).
-    // (Subgroups of fewer than U lanes read each index in every lane.)
+    // SRC 2 does the same with the ids: each lane probes the map for its own
+    // lookup (home slot, then the probe sequence on a miss) and holds the
+    // row, so the subgroup's probes run side by side. (Subgroups of fewer
+    // than U lanes read each index in every lane.)
     constexpr uint32_t kNoRow = 0xffffffffu;
-    constexpr bool kLaneIdx = SRC != 2 && LPR >= U;
+    constexpr bool kLaneIdx = LPR >= U;
     uint32_t myrow = kNoRow;
     int blk_end = P0;  // lookups [P0, blk_end) have had their indices read
     for (int p = P0; p < P1; p += U) {
@@ -155,11 +161,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SRC == 2 ? 
           const int q = p + lsg;
           myrow = kNoRow;
           if (q < P1) {
-            long long r;
-            if constexpr (SRC == 1) r = reinterpret_cast<const int32_t*>(a.indices)[q];
-            else r = ld_idx<IDX>(a.indices, q);
-            if (r >= 0 && r < rows_t) myrow = (uint32_t)r;
-            else bad = 1;
+            if constexpr (SRC == 2) {
+              const long long id = reinterpret_cast<const long long*>(a.indices)[q];
+              if (id != kEmpty) {  // an id without a row pools to nothing
+                const long long s0 = hm.base + (uint32_t)(mix64((uint64_t)id) & hm.mask);
+                const long long k0 = (long long)a.hkeys[s0];
+                long long r = -1;
+                if (k0 == id) {
+                  r = a.hvals[s0];
+                } else if (k0 != kEmpty) {
+                  const long long slot = find_slot(hm, a.hkeys, id, false);
+                  if (slot >= 0) r = a.hvals[slot];
+                }
+                if (r >= 0 && r < rows_t) myrow = (uint32_t)r;
+              }
+            } else {
+              long long r;
+              if constexpr (SRC == 1) r = reinterpret_cast<const int32_t*>(a.indices)[q];
+              else r = ld_idx<IDX>(a.indices, q);
+              if (r >= 0 && r < rows_t) myrow = (uint32_t)r;
+              else bad = 1;
+            }
           }
           blk_end = p + LPR;
         }
@@ -168,7 +190,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SRC == 2 ? 
       // home slots' keys, then the rows of the hits -- and only an id not in
       // its home slot walks the probe sequence
       long long hr[U];
-      if constexpr (SRC == 2) {
+      if constexpr (SRC == 2 && !kLaneIdx) {
         long long id[U];
         unsigned long long k0[U];
         long long s0[U];
@@ -195,7 +217,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SRC == 2 ? 
 #pragma unroll
       for (int k = 0; k < U; ++k) {
         v[k] = u4{0u, 0u, 0u, 0u};
-        if constexpr (SRC == 2) {
+        if constexpr (SRC == 2 && !kLaneIdx) {
           const long long r = hr[k];
           if (p + k < P1 && r >= 0 && r < rows_t && act)
             v[k] = *reinterpret_cast<const u4*>(wbase + (size_t)r * rstride);
