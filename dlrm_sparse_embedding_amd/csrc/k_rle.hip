@@ -67,15 +67,20 @@ __global__ __launch_bounds__(256) void k_rle_scan(u4* __restrict__ blk, int nblk
                                                   int32_t* __restrict__ num_chunks) {
   __shared__ uint32_t lds[8];
   __shared__ uint32_t s_max[4];
+  // thread t owns tiles [t*per, (t+1)*per), read 8 at a time
   const int per = (nblk + 255) / 256;
   const int b0 = threadIdx.x * per;
+  const int b1 = min(b0 + per, nblk);
   uint32_t ss = 0, sc = 0, sm = 0;
-  for (int i = 0; i < per; ++i) {
-    if (b0 + i < nblk) {
-      const u4 v = blk[b0 + i];
-      ss += v.x;
-      sc += v.y;
-      sm = max(sm, v.z);
+  for (int i0 = b0; i0 < b1; i0 += 8) {
+    u4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = i0 + k < b1 ? blk[i0 + k] : u4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      ss += v[k].x;
+      sc += v[k].y;
+      sm = max(sm, v[k].z);
     }
   }
   uint32_t ts, tc;
@@ -90,13 +95,16 @@ __global__ __launch_bounds__(256) void k_rle_scan(u4* __restrict__ blk, int nblk
   if (lane == 63) s_max[wave] = incl;
   __syncthreads();
   for (int w = 0; w < wave; ++w) pm = max(pm, s_max[w]);
-  for (int i = 0; i < per; ++i) {
-    if (b0 + i < nblk) {
-      const u4 v = blk[b0 + i];
-      blk[b0 + i] = u4{ps, pc, pm, 0u};
-      ps += v.x;
-      pc += v.y;
-      pm = max(pm, v.z);
+  for (int i0 = b0; i0 < b1; i0 += 8) {
+    u4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = i0 + k < b1 ? blk[i0 + k] : u4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (i0 + k < b1) blk[i0 + k] = u4{ps, pc, pm, 0u};
+      ps += v[k].x;
+      pc += v[k].y;
+      pm = max(pm, v[k].z);
     }
   }
   if (threadIdx.x == 0) {
