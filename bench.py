@@ -404,8 +404,12 @@ def main() -> int:
         "atomic": B * T * D * 4 + Navg * D * 4 * 2 + Navg * 4,
     }
     # the kernel family with the most time per step among those the roofline
-    # has a byte count for (on the real workloads: the fused update)
-    dominant = max((k for k in ktot if k in per_launch and ktot[k] > 0), key=lambda k: ktot[k])
+    # has a byte count for (on the real workloads: the fused update). When the
+    # dedup runs on the second stream (pipeline, overlap) only the main
+    # stream's kernels are ranked: a side-stream launch's duration includes
+    # the time it waits for wave slots beside the main stream's kernels.
+    side = {"keys", "sort_hist", "sort_scan", "sort_scatter", "rle"} if args.schedule != "serial" else set()
+    dominant = max((k for k in ktot if k in per_launch and ktot[k] > 0 and k not in side), key=lambda k: ktot[k])
     alg = per_launch.get(dominant)
 
     def roofline_of(avg_us):

@@ -43,5 +43,9 @@ def test_json_line_fields():
     r = d["roofline"]
     assert r["bound"] == "hbm" and r["peak"] == 8000.0 and r["unit"] == "GB/s"
     assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
+    # the default (pipelined) schedule runs the dedup on a second stream: the
+    # roofline kernel is a main-stream one
+    assert d["schedule"] == "pipeline"
+    assert r["kernel"] not in ("keys", "sort_hist", "sort_scan", "sort_scatter", "rle")
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["cores"] == 1 and c["value"] > 0 and c["unit"] == d["unit"]
