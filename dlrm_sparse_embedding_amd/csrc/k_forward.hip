@@ -16,7 +16,8 @@
 // flat stream of lookups, issuing U = 4 row loads before consuming them, so
 // one-hot bags (one row per bag) still keep 4 rows per subgroup in flight.
 // The run's bag boundaries (bps+1 offsets) sit one per lane and are read by
-// lane shuffles (ds_bpermute), not by dependent global loads. Pooled rows
+// lane shuffles (ds_bpermute), not by dependent global loads; so do its row
+// indices, LPR at a time, so that a row load waits on one round trip. Pooled rows
 // are written with non-temporal stores so the L2 keeps Zipf-hot table rows.
 // The grid may be capped (grid-stride over the work) so that the dedup, run
 // on a second stream, keeps some wave slots while the forward streams.

@@ -20,14 +20,19 @@
 //
 // Work split. Segments are cut into chunks (at segment starts and every
 // kChunk sorted positions). One subgroup of LPR lanes (4 fp32 columns per
-// lane, so a dY row is one coalesced access) reduces one chunk, keeping 6 dY
-// rows in flight; a chunk that is a whole segment applies the optimizer
-// right there with the weight (and state) row prefetched before the dY loop,
-// so the reduced gradient never leaves VGPRs. A segment longer than a tile
-// leaves one partial per tile it touches (at most two partial slots per
-// tile), and the combine kernel adds them in tile order -- a fixed order, so
-// results are bit-reproducible run to run -- with the whole block, then
-// applies the update. No atomics touch gradients or weights.
+// lane, so a dY row is one coalesced access; rows wider than a wave's 256
+// columns take two column blocks on the grid's y axis) reduces one chunk,
+// keeping 4 to 6 dY rows in flight (as many as fit 64 VGPRs without spills).
+// On multi-hot batches a run of equal bags inside a segment loads its dY row
+// once and adds it with its multiplicity. A chunk that is a whole segment
+// applies the optimizer right there, with the weight (and state) row
+// prefetched before the dY loop, so the reduced gradient never leaves VGPRs.
+// A segment longer than a tile leaves one partial per kChunk-tile it touches
+// (at most two partial slots per tile). k_level1 adds them per kChunk1-tile,
+// and k_combine adds what the segment needs (level-0 partials inside one
+// kChunk1-tile, else the level-1 ones) in tile order -- a fixed order, so
+// results are bit-reproducible run to run -- and applies the update. No
+// atomics touch gradients or weights.
 #include "emb_device.h"
 
 namespace emb {
