@@ -208,8 +208,9 @@ WsLayout ws_layout(const Geom& g, long long N, int B) {
   const long long TB = (long long)g.T * B;
   L.ntiles = (int)((N + kChunk - 1) / kChunk);
   L.ntiles1 = (int)((N + kChunk1 - 1) / kChunk1);
-  L.nblk_sort = (int)((N + kSortTile - 1) / kSortTile);
-  L.nblk_rle = L.nblk_sort;
+  const SortPlan sp = sort_plan_dedup(g, N);
+  L.nblk_sort = sp.nblk;
+  L.nblk_rle = (int)((N + kSortTile - 1) / kSortTile);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -219,6 +220,7 @@ WsLayout ws_layout(const Geom& g, long long N, int B) {
   L.keys_a = take(8ull * N);
   L.keys_b = take(8ull * N);
   L.bag_of_pos = take(4ull * N);
+  L.unit_grp = take(4ull * ((TB + 63) / 64 + 1));
   L.sorted_bag = take(4ull * N);
   L.inv_len = take(4ull * (TB > 0 ? TB : 1));
   L.seg_off = take(4ull * (N + 1));
@@ -228,8 +230,14 @@ WsLayout ws_layout(const Geom& g, long long N, int B) {
   L.tile_last_seg = take(4ull * (L.ntiles > 0 ? L.ntiles : 1));
   L.partial0 = take(4ull * 2 * (L.ntiles > 0 ? L.ntiles : 1) * g.D);
   L.partial1 = take(4ull * 2 * (L.ntiles1 > 0 ? L.ntiles1 : 1) * g.D);
-  L.ghist = take(4ull * kRadixMax * (L.nblk_sort > 0 ? L.nblk_sort : 1));
-  L.digit_tot = take(4ull * kRadixMax);
+  L.seg_start = take(4ull * g.T);
+  // sized for the widest digit, so that any plan over these N words fits:
+  // the dedup's, and the shard-routing sort's (a global plan over the same N
+  // with digits up to kRadixMaxBits wide)
+  L.ghist_cap = (size_t)L.nblk_sort << kRadixMaxBits;
+  L.segbase_cap = (size_t)(sp.S + 1) << kRadixMaxBits;
+  L.ghist = take(4ull * L.ghist_cap);
+  L.segbase = take(4ull * L.segbase_cap);
   L.rle_blk = take(16ull * (L.nblk_rle > 0 ? L.nblk_rle : 1));
   L.scalars = take(64);
   L.total = off;
@@ -309,6 +317,11 @@ int emb_create_tables(const emb_table_desc* descs, int32_t num_tables, emb_ctx**
     int bits = 1;
     while (bits < 32 && (1ull << bits) <= (uint64_t)sum) ++bits;
     c->g.key_bits = bits;  // keys 0..sum (sum = invalid-index sentinel)
+    int64_t max_rows = 0;
+    for (int t = 0; t < num_tables; ++t) max_rows = std::max<int64_t>(max_rows, descs[t].rows);
+    int rbits = 1;
+    while (rbits < 32 && (1ull << rbits) <= (uint64_t)max_rows) ++rbits;
+    c->g.row_bits = rbits;  // rows 0..max_rows (max_rows = a key outside its table)
     c->has_state = state0;
     *out = c;
     return ok();
@@ -444,6 +457,31 @@ int check_dedup_args(emb_ctx* ctx, const void* indices, const void* offsets, int
   return EMB_OK;
 }
 
+// The passes of one radix sort of the words in *a (*b: scratch of the same
+// size); on return *a holds the sorted words.
+int run_sort(emb_ctx* ctx, const SortPlan& sp, const SortBufs& sb, uint64_t** a, uint64_t** b, int N,
+             hipStream_t st) {
+  if (((size_t)sp.nblk << sp.rb) > sb.ghist_cap || ((size_t)(sp.S + 1) << sp.rb) > sb.segbase_cap)
+    return fail(EMB_E_INVAL, "internal: radix sort plan exceeds its workspace buffers");
+  hipError_t e;
+  for (int shift = 0; shift < sp.bits; shift += sp.rb) {
+    {
+      KScope ks(ctx, EMB_K_SORT_HIST, st);
+      if ((e = launch_sort_hist(sp, sb, *a, N, shift, st)) != hipSuccess) return hip_fail(e, "sort histogram");
+    }
+    {
+      KScope ks(ctx, EMB_K_SORT_SCAN, st);
+      if ((e = launch_sort_scan(sp, sb, N, st)) != hipSuccess) return hip_fail(e, "sort scan");
+    }
+    {
+      KScope ks(ctx, EMB_K_SORT_SCATTER, st);
+      if ((e = launch_sort_scatter(sp, sb, *a, *b, N, shift, st)) != hipSuccess) return hip_fail(e, "sort scatter");
+    }
+    std::swap(*a, *b);
+  }
+  return EMB_OK;
+}
+
 // Keys -> radix sort -> run-length encoding, on `st`.
 int run_dedup(emb_ctx* ctx, const void* indices, const void* offsets, int32_t itype, int64_t N, int32_t B,
               int32_t pool, char* w, const WsLayout& L, uint32_t* unique_keys, int32_t* counts,
@@ -462,32 +500,17 @@ int run_dedup(emb_ctx* ctx, const void* indices, const void* offsets, int32_t it
   }
   uint64_t* a = reinterpret_cast<uint64_t*>(w + L.keys_a);
   uint64_t* b = reinterpret_cast<uint64_t*>(w + L.keys_b);
-  uint32_t* ghist = reinterpret_cast<uint32_t*>(w + L.ghist);
-  uint32_t* dtot = reinterpret_cast<uint32_t*>(w + L.digit_tot);
-  const int rb = radix_bits_for(ctx->g.key_bits);
-  for (int shift = 0; shift < ctx->g.key_bits; shift += rb) {
-    {
-      KScope ks(ctx, EMB_K_SORT_HIST, st);
-      if ((e = launch_sort_hist(rb, a, (int)N, shift, ghist, L.nblk_sort, st)) != hipSuccess)
-        return hip_fail(e, "sort histogram");
-    }
-    {
-      KScope ks(ctx, EMB_K_SORT_SCAN, st);
-      if ((e = launch_sort_scan(rb, ghist, L.nblk_sort, dtot, st)) != hipSuccess) return hip_fail(e, "sort scan");
-    }
-    {
-      KScope ks(ctx, EMB_K_SORT_SCATTER, st);
-      if ((e = launch_sort_scatter(rb, a, b, (int)N, shift, ghist, dtot, L.nblk_sort, st)) != hipSuccess)
-        return hip_fail(e, "sort scatter");
-    }
-    uint64_t* tmp = a;
-    a = b;
-    b = tmp;
-  }
+  const SortPlan sp = sort_plan_dedup(ctx->g, N);
+  const SortBufs sb{reinterpret_cast<uint32_t*>(w + L.ghist), reinterpret_cast<uint32_t*>(w + L.segbase),
+                    reinterpret_cast<const int32_t*>(w + L.seg_start), ctx->dc.row_off, L.ghist_cap,
+                    L.segbase_cap};
+  if (int rc = run_sort(ctx, sp, sb, &a, &b, (int)N, st)) return rc;
   {
     KScope ks(ctx, EMB_K_RLE, st);
     RleOut o{unique_keys, counts, inverse, num_unique};
-    if ((e = launch_rle(a, (int)N, L, w, o, st)) != hipSuccess) return hip_fail(e, "run-length encode");
+    const long long TB = (long long)ctx->g.T * B;
+    const int ngrp = N == TB ? (int)((TB + 63) / 64) : 0;
+    if ((e = launch_rle(a, (int)N, ngrp, L, w, o, st)) != hipSuccess) return hip_fail(e, "run-length encode");
   }
   return EMB_OK;
 }
@@ -864,28 +887,10 @@ int emb_pack_by_shard(emb_ctx* ctx, void* ws, const float* dY, uint32_t* send_ke
     // destinations 0..S (S = sent nowhere), sorted stably
     int bits = 1;
     while ((1 << bits) <= S) ++bits;
-    const int rb = radix_bits_for(bits);
-    uint32_t* ghist = reinterpret_cast<uint32_t*>(w + L.ghist);
-    uint32_t* dtot = reinterpret_cast<uint32_t*>(w + L.digit_tot);
-    for (int shift = 0; shift < bits; shift += rb) {
-      {
-        KScope ks(ctx, EMB_K_SORT_HIST, st);
-        if ((e = launch_sort_hist(rb, a, (int)N, shift, ghist, L.nblk_sort, st)) != hipSuccess)
-          return hip_fail(e, "pack sort histogram");
-      }
-      {
-        KScope ks(ctx, EMB_K_SORT_SCAN, st);
-        if ((e = launch_sort_scan(rb, ghist, L.nblk_sort, dtot, st)) != hipSuccess) return hip_fail(e, "pack sort scan");
-      }
-      {
-        KScope ks(ctx, EMB_K_SORT_SCATTER, st);
-        if ((e = launch_sort_scatter(rb, a, b, (int)N, shift, ghist, dtot, L.nblk_sort, st)) != hipSuccess)
-          return hip_fail(e, "pack sort scatter");
-      }
-      uint64_t* tmp = a;
-      a = b;
-      b = tmp;
-    }
+    const SortPlan sp = sort_plan_global(bits, N);
+    const SortBufs sb{reinterpret_cast<uint32_t*>(w + L.ghist), reinterpret_cast<uint32_t*>(w + L.segbase),
+                      nullptr, ctx->dc.row_off, L.ghist_cap, L.segbase_cap};
+    if (int rc = run_sort(ctx, sp, sb, &a, &b, (int)N, st)) return rc;
     {
       KScope ks(ctx, EMB_K_PACK, st);
       if ((e = launch_pack_place(a, ctx->last.unique_keys, ctx->last.num_unique, (int)N, S, send_keys,

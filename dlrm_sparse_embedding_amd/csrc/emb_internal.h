@@ -70,8 +70,11 @@ constexpr int kFwdBlocksPerCU = 0;
 constexpr int kSortThreads = 256;
 constexpr int kSortIPT = 8;
 constexpr int kSortTile = kSortThreads * kSortIPT;  // 2048 items
-constexpr int kRadixMaxBits = 9;
+constexpr int kRadixMaxBits = 10;
 constexpr int kRadixMax = 1 << kRadixMaxBits;
+// The table-segmented sort handles at most this many tables (every block
+// rebuilds the segment map in LDS).
+constexpr int kSegMaxTables = 256;
 
 inline int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 inline int next_pow2(int x) {
@@ -93,6 +96,8 @@ struct Geom {
   bool master;    // fp32 master weights present (low-precision storage only)
   uint32_t total_rows;
   int key_bits;   // bits needed for keys 0..total_rows (total_rows = invalid-index sentinel)
+  int row_bits;   // bits needed for rows 0..max_rows (max over tables; max_rows itself
+                  // stands for a key outside the table in the table-segmented sort)
 };
 
 // Device-side context block.
@@ -106,6 +111,7 @@ struct DevCtx {
 struct WsLayout {
   size_t keys_a, keys_b;        // uint64 [N] (key << 32 | position), ping-pong
   size_t bag_of_pos;            // int32 [N]
+  size_t unit_grp;              // int32 [ceil(T*B/64)] 1 if each of a key-build group's 64 bags is [b, b+1)
   size_t sorted_bag;            // int32 [N] bag of each sorted lookup
   size_t inv_len;               // fp32 [T*B] 1/L per bag (mean pooling)
   size_t seg_off;               // int32 [N+1]
@@ -115,8 +121,10 @@ struct WsLayout {
   size_t tile_last_seg;         // int32 [ntiles] segment of a tile's last position
   size_t partial0;              // fp32 [2*ntiles][D]
   size_t partial1;              // fp32 [2*ntiles1][D]
-  size_t ghist;                 // uint32 [digits][nblk_sort]
-  size_t digit_tot;             // uint32 [digits]
+  size_t seg_start;             // int32 [T] first position of each table's bags
+  size_t ghist;                 // uint32 [digits][nblk] of a sort plan (ghist_cap entries)
+  size_t segbase;               // uint32 [S+1][digits] (segbase_cap entries)
+  size_t ghist_cap, segbase_cap;
   size_t rle_blk;               // uint32x4 [nblk_rle]
   size_t scalars;               // int32 [16]: [0] num_chunks
   size_t total;
@@ -146,14 +154,31 @@ hipError_t launch_keys(const Geom& g, const DevCtx& dc, const void* indices, con
                        int itype, long long N, int B, int pool, const WsLayout& L, char* ws,
                        hipStream_t st);
 
-// radix sort pass kernels; rb = digit bits (8 or 9, radix_bits_for(key_bits))
-int radix_bits_for(int key_bits);
-hipError_t launch_sort_hist(int rb, const uint64_t* keys, int N, int shift, uint32_t* ghist,
-                            int nblk, hipStream_t st);
-hipError_t launch_sort_scan(int rb, uint32_t* ghist, int nblk, uint32_t* digit_tot, hipStream_t st);
-hipError_t launch_sort_scatter(int rb, const uint64_t* in, uint64_t* out, int N, int shift,
-                               const uint32_t* ghist, const uint32_t* digit_tot, int nblk,
-                               hipStream_t st);
+// One stable LSD radix sort of N (key << 32 | position) words: passes over
+// shift = 0, rb, 2*rb, ... < bits, each = hist, scan, scatter.
+struct SortPlan {
+  bool seg;    // table-segmented: each table's positions sorted on its row bits
+  int bits;    // bits sorted (key bits, or row bits when seg)
+  int passes;
+  int rb;      // digit bits, 8..kRadixMaxBits
+  int S;       // segments (T when seg, else 1)
+  int nblk;    // tiles of the hist / scatter grids (multiple of 8)
+};
+SortPlan sort_plan_global(int bits, long long N);
+SortPlan sort_plan_dedup(const Geom& g, long long N);
+struct SortBufs {
+  uint32_t* ghist;            // nblk << rb entries used
+  uint32_t* segbase;          // (S + 1) << rb entries used
+  const int32_t* seg_start;   // [T] (table-segmented plans)
+  const uint32_t* row_off;    // [T+1]
+  size_t ghist_cap;           // entries of ghist and segbase
+  size_t segbase_cap;
+};
+hipError_t launch_sort_hist(const SortPlan& p, const SortBufs& b, const uint64_t* keys, int N, int shift,
+                            hipStream_t st);
+hipError_t launch_sort_scan(const SortPlan& p, const SortBufs& b, int N, hipStream_t st);
+hipError_t launch_sort_scatter(const SortPlan& p, const SortBufs& b, const uint64_t* in, uint64_t* out, int N,
+                               int shift, hipStream_t st);
 
 struct RleOut {
   uint32_t* unique_keys;
@@ -161,7 +186,9 @@ struct RleOut {
   int32_t* inverse;
   int32_t* num_unique;
 };
-hipError_t launch_rle(const uint64_t* sorted, int N, const WsLayout& L, char* ws, const RleOut& o,
+// ngrp: key-build groups whose one-lookup-per-bag flags decide whether the
+// bag of position p is p itself (0 when N != T*B: never).
+hipError_t launch_rle(const uint64_t* sorted, int N, int ngrp, const WsLayout& L, char* ws, const RleOut& o,
                       hipStream_t st);
 hipError_t launch_set_empty(const WsLayout& L, char* ws, int32_t* num_unique, hipStream_t st);
 

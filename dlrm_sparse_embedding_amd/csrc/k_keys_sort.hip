@@ -5,18 +5,33 @@
 // article, section on embedding clusters) applied to one GPU's share: before
 // any gradient is reduced or a row is written, the step's lookups are grouped
 // by global key g = row_offset[t] + idx. Here the grouping is a sort: each
-// lookup i becomes the 64-bit word (g << 32 | i), and an LSD radix sort over
-// the low key_bits bits of g orders the words by key, with
-// positions ascending inside a key because every pass is stable.
+// lookup i becomes the 64-bit word (g << 32 | i), and an LSD radix sort
+// orders the words by key, with positions ascending inside a key because
+// every pass is stable.
 //
-// Digits are 8 bits, or 9 when that saves a pass (27-bit keys: 3 passes, not 4).
+// The sort runs over segments of positions, each sorted on its own:
+//   global     one segment [0, N), digits of the key itself (key_bits bits);
+//   by table   the lookups are table-major, so table t's positions already
+//              form one contiguous segment and every key in it lies in
+//              [row_offset[t], row_offset[t+1]): sorting each segment on the
+//              row bits (key - row_offset[t]) gives the same order as the
+//              global sort with fewer bits (100 tables of 1M rows: 20 bits
+//              in 2 passes instead of 27 bits in 3).
+// Digits are 8 to 10 bits, as few passes as 10-bit digits allow (wider
+// digits cost more per pass than the pass they save: more counters per tile
+// to write and scan, shorter runs to scatter).
 // Sort pass = three kernels:
 //   hist    per 2048-item tile, count digits in LDS -> ghist[digit][tile]
-//   scan    one block per digit: exclusive scan of its row over tiles
+//           (tiles never straddle segments; consecutive tiles run on one
+//           XCD, so their counts share cache lines in one L2, and so do the
+//           runs that neighbouring tiles scatter to one digit's range)
+//   scan    one block per digit: exclusive scan of its row over tiles, plus
+//           the value at each segment's first tile (segbase)
 //   scatter per tile: rank every item among equal digits (wave ballots give
 //           the lanes holding the same digit; per-wave LDS counters carry the
 //           rank across the tile's items in order), stage the tile in LDS in
-//           digit order, then write runs of equal digits contiguously.
+//           digit order, then write runs of equal digits contiguously to
+//           segment start + digits below + this digit's tiles before.
 // The tile is striped per wave (item k of lane l of wave w sits at
 // w*512 + k*64 + l), which is the order the ranking visits, so ranks are
 // stable.
@@ -35,6 +50,8 @@ struct KeysArgs {
   uint64_t* keys;
   int32_t* bag_of_pos;
   float* inv_len;  // null unless mean pooling
+  int32_t* seg_start;  // [T] first position of each table's bags (clamped offsets[t*B])
+  int32_t* unit_grp;   // [groups] 1 if every bag of the group is [b, b+1) (its one lookup is position b)
   int* err;
   long long N;
   int T, B;
@@ -75,6 +92,12 @@ __global__ __launch_bounds__(256) void k_keys(KeysArgs a) {
     ro = a.row_off[t];
     rows = a.row_off[t + 1] - ro;
     if (a.inv_len) a.inv_len[bag] = e > s ? __fdiv_rn(1.0f, (float)(e - s)) : 0.f;
+    if (bag - (long long)t * a.B == 0) a.seg_start[t] = s;
+  }
+  {
+    const bool unit = bag >= nbags || (s == bag && nxt == bag + 1);
+    const uint64_t bu = __ballot(unit);
+    if (lane == 0) a.unit_grp[g0 / 64] = bu == ~0ull ? 1 : 0;
   }
   const int lo = g0 == 0 ? 0 : __shfl(s, 0);
   const int hi = g0 + 64 < nbags ? __shfl(nxt, 63) : N;
@@ -117,6 +140,8 @@ hipError_t launch_keys(const Geom& g, const DevCtx& dc, const void* indices, con
   a.keys = reinterpret_cast<uint64_t*>(ws + L.keys_a);
   a.bag_of_pos = reinterpret_cast<int32_t*>(ws + L.bag_of_pos);
   a.inv_len = pool == EMB_POOL_MEAN ? reinterpret_cast<float*>(ws + L.inv_len) : nullptr;
+  a.seg_start = reinterpret_cast<int32_t*>(ws + L.seg_start);
+  a.unit_grp = reinterpret_cast<int32_t*>(ws + L.unit_grp);
   a.err = dc.err_flag;
   a.N = N;
   a.T = g.T;
@@ -132,13 +157,113 @@ hipError_t launch_keys(const Geom& g, const DevCtx& dc, const void* indices, con
   return hipGetLastError();
 }
 
+
 // ---------------------------------------------------------------------------
 // radix sort
 // ---------------------------------------------------------------------------
 
+// Segment map of one sort, rebuilt in LDS by every block of the table-
+// segmented sort: segment t covers positions [sb[t], sb[t+1]) and tiles
+// [tf[t], tf[t+1]). sb is the running maximum of the clamped table starts
+// with sb[0] = 0 and sb[S] = N, so the segments partition [0, N) whatever the
+// offsets were (with offsets that break the CSR contract, a segment may hold
+// keys of another table; they take the largest row value, see local_of).
+struct SegLds {
+  int sb[kSegMaxTables + 1];
+  int tf[kSegMaxTables + 1];
+};
+
+struct SortKArgs {
+  const int32_t* seg_start;  // [S] (table-segmented) or null (one segment)
+  const uint32_t* row_off;   // [S+1] (table-segmented)
+  uint32_t* ghist;           // [R][nblk] per-tile digit counts, scanned in place
+  uint32_t* segbase;         // [S+1][R] scanned count at each segment's first tile
+  int S;                     // segments
+  int nblk;                  // tiles in the grid (multiple of 8)
+  int N;
+  uint32_t vmax;             // row value of a key outside its segment's table
+};
+
+// Builds the segment map (wave 0; every thread must call: barriers inside).
+__device__ void build_seg_map(const SortKArgs& a, SegLds& m) {
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x < 64) {
+    int carry = 0;
+    for (int c = 0; c <= a.S; c += 64) {
+      const int t = c + lane;
+      int v = a.N;
+      if (t == 0) v = 0;
+      else if (t < a.S) v = min(max(a.seg_start[t], 0), a.N);
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(v, d, 64);
+        if (lane >= d) v = max(v, y);
+      }
+      v = max(v, carry);
+      if (t <= a.S) m.sb[t] = v;
+      carry = __shfl(v, 63, 64);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    int carry = 0;
+    for (int c = 0; c < a.S; c += 64) {
+      const int t = c + lane;
+      const int n = t < a.S ? (m.sb[t + 1] - m.sb[t] + kSortTile - 1) / kSortTile : 0;
+      int x = n;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+      }
+      if (t < a.S) m.tf[t] = carry + x - n;
+      carry += __shfl(x, 63, 64);
+    }
+    if (lane == 0) m.tf[a.S] = carry;
+  }
+  __syncthreads();
+}
+
+// The tile a block works on: its segment and position range [lo, hi)
+// (empty past the last tile).
+struct TileRange {
+  int seg, lo, hi;
+};
+
+__device__ __forceinline__ TileRange tile_range(const SortKArgs& a, const SegLds& m, int k) {
+  TileRange r{0, a.N, a.N};
+  if (a.seg_start) {
+    if (k >= m.tf[a.S]) return r;
+    int lo = 0, hi = a.S;  // tf[lo] <= k < tf[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (m.tf[mid] <= k) lo = mid;
+      else hi = mid;
+    }
+    r.seg = lo;
+    r.lo = m.sb[lo] + (k - m.tf[lo]) * kSortTile;
+    r.hi = min(r.lo + kSortTile, m.sb[lo + 1]);
+  } else {
+    const long long s0 = (long long)k * kSortTile;
+    if (s0 < a.N) {
+      r.lo = (int)s0;
+      r.hi = (int)min(s0 + kSortTile, (long long)a.N);
+    }
+  }
+  return r;
+}
+
+// Value sorted for a word: its key (global sort), or its row within the
+// segment's table [lo, lo + span) -- a key outside that range (the invalid-
+// index sentinel) takes vmax, after every row of the table.
+__device__ __forceinline__ uint32_t local_of(uint64_t x, uint32_t lo, uint32_t span, uint32_t vmax) {
+  const uint32_t v = (uint32_t)(x >> 32) - lo;
+  return v < span ? v : vmax;
+}
+
 template <int RB>
-__device__ __forceinline__ uint32_t digit_of(uint64_t x, int shift) {
-  return (uint32_t)(x >> (32 + shift)) & ((1u << RB) - 1u);
+__device__ __forceinline__ uint32_t digit_of(uint32_t v, int shift) {
+  return (v >> shift) & ((1u << RB) - 1u);
 }
 
 // Mask of the wave's lanes that are valid and hold the same RB-bit digit as
@@ -174,42 +299,73 @@ __device__ __forceinline__ void block_excl_scan_digits(const uint32_t* in, uint3
   }
 }
 
+// Block of tile k: consecutive tiles on one XCD (a.nblk % 8 == 0).
+__device__ __forceinline__ int sort_tile_of_block(const SortKArgs& a) {
+  return xcd_remap((int)blockIdx.x, a.nblk);
+}
+
+// Row range of the block's segment (the whole key range in the global sort).
+__device__ __forceinline__ void seg_rows(const SortKArgs& a, int seg, uint32_t* lo, uint32_t* span) {
+  if (a.seg_start) {
+    *lo = a.row_off[seg];
+    *span = a.row_off[seg + 1] - *lo;
+  } else {
+    *lo = 0;
+    *span = 0xffffffffu;
+  }
+}
+
 template <int RB>
-__global__ __launch_bounds__(256) void k_sort_hist(const uint64_t* __restrict__ keys, int N,
-                                                   int shift, uint32_t* __restrict__ ghist,
-                                                   int nblk) {
+__global__ __launch_bounds__(256) void k_sort_hist(const uint64_t* __restrict__ keys, int shift, SortKArgs a) {
   constexpr int R = 1 << RB;
   __shared__ uint32_t h[R];
+  __shared__ SegLds m;
   for (int d = threadIdx.x; d < R; d += 256) h[d] = 0;
+  if (a.seg_start) build_seg_map(a, m);
+  const int k = sort_tile_of_block(a);
+  const TileRange r = tile_range(a, m, k);
+  uint32_t lo = 0, span = 0;
+  if (r.lo < r.hi) seg_rows(a, r.seg, &lo, &span);
   __syncthreads();
-  const long long base = (long long)blockIdx.x * kSortTile;
   // equal digits of a wave are counted by one LDS add from their first lane:
   // skewed keys put many lanes on one bin, which would serialise per-lane adds
   const uint64_t lt = lanemask_lt();
 #pragma unroll
-  for (int k = 0; k < kSortIPT; ++k) {
-    const long long i = base + k * 256 + threadIdx.x;
-    const bool valid = i < N;
-    const uint32_t d = valid ? digit_of<RB>(keys[i], shift) : 0u;
+  for (int j = 0; j < kSortIPT; ++j) {
+    const int i = r.lo + j * 256 + threadIdx.x;
+    const bool valid = i < r.hi;
+    const uint32_t d = valid ? digit_of<RB>(local_of(keys[i], lo, span, a.vmax), shift) : 0u;
     const uint64_t peers = digit_peers<RB>(d, valid);
     if (valid && (peers & lt) == 0) atomicAdd(&h[d], (uint32_t)__popcll(peers));
   }
   __syncthreads();
-  for (int d = threadIdx.x; d < R; d += 256) ghist[(size_t)d * nblk + blockIdx.x] = h[d];
+  for (int d = threadIdx.x; d < R; d += 256) a.ghist[(size_t)d * a.nblk + k] = h[d];
 }
 
-__global__ __launch_bounds__(256) void k_sort_scan(uint32_t* __restrict__ ghist, int nblk,
-                                                   uint32_t* __restrict__ digit_tot) {
+// One block per digit.
+template <int RB>
+__global__ __launch_bounds__(256) void k_sort_scan(SortKArgs a) {
+  constexpr int R = 1 << RB;
   __shared__ uint32_t lds[8];
-  uint32_t* row = ghist + (size_t)blockIdx.x * nblk;
+  __shared__ SegLds m;
+  __shared__ uint32_t s_base[kSegMaxTables + 1];
+  const int d = (int)blockIdx.x;
+  uint32_t* row = a.ghist + (size_t)d * a.nblk;
+  if (a.seg_start) {
+    build_seg_map(a, m);
+  } else if (threadIdx.x == 0) {
+    m.tf[0] = 0;
+    m.tf[1] = a.nblk;
+  }
+  __syncthreads();
   uint32_t running = 0;
-  for (int base = 0; base < nblk; base += 256 * 4) {
+  for (int base = 0; base < a.nblk; base += 256 * 4) {
     uint32_t v[4];
     uint32_t sum = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int i = base + threadIdx.x * 4 + j;
-      v[j] = i < nblk ? row[i] : 0u;
+      v[j] = i < a.nblk ? row[i] : 0u;
       sum += v[j];
     }
     uint32_t tot;
@@ -217,70 +373,94 @@ __global__ __launch_bounds__(256) void k_sort_scan(uint32_t* __restrict__ ghist,
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int i = base + threadIdx.x * 4 + j;
-      if (i < nblk) row[i] = run;
+      if (i < a.nblk) {
+        row[i] = run;
+        // segments whose first tile is i (several when segments are empty)
+        int lo = 0, hi = a.S + 1;  // first t with tf[t] >= i
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (m.tf[mid] < i) lo = mid + 1;
+          else hi = mid;
+        }
+        for (int t = lo; t <= a.S && m.tf[t] == i; ++t) s_base[t] = run;
+      }
       run += v[j];
     }
     running += tot;
   }
-  if (threadIdx.x == 0) digit_tot[blockIdx.x] = running;
+  for (int t = threadIdx.x; t <= a.S; t += 256)
+    if (m.tf[t] >= a.nblk) s_base[t] = running;
+  __syncthreads();
+  for (int t = threadIdx.x; t <= a.S; t += 256) a.segbase[(size_t)t * R + d] = s_base[t];
 }
 
 template <int RB>
 __global__ __launch_bounds__(256) void k_sort_scatter(const uint64_t* __restrict__ in,
-                                                      uint64_t* __restrict__ out, int N, int shift,
-                                                      const uint32_t* __restrict__ ghist,
-                                                      const uint32_t* __restrict__ digit_tot,
-                                                      int nblk) {
+                                                      uint64_t* __restrict__ out, int shift,
+                                                      SortKArgs a) {
   constexpr int R = 1 << RB;
   constexpr int PER = R / 256;
   __shared__ uint32_t s_gbase[R];    // global start of this tile's digit-d run
-  __shared__ uint32_t s_wcnt[4][R];  // per-wave digit counters, then per-wave offsets
-  __shared__ uint32_t s_bexcl[R];    // tile-local start of digit d
+  __shared__ uint16_t s_wcnt[4][R];  // per-wave digit counters, then per-wave offsets
+  __shared__ uint16_t s_bexcl[R];    // tile-local start of digit d
   __shared__ uint64_t s_stage[kSortTile];
   __shared__ uint32_t s_scan[8];
+  __shared__ SegLds m;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int blk = blockIdx.x;
+  if (a.seg_start) build_seg_map(a, m);
+  const int k = sort_tile_of_block(a);
+  const TileRange r = tile_range(a, m, k);
+  if (r.lo >= r.hi) return;  // uniform over the block, after the map's barriers
+  uint32_t lo, span;
+  seg_rows(a, r.seg, &lo, &span);
+  const int sb = a.seg_start ? m.sb[r.seg] : 0;
 
   {
+    // digit d's run of this tile starts at: segment start + items of the
+    // segment with smaller digits + items of digit d in the segment's tiles
+    // before this one
+    const uint32_t* b0 = a.segbase + (size_t)r.seg * R;
+    const uint32_t* b1 = b0 + R;
+    const uint32_t* gh = a.ghist + k;
     uint32_t in_[PER], pre[PER];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) in_[j] = digit_tot[tid * PER + j];
+    for (int j = 0; j < PER; ++j) in_[j] = b1[tid * PER + j] - b0[tid * PER + j];
     block_excl_scan_digits<PER>(in_, pre, s_scan);
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-      const int d = tid * PER + j;
-      s_gbase[d] = pre[j] + ghist[(size_t)d * nblk + blk];
+      const int dd = tid * PER + j;
+      s_gbase[dd] = (uint32_t)sb + pre[j] + gh[(size_t)dd * a.nblk] - b0[dd];
     }
   }
 #pragma unroll
   for (int w = 0; w < 4; ++w)
-    for (int d = tid; d < R; d += 256) s_wcnt[w][d] = 0;
+    for (int dd = tid; dd < R; dd += 256) s_wcnt[w][dd] = 0;
   __syncthreads();
 
-  const long long base = (long long)blk * kSortTile + wave * (64 * kSortIPT);
+  const int base = r.lo + wave * (64 * kSortIPT);
   uint64_t item[kSortIPT];
   uint32_t rank[kSortIPT];
 #pragma unroll
-  for (int k = 0; k < kSortIPT; ++k) {
-    const long long i = base + k * 64 + lane;
-    item[k] = i < N ? in[i] : 0ull;
+  for (int j = 0; j < kSortIPT; ++j) {
+    const int i = base + j * 64 + lane;
+    item[j] = i < r.hi ? in[i] : 0ull;
   }
   const uint64_t lt = lanemask_lt();
 #pragma unroll
-  for (int k = 0; k < kSortIPT; ++k) {
-    const bool valid = base + k * 64 + lane < N;
-    const uint32_t d = digit_of<RB>(item[k], shift);
+  for (int j = 0; j < kSortIPT; ++j) {
+    const bool valid = base + j * 64 + lane < r.hi;
+    const uint32_t d = digit_of<RB>(local_of(item[j], lo, span, a.vmax), shift);
     const uint64_t peers = digit_peers<RB>(d, valid);
     const uint32_t before = (uint32_t)__popcll(peers & lt);
     uint32_t basev = 0;
     if (valid) basev = s_wcnt[wave][d];
-    rank[k] = basev + before;
+    rank[j] = basev + before;
     // every lane has read the counter (LDS ops of one wave complete in
     // order); the group's first lane now advances it
     __builtin_amdgcn_wave_barrier();
-    if (valid && before == 0) s_wcnt[wave][d] = basev + (uint32_t)__popcll(peers);
+    if (valid && before == 0) s_wcnt[wave][d] = (uint16_t)(basev + (uint32_t)__popcll(peers));
     __builtin_amdgcn_wave_barrier();
   }
   __syncthreads();
@@ -288,68 +468,107 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const uint64_t* __restrict
     uint32_t tot_[PER], pre[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-      const int d = tid * PER + j;
-      const uint32_t c0 = s_wcnt[0][d], c1 = s_wcnt[1][d], c2 = s_wcnt[2][d], c3 = s_wcnt[3][d];
-      s_wcnt[0][d] = 0;
-      s_wcnt[1][d] = c0;
-      s_wcnt[2][d] = c0 + c1;
-      s_wcnt[3][d] = c0 + c1 + c2;
+      const int dd = tid * PER + j;
+      const uint32_t c0 = s_wcnt[0][dd], c1 = s_wcnt[1][dd], c2 = s_wcnt[2][dd], c3 = s_wcnt[3][dd];
+      s_wcnt[0][dd] = 0;
+      s_wcnt[1][dd] = (uint16_t)c0;
+      s_wcnt[2][dd] = (uint16_t)(c0 + c1);
+      s_wcnt[3][dd] = (uint16_t)(c0 + c1 + c2);
       tot_[j] = c0 + c1 + c2 + c3;
     }
     block_excl_scan_digits<PER>(tot_, pre, s_scan);
 #pragma unroll
-    for (int j = 0; j < PER; ++j) s_bexcl[tid * PER + j] = pre[j];
+    for (int j = 0; j < PER; ++j) s_bexcl[tid * PER + j] = (uint16_t)pre[j];
   }
   __syncthreads();
 #pragma unroll
-  for (int k = 0; k < kSortIPT; ++k) {
-    const bool valid = base + k * 64 + lane < N;
+  for (int j = 0; j < kSortIPT; ++j) {
+    const bool valid = base + j * 64 + lane < r.hi;
     if (valid) {
-      const uint32_t d = digit_of<RB>(item[k], shift);
-      s_stage[s_bexcl[d] + s_wcnt[wave][d] + rank[k]] = item[k];
+      const uint32_t d = digit_of<RB>(local_of(item[j], lo, span, a.vmax), shift);
+      s_stage[s_bexcl[d] + s_wcnt[wave][d] + rank[j]] = item[j];
     }
   }
   __syncthreads();
-  const long long rem = (long long)N - (long long)blk * kSortTile;
-  const int cnt = rem < kSortTile ? (int)rem : kSortTile;
+  const int cnt = r.hi - r.lo;
   for (int j = tid; j < cnt; j += 256) {
     const uint64_t x = s_stage[j];
-    const uint32_t d = digit_of<RB>(x, shift);
-    const size_t dst = (size_t)s_gbase[d] + (uint32_t)(j - (int)s_bexcl[d]);
-    if (dst < (size_t)N) __builtin_nontemporal_store(x, out + dst);  // see k_keys
+    const uint32_t d = digit_of<RB>(local_of(x, lo, span, a.vmax), shift);
+    const uint32_t dst = s_gbase[d] + (uint32_t)(j - (int)s_bexcl[d]);
+    if (dst < (uint32_t)a.N) __builtin_nontemporal_store(x, out + dst);  // see k_keys
   }
 }
 
-int radix_bits_for(int key_bits) {
-  const int p8 = (key_bits + 7) / 8;
-  const int p9 = (key_bits + 8) / 9;
-  return p9 < p8 ? 9 : 8;
+namespace {
+
+int passes_for(int bits) { return bits <= kRadixMaxBits ? 1 : (bits + kRadixMaxBits - 1) / kRadixMaxBits; }
+
+SortPlan make_plan(bool seg, int bits, int S, long long N) {
+  SortPlan p{};
+  p.seg = seg;
+  p.bits = bits;
+  p.passes = passes_for(bits);
+  p.rb = std::min(kRadixMaxBits, std::max(8, (bits + p.passes - 1) / p.passes));
+  p.S = seg ? S : 1;
+  const long long tiles = (N + kSortTile - 1) / kSortTile + (seg ? S : 0);
+  p.nblk = (int)((tiles + 7) / 8 * 8);
+  return p;
 }
 
-hipError_t launch_sort_hist(int rb, const uint64_t* keys, int N, int shift, uint32_t* ghist,
-                            int nblk, hipStream_t st) {
-  if (rb == 9)
-    hipLaunchKernelGGL(k_sort_hist<9>, dim3(nblk), dim3(256), 0, st, keys, N, shift, ghist, nblk);
-  else
-    hipLaunchKernelGGL(k_sort_hist<8>, dim3(nblk), dim3(256), 0, st, keys, N, shift, ghist, nblk);
+SortKArgs kargs(const SortPlan& p, const SortBufs& b, int N) {
+  SortKArgs a;
+  a.seg_start = p.seg ? b.seg_start : nullptr;
+  a.row_off = b.row_off;
+  a.ghist = b.ghist;
+  a.segbase = b.segbase;
+  a.S = p.S;
+  a.nblk = p.nblk;
+  a.N = N;
+  a.vmax = p.seg ? (1u << p.bits) - 1u : 0xffffffffu;
+  return a;
+}
+
+}  // namespace
+
+SortPlan sort_plan_global(int bits, long long N) { return make_plan(false, bits, 1, N); }
+
+// Per table when that takes fewer passes, or as many passes with narrower
+// digits (fewer counters per tile to write and scan, longer runs per digit).
+SortPlan sort_plan_dedup(const Geom& g, long long N) {
+  const SortPlan glob = make_plan(false, g.key_bits, 1, N);
+  if (g.T > kSegMaxTables) return glob;
+  const SortPlan seg = make_plan(true, g.row_bits, g.T, N);
+  return seg.passes < glob.passes || (seg.passes == glob.passes && seg.rb < glob.rb) ? seg : glob;
+}
+
+#define EMB_SORT_DISPATCH(RBV, KERNEL, GRID, ...)                                    \
+  switch (RBV) {                                                                     \
+    case 8: hipLaunchKernelGGL(KERNEL<8>, GRID, dim3(256), 0, st, __VA_ARGS__); break;   \
+    case 9: hipLaunchKernelGGL(KERNEL<9>, GRID, dim3(256), 0, st, __VA_ARGS__); break;   \
+    case 10: hipLaunchKernelGGL(KERNEL<10>, GRID, dim3(256), 0, st, __VA_ARGS__); break; \
+    default: hipLaunchKernelGGL(KERNEL<11>, GRID, dim3(256), 0, st, __VA_ARGS__); break; \
+  }
+
+hipError_t launch_sort_hist(const SortPlan& p, const SortBufs& b, const uint64_t* keys, int N, int shift,
+                            hipStream_t st) {
+  const SortKArgs a = kargs(p, b, N);
+  EMB_SORT_DISPATCH(p.rb, k_sort_hist, dim3(p.nblk), keys, shift, a);
   return hipGetLastError();
 }
 
-hipError_t launch_sort_scan(int rb, uint32_t* ghist, int nblk, uint32_t* digit_tot, hipStream_t st) {
-  hipLaunchKernelGGL(k_sort_scan, dim3(1 << rb), dim3(256), 0, st, ghist, nblk, digit_tot);
+hipError_t launch_sort_scan(const SortPlan& p, const SortBufs& b, int N, hipStream_t st) {
+  const SortKArgs a = kargs(p, b, N);
+  EMB_SORT_DISPATCH(p.rb, k_sort_scan, dim3(1u << p.rb), a);
   return hipGetLastError();
 }
 
-hipError_t launch_sort_scatter(int rb, const uint64_t* in, uint64_t* out, int N, int shift,
-                               const uint32_t* ghist, const uint32_t* digit_tot, int nblk,
-                               hipStream_t st) {
-  if (rb == 9)
-    hipLaunchKernelGGL(k_sort_scatter<9>, dim3(nblk), dim3(256), 0, st, in, out, N, shift, ghist,
-                       digit_tot, nblk);
-  else
-    hipLaunchKernelGGL(k_sort_scatter<8>, dim3(nblk), dim3(256), 0, st, in, out, N, shift, ghist,
-                       digit_tot, nblk);
+hipError_t launch_sort_scatter(const SortPlan& p, const SortBufs& b, const uint64_t* in, uint64_t* out, int N,
+                               int shift, hipStream_t st) {
+  const SortKArgs a = kargs(p, b, N);
+  EMB_SORT_DISPATCH(p.rb, k_sort_scatter, dim3(p.nblk), in, out, shift, a);
   return hipGetLastError();
 }
+
+#undef EMB_SORT_DISPATCH
 
 }  // namespace emb

@@ -31,9 +31,11 @@ __device__ __forceinline__ uint32_t wave_incl_max(uint32_t v) {
   return v;
 }
 
-// Per tile: segment starts, chunk starts, and 1 + the last segment start in
-// the tile (0 if none).
+// Per tile: segment starts, chunk starts, 1 + the last segment start in the
+// tile (0 if none), and whether the key-build groups of this tile's share
+// (32 groups of 64 bags) all hold one lookup per bag at the bag's own index.
 __global__ __launch_bounds__(256) void k_rle_count(const uint64_t* __restrict__ sorted, int N,
+                                                   const int32_t* __restrict__ unit_grp, int ngrp,
                                                    u4* __restrict__ blk_out) {
   __shared__ uint32_t lds[8];
   __shared__ uint32_t s_max[4];
@@ -53,15 +55,23 @@ __global__ __launch_bounds__(256) void k_rle_count(const uint64_t* __restrict__ 
   uint32_t ts, tc;
   block_excl_scan_256(cs, lds, &ts);
   block_excl_scan_256(cc, lds, &tc);
+  uint32_t unit = 0;
+  if (ngrp > 0) {  // uniform over the grid
+    constexpr int kGrp = kSortTile / 64;
+    const int gi = (int)blockIdx.x * kGrp + (int)threadIdx.x;
+    unit = (uint32_t)__syncthreads_and((int)threadIdx.x >= kGrp || gi >= ngrp || unit_grp[gi] != 0);
+  }
   const uint32_t wm = wave_incl_max(ms);
   if ((threadIdx.x & 63) == 63) s_max[threadIdx.x >> 6] = wm;
   __syncthreads();
   if (threadIdx.x == 0)
-    blk_out[blockIdx.x] = u4{ts, tc, max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3])), 0u};
+    blk_out[blockIdx.x] = u4{ts, tc, max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3])), unit};
 }
 
 // One block: exclusive scans of the per-tile counts (sum) and of the last
-// segment start (max), in place; totals to *num_unique and num_chunks.
+// segment start (max), in place; totals to *num_unique and num_chunks. Every
+// entry's 4th word becomes 1 if all tiles reported one lookup per bag at
+// the bag's own index (then the bag of position p is p).
 __global__ __launch_bounds__(256) void k_rle_scan(u4* __restrict__ blk, int nblk,
                                                   int32_t* __restrict__ num_unique,
                                                   int32_t* __restrict__ num_chunks) {
@@ -71,18 +81,20 @@ __global__ __launch_bounds__(256) void k_rle_scan(u4* __restrict__ blk, int nblk
   const int per = (nblk + 255) / 256;
   const int b0 = threadIdx.x * per;
   const int b1 = min(b0 + per, nblk);
-  uint32_t ss = 0, sc = 0, sm = 0;
+  uint32_t ss = 0, sc = 0, sm = 0, su = 1;
   for (int i0 = b0; i0 < b1; i0 += 8) {
     u4 v[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = i0 + k < b1 ? blk[i0 + k] : u4{0u, 0u, 0u, 0u};
+    for (int k = 0; k < 8; ++k) v[k] = i0 + k < b1 ? blk[i0 + k] : u4{0u, 0u, 0u, 1u};
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       ss += v[k].x;
       sc += v[k].y;
       sm = max(sm, v[k].z);
+      su &= v[k].w;
     }
   }
+  const uint32_t unit = (uint32_t)__syncthreads_and((int)su);
   uint32_t ts, tc;
   uint32_t ps = block_excl_scan_256(ss, lds, &ts);
   uint32_t pc = block_excl_scan_256(sc, lds, &tc);
@@ -101,7 +113,7 @@ __global__ __launch_bounds__(256) void k_rle_scan(u4* __restrict__ blk, int nblk
     for (int k = 0; k < 8; ++k) v[k] = i0 + k < b1 ? blk[i0 + k] : u4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      if (i0 + k < b1) blk[i0 + k] = u4{ps, pc, pm, 0u};
+      if (i0 + k < b1) blk[i0 + k] = u4{ps, pc, pm, unit};
       ps += v[k].x;
       pc += v[k].y;
       pm = max(pm, v[k].z);
@@ -179,6 +191,9 @@ __global__ __launch_bounds__(256) void k_rle_write(RleArgs a) {
   }
   // gathers first (independent across items), stores after, so the loads
   // of all items are in flight together
+  // one lookup per bag at the bag's own index (one-hot features): the bag of
+  // position p is p, and the random gathers of bag_of_pos are skipped
+  const bool unit = bp.w != 0u;
   const int32_t* __restrict__ bag_of_pos = a.bag_of_pos;
   const uint64_t* __restrict__ sorted = a.sorted;
   int32_t bag[kSortIPT], cbv[kSortIPT], bag0[kSortIPT];
@@ -186,7 +201,7 @@ __global__ __launch_bounds__(256) void k_rle_write(RleArgs a) {
   for (int k = 0; k < kSortIPT; ++k) {
     const long long i = base + k * 64 + lane;
     const uint32_t pos = (uint32_t)item[k];
-    bag[k] = (i < a.N && pos < (uint32_t)a.N) ? bag_of_pos[pos] : -1;
+    bag[k] = (i < a.N && pos < (uint32_t)a.N) ? (unit ? (int32_t)pos : bag_of_pos[pos]) : -1;
     // chunk start: the later of its segment's start and its tile's start
     const int32_t seg_start = (int32_t)max(pm, im[k]) - 1;
     const int32_t tile0 = (int32_t)((i / kChunk) * kChunk);
@@ -198,7 +213,7 @@ __global__ __launch_bounds__(256) void k_rle_write(RleArgs a) {
     bag0[k] = bag[k];
     if (i < a.N && (fl & (1u << (24 + k))) && cbv[k] != (int32_t)i) {
       const uint32_t p0 = (uint32_t)sorted[cbv[k]];
-      bag0[k] = p0 < (uint32_t)a.N ? bag_of_pos[p0] : -1;
+      bag0[k] = p0 < (uint32_t)a.N ? (unit ? (int32_t)p0 : bag_of_pos[p0]) : -1;
     }
   }
 #pragma unroll
@@ -240,12 +255,13 @@ __global__ void k_set_empty(int32_t* num_unique, int32_t* num_chunks) {
   }
 }
 
-hipError_t launch_rle(const uint64_t* sorted, int N, const WsLayout& L, char* ws, const RleOut& o,
+hipError_t launch_rle(const uint64_t* sorted, int N, int ngrp, const WsLayout& L, char* ws, const RleOut& o,
                       hipStream_t st) {
   u4* blk = reinterpret_cast<u4*>(ws + L.rle_blk);
   int32_t* num_chunks = reinterpret_cast<int32_t*>(ws + L.scalars);
   const int nblk = L.nblk_rle;
-  hipLaunchKernelGGL(k_rle_count, dim3(nblk), dim3(256), 0, st, sorted, N, blk);
+  hipLaunchKernelGGL(k_rle_count, dim3(nblk), dim3(256), 0, st, sorted, N,
+                     reinterpret_cast<const int32_t*>(ws + L.unit_grp), ngrp, blk);
   hipLaunchKernelGGL(k_rle_scan, dim3(1), dim3(256), 0, st, blk, nblk, o.num_unique, num_chunks);
   RleArgs a;
   a.sorted = sorted;

@@ -195,9 +195,15 @@ size_t emb_backward_workspace_bytes(const emb_ctx* ctx, int64_t N, int32_t B);
  * dY is [B][T*dim] fp32. ws (device, >= emb_backward_workspace_bytes)
  * carries the sorted segments to emb_sparse_update; it, offsets and dY
  * must stay valid and unchanged until that call. A lookup with an
- * out-of-range index gets the key sum(rows) (which sorts last and is never
- * applied by the update) and raises the device error flag; offsets that
- * break the CSR contract raise it too (see emb_check_device_error).
+ * out-of-range index gets the key sum(rows), which is never applied by the
+ * update, and raises the device error flag. That key sorts after every
+ * in-range key of the lookup's own table; when the library sorts each
+ * table's lookups on their row bits (it does so whenever that takes fewer
+ * radix passes than sorting the whole key), it therefore appears once per
+ * table holding such lookups and unique_keys is ascending apart from it.
+ * In-range keys, their counts and inverse entries are unaffected. Offsets
+ * that break the CSR contract raise the flag too (see
+ * emb_check_device_error).
  * N must be < 2^31. */
 int emb_backward_unique_reduce(emb_ctx* ctx, const void* indices, const void* offsets,
                                int32_t itype, int64_t N, int32_t B, int32_t pool,
