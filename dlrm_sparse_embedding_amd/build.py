@@ -54,7 +54,9 @@ def _compile(src: str) -> str:
     cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd = [HIPCC, "-O2", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC, "-Wall",
-               "-x", "hip", f"--offload-arch={ARCH}", "-c", os.path.join(CSRC, src), "-o", obj]
+               "-x", "hip", f"--offload-arch={ARCH}",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -129,22 +129,39 @@ def test_table_plan_out_of_range_indices():
     tabs.close()
 
 
-@pytest.mark.parametrize("where", ["alternating", "last_bag", "none"])
-def test_one_lookup_per_bag_detection(where):
+LENGTH_CASES = {
+    # name: rows, B, bag lengths per table (an int: every bag; a list: a pattern repeated)
+    "one_hot": ([3000, 700, 1999], 1000, [1, 1, 1]),
+    "fixed_hotness": ([3000, 700, 1999, 50], 1000, [3, 1, 7, 2]),
+    "pairs_and_empties": ([3000, 700, 1999], 1000, [1, [0, 2], 1]),   # N == T*B, not one lookup per bag
+    "one_odd_bag_last": ([3000, 700, 1999], 1000, [1, 1, "last2"]),   # N == T*B + 1
+    "empty_table": ([3000, 700, 1999], 1000, [2, 0, 2]),
+    "straddling_groups": ([3000, 700, 1999, 800], 1000 - 37, [1, 1, 1, 1]),   # B % 64 != 0
+    "many_tables_per_group": ([300, 70, 199, 80, 90], 13, [1, 1, 1, 1, 1]),  # B < 32
+}
+
+
+@pytest.mark.parametrize("name", sorted(LENGTH_CASES))
+def test_bag_of_position(name):
     # the dedup takes the bag of position p to be p only when every bag holds
-    # exactly one lookup at its own index; N == T*B alone must not trigger it
-    rows = [3000, 700, 1999]
-    B = 1000
-    rng = np.random.default_rng(11)
-    lens = [np.ones(B, int) for _ in rows]
-    if where == "alternating":
-        lens[1][0::2], lens[1][1::2] = 0, 2
-    elif where == "last_bag":
-        lens[2][-2], lens[2][-1] = 2, 0
+    # exactly one lookup at its own index, and gathers it otherwise (N == T*B
+    # alone must not trigger it); mean pooling weights each lookup by 1/L, so a
+    # wrong bag shows up in the reduced gradient
+    rows, B, spec = LENGTH_CASES[name]
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    lens = []
+    for r in spec:
+        if isinstance(r, int):
+            lens.append(np.full(B, r, int))
+        elif r == "last2":
+            l = np.ones(B, int)
+            l[-1] = 2
+            lens.append(l)
+        else:
+            lens.append(np.resize(np.array(r, int), B))
     keys = [np.minimum(W.zipf_ranks(rng, r, 1.1, int(l.sum())), r) - 1 for l, r in zip(lens, rows)]
     batch = W.make_batch_from_lengths(lens, keys, B)
-    assert batch.N == len(rows) * B
     cfg = P.custom_cfg(rows, dim=16, B=B, pool="mean", opt="adagrad")
     dY = rng.standard_normal((B, len(rows) * 16)).astype(np.float32)
-    P.say("one lookup per bag detection", where)
+    P.say("bag of position", name, "B", B, "N", batch.N)
     P.run_step(cfg, batch, dY, path="materialized", sample_untouched=500)
