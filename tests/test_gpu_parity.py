@@ -235,15 +235,24 @@ def test_out_of_range_index_flagged_not_applied():
     tabs.close()
 
 
-@pytest.mark.parametrize("case", ["decreasing", "short_end", "long_end", "nonzero_start"])
-def test_malformed_offsets_flagged(case):
+# tables sorted globally (one radix pass over the keys) and tables sorted per
+# table on their row bits (the segments come from the table starts in the
+# offsets, so malformed offsets reach the sort's segment map)
+OFFSET_TABLES = {"global": [50, 60], "per_table": [1000, 700, 1023, 10, 500, 999]}
+
+
+@pytest.mark.parametrize("tables", sorted(OFFSET_TABLES))
+@pytest.mark.parametrize("case", ["decreasing", "short_end", "long_end", "nonzero_start", "table_start_past_next"])
+def test_malformed_offsets_flagged(case, tables):
     # offsets that break the CSR contract: the backward's key build reports
     # EMB_E_INVAL through the device flag; every kernel clamps offsets into
     # [0, N], so the whole step still runs inside the caller's buffers
-    cfg = _custom_cfg([50, 60], B=8, opt="sgd")
+    rows = OFFSET_TABLES[tables]
+    T = len(rows)
+    cfg = _custom_cfg(rows, B=8, opt="sgd")
     rng = np.random.default_rng(11)
-    lens = [rng.integers(0, 4, 8), rng.integers(0, 4, 8)]
-    keys = [rng.integers(0, 50, int(lens[0].sum())), rng.integers(0, 60, int(lens[1].sum()))]
+    lens = [rng.integers(0, 4, 8) for _ in rows]
+    keys = [rng.integers(0, r, int(l.sum())) for r, l in zip(rows, lens)]
     batch = W.make_batch_from_lengths(lens, keys, 8)
     off = batch.offsets.copy()
     N = batch.N
@@ -255,20 +264,27 @@ def test_malformed_offsets_flagged(case):
         off[-2] = min(off[-2], N - 3)
     elif case == "long_end":
         off[-1] = N + 5
-    else:
+    elif case == "nonzero_start":
         off[0] = 2
-    _say("malformed offsets", case)
+    else:  # table 1 starts past table 2's start (past the end with two tables)
+        off[8] = off[16] + 1
+    _say("malformed offsets", case, tables)
     tabs = P.make_tables(cfg)
     idx = torch.from_numpy(batch.indices).cuda()
     offd = torch.from_numpy(off).cuda()
-    dy = torch.ones((8, 32), dtype=torch.float32, device="cuda")
+    dy = torch.ones((8, T * 16), dtype=torch.float32, device="cuda")
     tabs.forward(idx, offd, 8, "mean")
     bufs = tabs.backward_buffers(N, 8, with_grad=False)
     tabs.backward(idx, offd, 8, "mean", dy, bufs)
     tabs.update("sgd", 0.5, 0.0, bufs, dY=dy)
     with pytest.raises(E.EmbError) as ei:
         tabs.check_device_error()
-    assert ei.value.code == E.EMB_E_INVAL
+    if tables == "global" and case != "table_start_past_next":
+        assert ei.value.code == E.EMB_E_INVAL
+    else:
+        # positions the broken offsets hand to another table's bags may also
+        # hold rows outside that table, which is reported first
+        assert ei.value.code in (E.EMB_E_INVAL, E.EMB_E_BOUNDS)
     tabs.check_device_error()                # flag was cleared
     tabs.close()
 
