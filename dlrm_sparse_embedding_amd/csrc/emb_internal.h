@@ -162,8 +162,11 @@ struct SortPlan {
   int passes;
   int rb;      // digit bits, 8..kRadixMaxBits
   int S;       // segments (T when seg, else 1)
+  int ipt;     // items per thread: tiles of 256 * ipt items
   int nblk;    // tiles of the hist / scatter grids (multiple of 8)
 };
+// sorts of at least this many items use 4096-item tiles
+constexpr long long kSortBigN = 16ll << 20;
 SortPlan sort_plan_global(int bits, long long N);
 SortPlan sort_plan_dedup(const Geom& g, long long N);
 struct SortBufs {

@@ -181,6 +181,7 @@ struct SortKArgs {
   int S;                     // segments
   int nblk;                  // tiles in the grid (multiple of 8)
   int N;
+  int tile;                  // items per tile: 256 x items per thread
   uint32_t vmax;             // row value of a key outside its segment's table
 };
 
@@ -209,7 +210,7 @@ __device__ void build_seg_map(const SortKArgs& a, SegLds& m) {
     int carry = 0;
     for (int c = 0; c < a.S; c += 64) {
       const int t = c + lane;
-      const int n = t < a.S ? (m.sb[t + 1] - m.sb[t] + kSortTile - 1) / kSortTile : 0;
+      const int n = t < a.S ? (m.sb[t + 1] - m.sb[t] + a.tile - 1) / a.tile : 0;
       int x = n;
 #pragma unroll
       for (int d = 1; d < 64; d <<= 1) {
@@ -241,13 +242,13 @@ __device__ __forceinline__ TileRange tile_range(const SortKArgs& a, const SegLds
       else hi = mid;
     }
     r.seg = lo;
-    r.lo = m.sb[lo] + (k - m.tf[lo]) * kSortTile;
-    r.hi = min(r.lo + kSortTile, m.sb[lo + 1]);
+    r.lo = m.sb[lo] + (k - m.tf[lo]) * a.tile;
+    r.hi = min(r.lo + a.tile, m.sb[lo + 1]);
   } else {
-    const long long s0 = (long long)k * kSortTile;
+    const long long s0 = (long long)k * a.tile;
     if (s0 < a.N) {
       r.lo = (int)s0;
-      r.hi = (int)min(s0 + kSortTile, (long long)a.N);
+      r.hi = (int)min(s0 + a.tile, (long long)a.N);
     }
   }
   return r;
@@ -315,7 +316,7 @@ __device__ __forceinline__ void seg_rows(const SortKArgs& a, int seg, uint32_t* 
   }
 }
 
-template <int RB>
+template <int RB, int IPT>
 __global__ __launch_bounds__(256) void k_sort_hist(const uint64_t* __restrict__ keys, int shift, SortKArgs a) {
   constexpr int R = 1 << RB;
   __shared__ uint32_t h[R];
@@ -331,7 +332,7 @@ __global__ __launch_bounds__(256) void k_sort_hist(const uint64_t* __restrict__ 
   // skewed keys put many lanes on one bin, which would serialise per-lane adds
   const uint64_t lt = lanemask_lt();
 #pragma unroll
-  for (int j = 0; j < kSortIPT; ++j) {
+  for (int j = 0; j < IPT; ++j) {
     const int i = r.lo + j * 256 + threadIdx.x;
     const bool valid = i < r.hi;
     const uint32_t d = valid ? digit_of<RB>(local_of(keys[i], lo, span, a.vmax), shift) : 0u;
@@ -394,7 +395,7 @@ __global__ __launch_bounds__(256) void k_sort_scan(SortKArgs a) {
   for (int t = threadIdx.x; t <= a.S; t += 256) a.segbase[(size_t)t * R + d] = s_base[t];
 }
 
-template <int RB>
+template <int RB, int IPT>
 __global__ __launch_bounds__(256) void k_sort_scatter(const uint64_t* __restrict__ in,
                                                       uint64_t* __restrict__ out, int shift,
                                                       SortKArgs a) {
@@ -403,7 +404,7 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const uint64_t* __restrict
   __shared__ uint32_t s_gbase[R];    // global start of this tile's digit-d run
   __shared__ uint16_t s_wcnt[4][R];  // per-wave digit counters, then per-wave offsets
   __shared__ uint16_t s_bexcl[R];    // tile-local start of digit d
-  __shared__ uint64_t s_stage[kSortTile];
+  __shared__ uint64_t s_stage[256 * IPT];
   __shared__ uint32_t s_scan[8];
   __shared__ SegLds m;
   const int tid = threadIdx.x;
@@ -439,17 +440,17 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const uint64_t* __restrict
     for (int dd = tid; dd < R; dd += 256) s_wcnt[w][dd] = 0;
   __syncthreads();
 
-  const int base = r.lo + wave * (64 * kSortIPT);
-  uint64_t item[kSortIPT];
-  uint32_t rank[kSortIPT];
+  const int base = r.lo + wave * (64 * IPT);
+  uint64_t item[IPT];
+  uint32_t rank[IPT];
 #pragma unroll
-  for (int j = 0; j < kSortIPT; ++j) {
+  for (int j = 0; j < IPT; ++j) {
     const int i = base + j * 64 + lane;
     item[j] = i < r.hi ? in[i] : 0ull;
   }
   const uint64_t lt = lanemask_lt();
 #pragma unroll
-  for (int j = 0; j < kSortIPT; ++j) {
+  for (int j = 0; j < IPT; ++j) {
     const bool valid = base + j * 64 + lane < r.hi;
     const uint32_t d = digit_of<RB>(local_of(item[j], lo, span, a.vmax), shift);
     const uint64_t peers = digit_peers<RB>(d, valid);
@@ -482,7 +483,7 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const uint64_t* __restrict
   }
   __syncthreads();
 #pragma unroll
-  for (int j = 0; j < kSortIPT; ++j) {
+  for (int j = 0; j < IPT; ++j) {
     const bool valid = base + j * 64 + lane < r.hi;
     if (valid) {
       const uint32_t d = digit_of<RB>(local_of(item[j], lo, span, a.vmax), shift);
@@ -510,7 +511,12 @@ SortPlan make_plan(bool seg, int bits, int S, long long N) {
   p.passes = passes_for(bits);
   p.rb = std::min(kRadixMaxBits, std::max(8, (bits + p.passes - 1) / p.passes));
   p.S = seg ? S : 1;
-  const long long tiles = (N + kSortTile - 1) / kSortTile + (seg ? S : 0);
+  // larger tiles for large sorts: twice the items per digit run written,
+  // half the per-tile counters to write and scan (small sorts keep more
+  // tiles than the GPU has CUs)
+  p.ipt = N >= kSortBigN ? 16 : 8;
+  const long long tile = 256ll * p.ipt;
+  const long long tiles = (N + tile - 1) / tile + (seg ? S : 0);
   p.nblk = (int)((tiles + 7) / 8 * 8);
   return p;
 }
@@ -524,6 +530,7 @@ SortKArgs kargs(const SortPlan& p, const SortBufs& b, int N) {
   a.S = p.S;
   a.nblk = p.nblk;
   a.N = N;
+  a.tile = 256 * p.ipt;
   a.vmax = p.seg ? (1u << p.bits) - 1u : 0xffffffffu;
   return a;
 }
@@ -545,14 +552,22 @@ SortPlan sort_plan_dedup(const Geom& g, long long N) {
   switch (RBV) {                                                                     \
     case 8: hipLaunchKernelGGL(KERNEL<8>, GRID, dim3(256), 0, st, __VA_ARGS__); break;   \
     case 9: hipLaunchKernelGGL(KERNEL<9>, GRID, dim3(256), 0, st, __VA_ARGS__); break;   \
-    case 10: hipLaunchKernelGGL(KERNEL<10>, GRID, dim3(256), 0, st, __VA_ARGS__); break; \
-    default: hipLaunchKernelGGL(KERNEL<11>, GRID, dim3(256), 0, st, __VA_ARGS__); break; \
+    default: hipLaunchKernelGGL(KERNEL<10>, GRID, dim3(256), 0, st, __VA_ARGS__); break; \
+  }
+#define EMB_SORT_DISPATCH_IPT(RBV, IPTV, KERNEL, GRID, ...)                          \
+  switch (RBV * 100 + IPTV) {                                                        \
+    case 808: hipLaunchKernelGGL((KERNEL<8, 8>), GRID, dim3(256), 0, st, __VA_ARGS__); break;   \
+    case 908: hipLaunchKernelGGL((KERNEL<9, 8>), GRID, dim3(256), 0, st, __VA_ARGS__); break;   \
+    case 1008: hipLaunchKernelGGL((KERNEL<10, 8>), GRID, dim3(256), 0, st, __VA_ARGS__); break; \
+    case 816: hipLaunchKernelGGL((KERNEL<8, 16>), GRID, dim3(256), 0, st, __VA_ARGS__); break;  \
+    case 916: hipLaunchKernelGGL((KERNEL<9, 16>), GRID, dim3(256), 0, st, __VA_ARGS__); break;  \
+    default: hipLaunchKernelGGL((KERNEL<10, 16>), GRID, dim3(256), 0, st, __VA_ARGS__); break;  \
   }
 
 hipError_t launch_sort_hist(const SortPlan& p, const SortBufs& b, const uint64_t* keys, int N, int shift,
                             hipStream_t st) {
   const SortKArgs a = kargs(p, b, N);
-  EMB_SORT_DISPATCH(p.rb, k_sort_hist, dim3(p.nblk), keys, shift, a);
+  EMB_SORT_DISPATCH_IPT(p.rb, p.ipt, k_sort_hist, dim3(p.nblk), keys, shift, a);
   return hipGetLastError();
 }
 
@@ -565,10 +580,11 @@ hipError_t launch_sort_scan(const SortPlan& p, const SortBufs& b, int N, hipStre
 hipError_t launch_sort_scatter(const SortPlan& p, const SortBufs& b, const uint64_t* in, uint64_t* out, int N,
                                int shift, hipStream_t st) {
   const SortKArgs a = kargs(p, b, N);
-  EMB_SORT_DISPATCH(p.rb, k_sort_scatter, dim3(p.nblk), in, out, shift, a);
+  EMB_SORT_DISPATCH_IPT(p.rb, p.ipt, k_sort_scatter, dim3(p.nblk), in, out, shift, a);
   return hipGetLastError();
 }
 
 #undef EMB_SORT_DISPATCH
+#undef EMB_SORT_DISPATCH_IPT
 
 }  // namespace emb

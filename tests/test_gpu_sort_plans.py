@@ -70,6 +70,23 @@ CASES = {
 }
 
 
+def test_sort_plan_large_tiles():
+    # sorts of >= 16 Mi items use 4096-item tiles: 8 tables x 1M rows (per
+    # table, 2 passes of 10 bits), 65536 samples x 32 lookups = 16 Mi lookups
+    rows = [1_000_000] * 8
+    assert _plan(rows) == (True, 2, 10)
+    B, h = 65536, 32
+    rng = np.random.default_rng(5)
+    lens = [np.full(B, h, int) for _ in rows]
+    keys = [np.minimum(W.zipf_ranks(rng, r, 1.2, B * h), r) - 1 for r in rows]
+    batch = W.make_batch_from_lengths(lens, keys, B)
+    assert batch.N >= 16 << 20
+    cfg = P.custom_cfg(rows, dim=16, B=B, pool="mean", opt="sgd")
+    dY = rng.standard_normal((B, len(rows) * 16)).astype(np.float32)
+    P.say("sort plan, large tiles", "N", batch.N)
+    P.run_step(cfg, batch, dY, path="fused", sample_bags=256, sample_keys=2000, sample_untouched=500)
+
+
 @pytest.mark.parametrize("name", sorted(CASES))
 def test_sort_plan_step(name):
     rows, B, maxlen, dim, want = CASES[name]
