@@ -496,7 +496,10 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const uint64_t* __restrict
     const uint64_t x = s_stage[j];
     const uint32_t d = digit_of<RB>(local_of(x, lo, span, a.vmax), shift);
     const uint32_t dst = s_gbase[d] + (uint32_t)(j - (int)s_bexcl[d]);
-    if (dst < (uint32_t)a.N) __builtin_nontemporal_store(x, out + dst);  // see k_keys
+    // ordinary stores: neighbouring tiles run on one XCD and write adjacent
+    // runs of a digit, which then merge in its L2 (a non-temporal store would
+    // send each short run to memory as a partial line)
+    if (dst < (uint32_t)a.N) out[dst] = x;
   }
 }
 
