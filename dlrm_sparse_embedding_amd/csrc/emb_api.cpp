@@ -510,7 +510,7 @@ int run_dedup(emb_ctx* ctx, const void* indices, const void* offsets, int32_t it
     RleOut o{unique_keys, counts, inverse, num_unique};
     const long long TB = (long long)ctx->g.T * B;
     const int ngrp = N == TB ? (int)((TB + 63) / 64) : 0;
-    if ((e = launch_rle(a, (int)N, ngrp, N > TB, L, w, o, st)) != hipSuccess) return hip_fail(e, "run-length encode");
+    if ((e = launch_rle(a, (int)N, ngrp, L, w, o, st)) != hipSuccess) return hip_fail(e, "run-length encode");
   }
   return EMB_OK;
 }

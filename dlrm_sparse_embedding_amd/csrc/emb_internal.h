@@ -191,10 +191,8 @@ struct RleOut {
 };
 // ngrp: key-build groups whose one-lookup-per-bag flags decide whether the
 // bag of position p is p itself (0 when N != T*B: never).
-// multi_hot: more lookups than bags (the inverse index is then written with
-// ordinary stores, else non-temporal ones).
-hipError_t launch_rle(const uint64_t* sorted, int N, int ngrp, bool multi_hot, const WsLayout& L, char* ws,
-                      const RleOut& o, hipStream_t st);
+hipError_t launch_rle(const uint64_t* sorted, int N, int ngrp, const WsLayout& L, char* ws, const RleOut& o,
+                      hipStream_t st);
 hipError_t launch_set_empty(const WsLayout& L, char* ws, int32_t* num_unique, hipStream_t st);
 
 // mode: 0 = write reduced gradient, 1 = fused SGD, 2 = fused Adagrad.

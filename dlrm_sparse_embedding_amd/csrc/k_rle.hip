@@ -141,12 +141,6 @@ struct RleArgs {
   int N;
 };
 
-// NT: the inverse index is written with non-temporal stores (one-hot batches,
-// whose positions are scattered, so that the L2 keeps the rows of the
-// forward / update running beside the dedup); multi-hot batches write it with
-// ordinary stores, since a hot key's positions sit close together and their
-// stores merge in L2 (config 5's RLE: 51 -> 37 us).
-template <bool NT>
 __global__ __launch_bounds__(256) void k_rle_write(RleArgs a) {
   __shared__ uint32_t s_ws[4], s_wc[4], s_wm[4];
   const int lane = threadIdx.x & 63;
@@ -232,10 +226,10 @@ __global__ __launch_bounds__(256) void k_rle_write(RleArgs a) {
     const uint32_t key = key_of(item[k]);
     const uint32_t pos = (uint32_t)item[k];
     // non-temporal: keep the L2 for the forward / update beside the dedup
-    if (pos < (uint32_t)a.N) {
-      if constexpr (NT) __builtin_nontemporal_store(seg, a.inverse + pos);
-      else a.inverse[pos] = seg;
-    }
+    // the inverse index with ordinary stores: the 4-byte stores of nearby
+    // positions (a hot key's, or a tile's neighbours on one XCD) merge in L2
+    // before a line is written back
+    if (pos < (uint32_t)a.N) a.inverse[pos] = seg;
     __builtin_nontemporal_store(bag[k], a.sorted_bag + i);
     if (fl & (1u << k)) {
       a.unique_keys[seg] = key;
@@ -264,8 +258,8 @@ __global__ void k_set_empty(int32_t* num_unique, int32_t* num_chunks) {
   }
 }
 
-hipError_t launch_rle(const uint64_t* sorted, int N, int ngrp, bool multi_hot, const WsLayout& L, char* ws,
-                      const RleOut& o, hipStream_t st) {
+hipError_t launch_rle(const uint64_t* sorted, int N, int ngrp, const WsLayout& L, char* ws, const RleOut& o,
+                      hipStream_t st) {
   u4* blk = reinterpret_cast<u4*>(ws + L.rle_blk);
   int32_t* num_chunks = reinterpret_cast<int32_t*>(ws + L.scalars);
   const int nblk = L.nblk_rle;
@@ -286,10 +280,7 @@ hipError_t launch_rle(const uint64_t* sorted, int N, int ngrp, bool multi_hot, c
   a.tile_last_seg = reinterpret_cast<int32_t*>(ws + L.tile_last_seg);
   a.sorted_bag = reinterpret_cast<int32_t*>(ws + L.sorted_bag);
   a.N = N;
-  if (multi_hot)
-    hipLaunchKernelGGL(k_rle_write<false>, dim3(nblk), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL(k_rle_write<true>, dim3(nblk), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_rle_write, dim3(nblk), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
