@@ -225,11 +225,12 @@ __global__ __launch_bounds__(256) void k_rle_write(RleArgs a) {
     const int32_t seg_start = (int32_t)max(pm, im[k]) - 1;
     const uint32_t key = key_of(item[k]);
     const uint32_t pos = (uint32_t)item[k];
-    // non-temporal: keep the L2 for the forward / update beside the dedup
     // the inverse index with ordinary stores: the 4-byte stores of nearby
     // positions (a hot key's, or a tile's neighbours on one XCD) merge in L2
     // before a line is written back
     if (pos < (uint32_t)a.N) a.inverse[pos] = seg;
+    // the sorted bags are written whole lines at a time: non-temporal, so they
+    // keep the L2 for the forward / update running beside the dedup
     __builtin_nontemporal_store(bag[k], a.sorted_bag + i);
     if (fl & (1u << k)) {
       a.unique_keys[seg] = key;
