@@ -285,39 +285,42 @@ __device__ __forceinline__ void sum_partials(const float* partial, int D, int c0
   }
 }
 
-// Level 1: one subgroup per 4096-position tile J. The segments that cross a
-// level-1 boundary and touch J can only be J's first and last segments; for
-// each, the level-0 partials inside J are added (tile order) into its
-// level-1 partial of J.
+// Level 1: two subgroups per 4096-position tile J. The segments that cross
+// a level-1 boundary and touch J can only be J's first and last segments;
+// subgroup c of J takes the first (c = 0) or the last (c = 1, unless it is
+// the same segment) and adds its level-0 partials inside J (tile order) into
+// its level-1 partial of J.
 template <int LPR>
 __global__ __launch_bounds__(256) void k_level1(RedArgs a) {
   constexpr int SGW = 256 / LPR;
-  const int J = blockIdx.x * SGW + threadIdx.x / LPR;
+  const int sgi = blockIdx.x * SGW + threadIdx.x / LPR;
+  const int J = sgi >> 1;
   if (J >= a.ntiles1) return;
   const int c0 = (int)blockIdx.y * 4 * LPR + (threadIdx.x & (LPR - 1)) * 4;  // column block: blockIdx.y
   const bool act = c0 < a.D;
   const int jf = J * kL1Tiles;
   const int jl = min(jf + kL1Tiles - 1, a.ntiles - 1);
-  const int cand[2] = {a.tile_first_seg[jf], a.tile_last_seg[jl]};
-  for (int c = 0; c < 2; ++c) {
-    const int u = cand[c];
-    if (c == 1 && u == cand[0]) break;
-    if (u < 0 || u >= a.N || a.ukeys[u] >= a.total_rows) continue;
-    const int so = a.seg_off[u];
-    const int eo = a.seg_off[u + 1];
-    if (so / kChunk1 == (eo - 1) / kChunk1) continue;  // stays inside one level-1 tile
-    const int lo = max(so, J * kChunk1);
-    const int hi = min(eo, (J + 1) * kChunk1);
-    if (lo >= hi) continue;
-    const int j0 = lo / kChunk;
-    const int n = (hi - 1) / kChunk - j0 + 1;
-    float g[4];
-    sum_partials(a.partial0, a.D, c0, act, n, [&](int k) { return slot_of(so, j0 + k, kChunk); }, g);
-    const int slot1 = slot_of(so, J, kChunk1);
-    if (act) {
-      f4 o = {g[0], g[1], g[2], g[3]};
-      *reinterpret_cast<f4*>(a.partial1 + (size_t)slot1 * a.D + c0) = o;
-    }
+  const int first = a.tile_first_seg[jf];
+  int u = first;
+  if (sgi & 1) {
+    u = a.tile_last_seg[jl];
+    if (u == first) return;
+  }
+  if (u < 0 || u >= a.N || a.ukeys[u] >= a.total_rows) return;
+  const int so = a.seg_off[u];
+  const int eo = a.seg_off[u + 1];
+  if (so / kChunk1 == (eo - 1) / kChunk1) return;  // stays inside one level-1 tile
+  const int lo = max(so, J * kChunk1);
+  const int hi = min(eo, (J + 1) * kChunk1);
+  if (lo >= hi) return;
+  const int j0 = lo / kChunk;
+  const int n = (hi - 1) / kChunk - j0 + 1;
+  float g[4];
+  sum_partials(a.partial0, a.D, c0, act, n, [&](int k) { return slot_of(so, j0 + k, kChunk); }, g);
+  const int slot1 = slot_of(so, J, kChunk1);
+  if (act) {
+    f4 o = {g[0], g[1], g[2], g[3]};
+    *reinterpret_cast<f4*>(a.partial1 + (size_t)slot1 * a.D + c0) = o;
   }
 }
 
@@ -342,6 +345,20 @@ __global__ __launch_bounds__(256) void k_combine(RedArgs a) {
   if (so < j * kChunk || eo <= (j + 1) * kChunk) return;  // not the owner
   const uint32_t key = a.ukeys[u];
   if (key >= a.total_rows) return;
+  // the row (and state) is loaded before the partials are summed, so its
+  // latency overlaps theirs
+  char* wp = nullptr;
+  float* gp = nullptr;
+  float* mp = nullptr;
+  float wv[4] = {0.f, 0.f, 0.f, 0.f}, Gv[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (MODE != 0) {
+    if (act) {
+      const int t = table_of(s_ro, a.T, key);
+      row_ptrs<DT>(a, t, key - s_ro[t], c0, &wp, &gp, &mp);
+      load_weight<DT>(wp, mp, wv);
+      if constexpr (MODE == 2) load4<EMB_F32>(gp, Gv);
+    }
+  }
   float g[4];
   if (so / kChunk1 == (eo - 1) / kChunk1) {
     const int n = (eo - 1) / kChunk - j + 1;
@@ -351,7 +368,9 @@ __global__ __launch_bounds__(256) void k_combine(RedArgs a) {
     const int n = (eo - 1) / kChunk1 - J0 + 1;
     sum_partials(a.partial1, a.D, c0, act, n, [&](int k) { return slot_of(so, J0 + k, kChunk1); }, g);
   }
-  if (act) finish_row<DT, MODE>(a, s_ro, key, u, c0, g);
+  if (!act) return;
+  if constexpr (MODE == 0) finish_row<DT, MODE>(a, s_ro, key, u, c0, g);
+  else row_update<DT, MODE>(wp, gp, mp, wv, Gv, g, a.lr, a.eps);
 }
 
 // Update from a materialised reduced gradient (grad[u] for u < U).
@@ -527,7 +546,7 @@ hipError_t launch_combine(const Geom& g, const DevCtx& dc, int mode, int N, cons
   const int lpr = lpr_b(g);
   const int sgw = 256 / lpr;
   if (L.ntiles1 > 1) {
-    const int grid1 = ceil_div(L.ntiles1, sgw);
+    const int grid1 = ceil_div(2ll * L.ntiles1, sgw);  // two subgroups per level-1 tile
 #define L_L1(P) hipLaunchKernelGGL((k_level1<P>), dim3(grid1, col_blocks(a.D, P)), dim3(256), 0, st, a);
     LPR_SWITCH(L_L1)
 #undef L_L1
