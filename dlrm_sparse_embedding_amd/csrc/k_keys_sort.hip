@@ -20,8 +20,11 @@
 // Digits are 8 to 10 bits, as few passes as 10-bit digits allow (wider
 // digits cost more per pass than the pass they save: more counters per tile
 // to write and scan, shorter runs to scatter).
+// Tiles hold 2048 items (8 per thread), or 4096 for sorts of 16 Mi items and
+// more (longer runs per digit, half the counters; below that, fewer blocks
+// would hide less latency).
 // Sort pass = three kernels:
-//   hist    per 2048-item tile, count digits in LDS -> ghist[digit][tile]
+//   hist    per tile, count digits in LDS -> ghist[digit][tile]
 //           (tiles never straddle segments; consecutive tiles run on one
 //           XCD, so their counts share cache lines in one L2, and so do the
 //           runs that neighbouring tiles scatter to one digit's range)
@@ -33,7 +36,7 @@
 //           digit order, then write runs of equal digits contiguously to
 //           segment start + digits below + this digit's tiles before.
 // The tile is striped per wave (item k of lane l of wave w sits at
-// w*512 + k*64 + l), which is the order the ranking visits, so ranks are
+// w*64*IPT + k*64 + l), which is the order the ranking visits, so ranks are
 // stable.
 #include "emb_device.h"
 
