@@ -354,15 +354,17 @@ def test_master_weights_three_steps():
                    master=True)
 
 
-def test_pipelined_dedup_matches_serial():
+@pytest.mark.parametrize("cfg_id", [2, 5])
+def test_pipelined_dedup_matches_serial(cfg_id):
     # three steps where the next batch's dedup runs on a side stream, into a
     # second workspace, while the current step's forward and update run --
     # the pattern of bench.py's pipeline schedule -- against three serial steps
-    cfg = W.make_config(2, batch=4096)
+    # (one-hot tables; and the multi-hot column-sliced fp16 shard)
+    cfg = W.make_config(2, batch=4096) if cfg_id == 2 else W.make_config(5, batch=4096, rows=2_000_000)
     batches = [W.make_batch(cfg, k=k) for k in range(3)]
     dys = [W.make_dy(cfg, k=k) for k in range(3)]
     u = np.unique(np.concatenate([P.oracle_dedup(cfg, b)[0] for b in batches]))
-    _say("pipelined dedup cfg2")
+    _say("pipelined dedup cfg", cfg_id)
     results = []
     for pipelined in (False, True):
         tabs = P.make_tables(cfg)
