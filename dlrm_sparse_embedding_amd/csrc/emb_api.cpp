@@ -82,8 +82,6 @@ struct emb_ctx {
     const int32_t* num_unique = nullptr;
     bool valid = false;
   } dedup;
-  // cap on forward blocks (0 = one block per work unit), see ensure_device
-  int fwd_max_blocks = 0;
   // shard map (emb_set_shard_map): host copy, device copy uploaded on first use
   std::vector<emb_shard_rule> shard_rules;
   int num_shards = 0;
@@ -137,13 +135,6 @@ int ensure_device(emb_ctx* c) {
   }
   c->dev_block = p;
   c->device = dev;
-  // Forward grid cap: kFwdBlocksPerCU blocks per compute unit (EMB_FWD_BLOCKS_PER_CU
-  // overrides it; 0 = uncapped), leaving wave slots to a dedup on another stream.
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
-  int per_cu = kFwdBlocksPerCU;
-  if (const char* v = std::getenv("EMB_FWD_BLOCKS_PER_CU")) per_cu = std::atoi(v);
-  c->fwd_max_blocks = per_cu > 0 ? per_cu * cus : 0;
   c->dc.tables = reinterpret_cast<const DevTable*>(p);
   c->dc.row_off = reinterpret_cast<const uint32_t*>(static_cast<char*>(p) + ro_off);
   c->dc.err_flag = reinterpret_cast<int*>(static_cast<char*>(p) + err_off);
@@ -384,7 +375,7 @@ int emb_forward_pooled(emb_ctx* ctx, const void* indices, const void* offsets, i
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   KScope ks(ctx, EMB_K_FORWARD, st);
   hipError_t e = launch_forward(ctx->g, ctx->dc, indices, offsets, itype, N, B, pool, out,
-                                ctx->fwd_max_blocks, st);
+                                0, st);
   if (e != hipSuccess) return hip_fail(e, "forward kernel");
   return ok();
 }
@@ -418,7 +409,7 @@ int emb_forward_pooled_unique(emb_ctx* ctx, const void* indices, const void* off
   }
   {
     KScope ks(ctx, EMB_K_FORWARD, st);
-    if ((e = launch_forward(ctx->g, ctx->dc, d.inverse, offsets, itype, N, B, pool, out, ctx->fwd_max_blocks, st,
+    if ((e = launch_forward(ctx->g, ctx->dc, d.inverse, offsets, itype, N, B, pool, out, 0, st,
                             rows_buf, N)) != hipSuccess)
       return hip_fail(e, "forward from unique rows");
   }
@@ -812,7 +803,7 @@ int emb_forward_pooled_hashed(emb_ctx* ctx, const int64_t* ids, const void* offs
   if ((rc = ensure_device(ctx))) return rc;
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   KScope ks(ctx, EMB_K_FORWARD, st);
-  hipError_t e = launch_forward(ctx->g, ctx->dc, ids, offsets, itype, N, B, pool, out, ctx->fwd_max_blocks, st,
+  hipError_t e = launch_forward(ctx->g, ctx->dc, ids, offsets, itype, N, B, pool, out, 0, st,
                                 nullptr, 0, &ctx->hv);
   if (e != hipSuccess) return hip_fail(e, "hashed forward");
   return ok();

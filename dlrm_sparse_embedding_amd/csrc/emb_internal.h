@@ -63,9 +63,6 @@ constexpr int kChunk = 128;
 constexpr int kL1Tiles = 32;
 constexpr int kChunk1 = kChunk * kL1Tiles;  // 4096 positions
 
-// Forward grid cap in blocks per compute unit (0 = uncapped).
-constexpr int kFwdBlocksPerCU = 0;
-
 // Radix sort / run-length tiles.
 constexpr int kSortThreads = 256;
 constexpr int kSortIPT = 8;

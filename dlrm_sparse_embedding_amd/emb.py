@@ -19,8 +19,7 @@ from dataclasses import dataclass
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-# EMB_LIBRARY may name another build of the same library (e.g. a tuning variant)
-LIB_PATH = os.environ.get("EMB_LIBRARY") or os.path.join(_PKG, "libemb.so")
+LIB_PATH = os.path.join(_PKG, "libemb.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "emb.h")
 
 EMB_OK = 0
@@ -447,6 +446,13 @@ class EmbeddingTables:
         ws = torch.empty(max(emb_hash_workspace_bytes(self.ctx, ids.numel()), 256), dtype=torch.uint8,
                          device=ids.device)
         emb_hash_translate(self.ctx, ids, offsets, B, insert, ws, rows, stream)
+        if stream is not None:
+            # the allocator must not hand ws (or rows) to another tensor while
+            # the translation still runs on a stream other than the current one
+            st = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream))
+            if st != torch.cuda.current_stream(ids.device):
+                ws.record_stream(st)
+                rows.record_stream(st)
         return rows
 
     def forward_hashed(self, ids, offsets, B: int, pool: str, out=None, stream=None):

@@ -155,8 +155,9 @@ int emb_init_uniform(emb_ctx* ctx, uint64_t seed, void* hip_stream);
  * W_t[idx][c] (EMB_POOL_SUM) or that sum / bag length (EMB_POOL_MEAN),
  * accumulated in fp32 whatever the storage type; an empty bag gives 0.
  * N = number of lookups (= offsets[T*B]), B = batch size (samples).
- * A lookup whose index is outside [0, rows_t) contributes nothing and
- * raises the context's device error flag (see emb_check_device_error). */
+ * A lookup whose index is outside [0, rows_t) contributes nothing, still
+ * counts in its bag's length (the mean divides by offsets[b+1] - offsets[b]),
+ * and raises the context's device error flag (see emb_check_device_error). */
 int emb_forward_pooled(emb_ctx* ctx, const void* indices, const void* offsets,
                        int32_t itype, int64_t N, int32_t B, int32_t pool,
                        float* out, void* hip_stream);
@@ -341,8 +342,8 @@ int emb_hash_translate(emb_ctx* ctx, const int64_t* ids, const void* offsets, in
 
 /* Fused hash lookup + pooled forward (lookup only, no insertion): as
  * emb_forward_pooled with each lookup's row found in its table's map; an id
- * without a row contributes nothing (no error). EMB_E_STATE if no map memory
- * is attached. */
+ * without a row contributes nothing (no error) and still counts in its bag's
+ * length under EMB_POOL_MEAN. EMB_E_STATE if no map memory is attached. */
 int emb_forward_pooled_hashed(emb_ctx* ctx, const int64_t* ids, const void* offsets, int32_t itype,
                               int64_t N, int32_t B, int32_t pool, float* out, void* hip_stream);
 

@@ -56,6 +56,12 @@ What is computed, and where the sources define it
   table's rows are used up, new ids get no row (their lookups pool to
   nothing; rows are never freed, so such an id never gets one); with
   insertion off, unseen ids get no row.
+* A lookup that finds no row (a hashed id without one, or an index outside
+  its table) -- the pages do not say how it pools. Read here as: it adds
+  nothing, and it is still one of its bag's lookups, so mean pooling divides
+  by the bag length the offsets give (forward), and every lookup of the bag
+  scales its gradient by 1/that length (backward); the row-less lookup itself
+  has no gradient row.
 * Untouched rows -- a dense step with g = 0 and G = 0 leaves w and G bit for
   bit unchanged, so only touched rows are computed.
 * Table contents -- synthetic: each element is a counter hash of (seed, table,
@@ -72,7 +78,7 @@ __all__ = [
     "to_storage", "TouchedRows", "pooled_forward", "global_keys", "dedup",
     "bag_of_positions", "reduced_grad", "sgd_step", "adagrad_step",
     "update_rows", "update_rows_master", "SHARD_TABLE", "SHARD_ROW_CYCLIC", "SHARD_ROW_BLOCK",
-    "shard_of_keys", "pack_by_shard", "HashTables",
+    "shard_of_keys", "pack_by_shard", "HashTables", "pooled_forward_hashed",
 ]
 
 _U64 = np.uint64
@@ -183,12 +189,20 @@ def bag_of_positions(offsets: np.ndarray, T: int, B: int) -> np.ndarray:
     return np.repeat(np.arange(T * B, dtype=np.int64), lengths)
 
 
-def pooled_forward(tables, indices, offsets, T: int, B: int, D: int, pool: str) -> np.ndarray:
+def pooled_forward(tables, indices, offsets, T: int, B: int, D: int, pool: str,
+                   num_rows=None) -> np.ndarray:
     """Y[b, t*D:(t+1)*D] = sum (or mean) over bag (t, b) of W_t[idx].
 
     ``tables[t][rows]`` must return the stored rows (any float type). Sums are
     taken in float64 and rounded once to fp32; a mean divides the float64 sum
-    by the bag length before that rounding; an empty bag gives zeros."""
+    by the bag length before that rounding; an empty bag gives zeros.
+
+    ``num_rows`` (rows per table, optional): a lookup whose index lies outside
+    [0, num_rows[t]) finds no row -- an index out of range, or a hashed id
+    that holds no row (row -1). It adds nothing to its bag's sum, and it still
+    counts as one of the bag's lookups: a mean divides by the bag length the
+    offsets give, whatever the lookups found. Without ``num_rows`` every index
+    must be a row of its table."""
     indices = np.asarray(indices, dtype=np.int64)
     offsets = np.asarray(offsets, dtype=np.int64)
     blocks = []
@@ -197,8 +211,12 @@ def pooled_forward(tables, indices, offsets, T: int, B: int, D: int, pool: str) 
         lengths = np.diff(offsets[t * B:(t + 1) * B + 1])
         local_bag = np.repeat(np.arange(B, dtype=np.int64), lengths)
         s = np.zeros((B, D), dtype=np.float64)
-        if p1 > p0:
-            rows = np.asarray(tables[t][indices[p0:p1]], dtype=np.float64).reshape(p1 - p0, D)
+        idx = indices[p0:p1]
+        if num_rows is not None:
+            found = (idx >= 0) & (idx < int(num_rows[t]))
+            idx, local_bag = idx[found], local_bag[found]
+        if idx.size:
+            rows = np.asarray(tables[t][idx], dtype=np.float64).reshape(idx.size, D)
             np.add.at(s, local_bag, rows)
         if pool == "mean":
             nz = lengths > 0
@@ -234,6 +252,8 @@ def reduced_grad(dY, offsets, T: int, B: int, D: int, pool: str, inverse, U: int
                  select: np.ndarray | None = None) -> np.ndarray:
     """gU[u] = sum over lookups i with inverse[i] == u of scale_i * dY[b(i), t(i)*D:(t(i)+1)*D],
     scale_i = 1 (sum) or 1/L(bag) (mean). float64 scatter-add, one fp32 rounding.
+    A lookup with inverse[i] < 0 found no row: it has no gradient row, and L
+    still counts it (the bag length the offsets give, as in the forward).
 
     ``select`` (sorted unique ids) restricts the result to those rows, in that
     order, for workloads too large to reduce whole."""
@@ -254,6 +274,8 @@ def reduced_grad(dY, offsets, T: int, B: int, D: int, pool: str, inverse, U: int
             continue
         lb = np.repeat(np.arange(B, dtype=np.int64), lengths[t * B:(t + 1) * B])
         inv = inverse[p0:p1]
+        has_row = inv >= 0
+        lb, inv = lb[has_row], inv[has_row]
         if target_of is not None:
             pos = np.searchsorted(target_of, inv)
             keep = (pos < target_of.size) & (target_of[np.minimum(pos, target_of.size - 1)] == inv)
@@ -412,3 +434,13 @@ class HashTables:
                     self.next_free[t] += 1
                     out[p] = m[x]
         return out
+
+
+def pooled_forward_hashed(tables, hash_tables: HashTables, ids, offsets, T: int, B: int, D: int,
+                          pool: str) -> np.ndarray:
+    """The hash lookup fused with the pooling (GTC 2022 deck, slide "HUGECTR
+    EMBEDDING LAYER"), lookup only: each id's row comes from its table's map
+    (no insertion), and the bags are pooled over those rows; an id without a
+    row adds nothing and still counts in its bag's length (mean)."""
+    rows = hash_tables.translate(ids, offsets, T, B, insert=False)
+    return pooled_forward(tables, rows, offsets, T, B, D, pool, num_rows=hash_tables.rows)

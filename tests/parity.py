@@ -62,11 +62,14 @@ class _Abs:
         return _V()
 
 
-def check_forward(Y_gpu: np.ndarray, cfg, batch, otabs, bags=None):
-    """Element-wise (or on sampled bags) forward check."""
+def check_forward(Y_gpu: np.ndarray, cfg, batch, otabs, bags=None, num_rows=None):
+    """Element-wise (or on sampled bags) forward check. num_rows: rows per
+    table when some lookups name no row (they add nothing and count in L)."""
     if bags is None:
-        ref = O.pooled_forward(otabs, batch.indices, batch.offsets, cfg.T, cfg.batch, cfg.dim, cfg.pool)
-        mag = O.pooled_forward(_Abs(otabs), batch.indices, batch.offsets, cfg.T, cfg.batch, cfg.dim, cfg.pool)
+        ref = O.pooled_forward(otabs, batch.indices, batch.offsets, cfg.T, cfg.batch, cfg.dim, cfg.pool,
+                               num_rows=num_rows)
+        mag = O.pooled_forward(_Abs(otabs), batch.indices, batch.offsets, cfg.T, cfg.batch, cfg.dim, cfg.pool,
+                               num_rows=num_rows)
         got = Y_gpu
     else:
         # sampled bags: build a sub-batch holding only them (sample b -> row j)

@@ -2,7 +2,8 @@
 emb_forward_pooled_hashed) against the oracle's HashTables: the rows handed
 out to 64-bit ids are compared bit for bit over several steps (insertion and
 lookup-only, tables filling up), and the fused hashed forward against the
-plain forward on the translated rows."""
+plain forward on the translated rows and against the oracle's hashed
+pooling (row-less ids add nothing and count in their bag's length)."""
 import gc
 
 import numpy as np
@@ -112,21 +113,19 @@ def test_fused_hashed_forward_equals_forward_on_rows(pool):
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
     with pytest.raises(E.EmbError):
         tabs.check_device_error()            # the plain forward saw rows of -1
-    # the oracle's own rows agree, and (sum pooling) so do the pooled values,
-    # row-less lookups dropped; mean divides by the whole bag and is covered
-    # by the bit equality with the plain forward above
+    # the oracle's own rows agree, and so do the pooled values: the oracle's
+    # fused lookup-only pooling, row-less ids adding nothing and (mean)
+    # counting in their bag's length
     ht = O.HashTables(rows)
     ht.translate(ids, batch.offsets, cfg.T, cfg.batch, True)
     ref_rows = ht.translate(ids2, batch.offsets, cfg.T, cfg.batch, False)
     assert np.array_equal(rows2.cpu().numpy().astype(np.int64), ref_rows)
-    if pool == "sum":
-        keep = ref_rows >= 0
-        bag = np.repeat(np.arange(cfg.T * cfg.batch), np.diff(batch.offsets))
-        sub_lens = np.bincount(bag[keep], minlength=cfg.T * cfg.batch).reshape(cfg.T, cfg.batch)
-        kept = ref_rows[keep]
-        cut = np.concatenate([[0], np.cumsum(sub_lens.sum(axis=1))])
-        sub = W.make_batch_from_lengths(list(sub_lens), [kept[cut[t]:cut[t + 1]] for t in range(cfg.T)], cfg.batch)
-        P.check_forward(a, cfg, sub, P.oracle_tables(cfg, sub))
+    assert (ref_rows < 0).sum() > 0.1 * len(ref_rows)     # the case is exercised
+    rbatch = W.Batch(ref_rows, batch.offsets, batch.lengths, cfg.T, cfg.batch)
+    otabs = P.oracle_tables(cfg, rbatch)
+    Y_ref = O.pooled_forward_hashed(otabs, ht, ids2, batch.offsets, cfg.T, cfg.batch, cfg.dim, pool)
+    ref = P.check_forward(a, cfg, rbatch, otabs, num_rows=rows)
+    assert np.array_equal(ref.view(np.uint32), Y_ref.view(np.uint32))
     tabs.close()
 
 

@@ -121,6 +121,116 @@ def test_integer_grad_bit_exact(cfg_id, opt):
         assert np.array_equal(r["G_new"].view(np.uint32), G_ref.view(np.uint32))
 
 
+# 16-bit storage: integer dY, sum pooling and lr = 2^-7 make the fp32 step
+# exact up to its own IEEE roundings (SGD: one subtraction; Adagrad: sqrt,
+# add, divide, subtract), so the stored bf16 / fp16 bits -- the
+# round-to-nearest-even write-back, or the master and its RNE copy -- must
+# equal the oracle's bit for bit. A truncating write-back differs from RNE in
+# about half the elements and fails here; the 2e-2 band cannot tell them apart.
+LOWP_EXACT = [(4, "sgd", False), (4, "sgd", True), (4, "adagrad", False),
+              (5, "sgd", False), (5, "adagrad", False), (5, "adagrad", True)]
+
+
+@pytest.mark.parametrize("cfg_id,opt,master", LOWP_EXACT)
+def test_integer_grad_bit_exact_low_precision(cfg_id, opt, master):
+    from dataclasses import replace
+    base = W.make_config(cfg_id, rows=2_000_000, **REDUCED[cfg_id])
+    if opt == "adagrad" and base.opt != "adagrad":
+        # Adagrad on a bf16 table that carries no state in its own workload
+        base = replace(base, opt="adagrad")
+    cfg = replace(base, pool="sum", opt=opt, lr=2.0 ** -7, eps=1e-8)
+    batch = W.make_batch(cfg)
+    dY = W.make_int_dy(cfg)
+    _say(f"int-grad {cfg.dtype} cfg{cfg_id} {opt} master={master} N={batch.N}")
+    tabs = P.make_tables(cfg, master=master)
+    r = P.run_step(cfg, batch, dY, path="fused", tabs=tabs, sample_untouched=200, master=master)
+    u, c, inv = P.oracle_dedup(cfg, batch)
+    g = O.reduced_grad(dY, batch.offsets, cfg.T, cfg.batch, cfg.dim, cfg.pool, inv, len(u))
+    assert np.all(np.abs(g) < 2 ** 24) and np.array_equal(g, np.round(g))   # every sum exact
+    G_old = np.zeros((len(u), cfg.dim), np.float32) if opt == "adagrad" else None
+    if master:
+        m_old = P.stored_init(cfg, u, rounded=False)
+        m_ref, w_ref, G_ref = O.update_rows_master(m_old, G_old, g, opt, cfg.lr, cfg.eps, cfg.dtype)
+        m_new = P.read_master(tabs, cfg, u)
+        assert np.array_equal(m_new.view(np.uint32), m_ref.view(np.uint32)), "master differs"
+    else:
+        w_old = P.stored_init(cfg, u)
+        w_ref, G_ref = O.update_rows(w_old, G_old, g, opt, cfg.lr, cfg.eps, cfg.dtype)
+    moved = np.mean(w_ref != P.stored_init(cfg, u))
+    assert moved > 0.5, moved                      # the step is visible in the stored type
+    bad = r["w_new"].view(np.uint32) != w_ref.view(np.uint32)
+    assert not bad.any(), f"{int(bad.sum())} of {bad.size} stored elements differ from the oracle's RNE"
+    if opt == "adagrad":
+        assert np.array_equal(r["G_new"].view(np.uint32), G_ref.view(np.uint32))
+    tabs.close()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_out_of_range_mean_matches_oracle(dtype):
+    # mean pooling over bags that hold indices outside their table: such a
+    # lookup adds nothing and still counts in its bag's length, in the forward
+    # and in the 1/L of its bag's other lookups in the backward (the oracle's
+    # definition); its own key is the never-applied sentinel
+    rng = np.random.default_rng(17)
+    rows = [40, 900, 7]
+    cfg = _custom_cfg(rows, dim=32, dtype=dtype, B=300, pool="mean", opt="sgd")
+    lens = [rng.integers(0, 6, cfg.batch) for _ in rows]
+    keys = []
+    for t, r in enumerate(rows):
+        k = rng.integers(0, r, int(lens[t].sum()))
+        bad = rng.random(len(k)) < 0.3
+        k[bad] = np.where(rng.random(int(bad.sum())) < 0.5, -1 - rng.integers(0, 5, int(bad.sum())),
+                          r + rng.integers(0, 5, int(bad.sum())))
+        keys.append(k)
+    batch = W.make_batch_from_lengths(lens, keys, cfg.batch, index_dtype=np.int64)
+    dY = rng.standard_normal((cfg.batch, cfg.T * cfg.dim)).astype(np.float32)
+    _say("out-of-range mean", dtype, batch.N)
+    tabs = P.make_tables(cfg)
+    idx, off, dy = P.to_dev(batch, dY)
+    Y = tabs.forward(idx, off, cfg.batch, "mean")
+    torch.cuda.synchronize()
+    with pytest.raises(E.EmbError) as ei:
+        tabs.check_device_error()
+    assert ei.value.code == E.EMB_E_BOUNDS
+    otabs = P.oracle_tables(cfg, batch)
+    P.check_forward(Y.cpu().numpy(), cfg, batch, otabs, num_rows=rows)
+    bufs = tabs.backward_buffers(batch.N, cfg.batch, with_grad=True)
+    tabs.backward(idx, off, cfg.batch, "mean", dy, bufs)
+    torch.cuda.synchronize()
+    # in-range keys, counts and inverse as the oracle's dedup of the lookups
+    # that found a row; row-less lookups point at the sentinel key
+    ro = cfg.row_offset()
+    t_of = np.repeat(np.arange(cfg.T), np.diff(batch.offsets[::cfg.batch].astype(np.int64)))
+    found = (batch.indices >= 0) & (batch.indices < np.asarray(rows)[t_of])
+    g_all = ro[t_of] + batch.indices
+    u, c, inv_f = O.dedup(g_all[found])
+    U = int(bufs["num_unique"].item())
+    uk = bufs["unique_keys"][:U].cpu().numpy().view(np.uint32).astype(np.int64)
+    cg = bufs["counts"][:U].cpu().numpy().astype(np.int64)
+    inv_g = bufs["inverse"][:batch.N].cpu().numpy().astype(np.int64)
+    valid = uk < cfg.total_rows
+    assert np.array_equal(uk[valid], u) and np.array_equal(cg[valid], c)
+    assert np.array_equal(uk[inv_g[found]], g_all[found])
+    assert np.all(uk[inv_g[~found]] == cfg.total_rows)
+    inv = np.full(batch.N, -1, np.int64)
+    inv[found] = inv_f
+    g_ref = O.reduced_grad(dY, batch.offsets, cfg.T, cfg.batch, cfg.dim, "mean", inv, len(u))
+    m_ref = O.reduced_grad(np.abs(dY), batch.offsets, cfg.T, cfg.batch, cfg.dim, "mean", inv, len(u))
+    slot = np.nonzero(valid)[0]
+    P.check_grad(bufs["reduced_grad"][torch.from_numpy(slot).cuda()].cpu().numpy(), g_ref, m_ref)
+    tabs.update("sgd", cfg.lr, 0.0, bufs, dY=dy)
+    torch.cuda.synchronize()
+    with pytest.raises(E.EmbError):
+        tabs.check_device_error()
+    w_new, _ = P.read_rows(tabs, cfg, u)
+    P.check_update(cfg, w_new, None, P.stored_init(cfg, u), None, g_ref, m_ref)
+    # rows no lookup found are untouched
+    rest = np.setdiff1d(np.arange(cfg.total_rows), u)
+    w_rest, _ = P.read_rows(tabs, cfg, rest)
+    assert np.array_equal(w_rest.view(np.uint32), P.stored_init(cfg, rest).view(np.uint32))
+    tabs.close()
+
+
 def test_fused_equals_materialized_and_reruns_bit_identical():
     cfg = W.make_config(2, batch=4096)
     batch = W.make_batch(cfg, k=3)

@@ -240,6 +240,153 @@ def test_forward_pin_catches_mistakes():
 
 
 # ---------------------------------------------------------------------------
+# Lookups that find no row (an index outside its table, a hashed id without a
+# row): they add nothing and still count in their bag's length
+# ---------------------------------------------------------------------------
+
+def _rowless_case(seed, T=3, B=9, rows=(11, 5, 23), D=6):
+    """A small batch in which about a third of the lookups name no row: -1,
+    an index past the table, or a large negative one."""
+    tables, batch, D = _small_case(seed, T=T, B=B, rows=rows, D=D, max_len=6, empty_every=4)
+    rng = np.random.default_rng(100 + seed)
+    idx = batch.indices.astype(np.int64).copy()
+    t_of = np.repeat(np.arange(T), np.diff(batch.offsets[::B].astype(np.int64)))
+    bad = rng.random(len(idx)) < 0.35
+    kinds = rng.integers(0, 3, len(idx))
+    past = np.asarray(rows)[t_of] + rng.integers(0, 4, len(idx))
+    idx[bad & (kinds == 0)] = -1
+    idx[bad & (kinds == 1)] = past[bad & (kinds == 1)]
+    idx[bad & (kinds == 2)] = -(2 ** 40)
+    rb = W.Batch(idx, batch.offsets, batch.lengths, T, B)
+    return tables, rb, D, list(rows)
+
+
+def _torch_weighted_forward(tables, batch, D, pool, rows):
+    """torch's embedding_bag in sum mode with per-lookup weights: 1 (sum) or
+    1/L (mean) for a lookup that finds a row, 0 for one that does not (its
+    index clamped to row 0, so it reads a real row and adds 0 times it)."""
+    T, B = batch.T, batch.B
+    out = []
+    for t in range(T):
+        o0, o1 = int(batch.offsets[t * B]), int(batch.offsets[(t + 1) * B])
+        lens = np.diff(batch.offsets[t * B:(t + 1) * B + 1].astype(np.int64))
+        idx = batch.indices[o0:o1].astype(np.int64)
+        found = (idx >= 0) & (idx < rows[t])
+        scale = np.repeat(1.0 / np.maximum(lens, 1), lens) if pool == "mean" else np.ones(len(idx))
+        wgt = np.where(found, scale, 0.0)
+        off = torch.from_numpy((batch.offsets[t * B:(t + 1) * B] - o0).astype(np.int64))
+        out.append(torch.nn.functional.embedding_bag(
+            torch.from_numpy(np.where(found, idx, 0)), torch.from_numpy(tables[t].astype(np.float64)), off,
+            mode="sum", per_sample_weights=torch.from_numpy(wgt)))
+    return torch.cat(out, dim=1).numpy()
+
+
+def _rowless_pin_ok(fwd, tables, batch, D, pool, rows):
+    got = fwd(tables, batch.indices, batch.offsets, batch.T, batch.B, D, pool, num_rows=rows)
+    ref = _torch_weighted_forward(tables, batch, D, pool, rows).astype(np.float32)
+    return got.shape == ref.shape and _f32_ulp_close(got, ref, 1)
+
+
+@pytest.mark.parametrize("pool", ["sum", "mean"])
+def test_forward_rowless_vs_torch_weighted_bag(pool):
+    for seed in range(6):
+        tables, batch, D, rows = _rowless_case(seed)
+        assert _rowless_pin_ok(O.pooled_forward, tables, batch, D, pool, rows)
+
+
+def test_forward_rowless_bruteforce_loops():
+    tables, batch, D, rows = _rowless_case(3, T=2, B=6, rows=(7, 4), D=3)
+    got = O.pooled_forward(tables, batch.indices, batch.offsets, batch.T, batch.B, D, "mean", num_rows=rows)
+    for t in range(batch.T):
+        for b in range(batch.B):
+            lo, hi = int(batch.offsets[t * batch.B + b]), int(batch.offsets[t * batch.B + b + 1])
+            acc = [0.0] * D
+            for i in range(lo, hi):
+                r = int(batch.indices[i])
+                if 0 <= r < rows[t]:
+                    for c in range(D):
+                        acc[c] += float(tables[t][r, c])
+            for c in range(D):
+                assert got[b, t * D + c] == np.float32(acc[c] / (hi - lo) if hi > lo else 0.0)
+
+
+def test_forward_rowless_closed_forms():
+    rng = np.random.default_rng(4)
+    W0 = rng.standard_normal((5, 4)).astype(np.float32)
+    # bag 0: only lookups without a row; bag 1: row 3 and two without one;
+    # bag 2: row 2 alone; bag 3: empty
+    idx = np.array([-1, 5, 3, -7, 9, 2])
+    off = np.array([0, 2, 5, 6, 6])
+    for pool in ("sum", "mean"):
+        Y = O.pooled_forward([W0], idx, off, 1, 4, 4, pool, num_rows=[5])
+        assert np.all(Y[0] == 0) and np.all(Y[3] == 0)
+        assert np.array_equal(Y[2], W0[2])
+        if pool == "sum":
+            assert np.array_equal(Y[1], W0[3])
+        else:                                   # one row over a bag of three
+            assert np.array_equal(Y[1], (W0[3].astype(np.float64) / 3).astype(np.float32))
+
+
+def test_forward_rowless_pin_catches_mistakes():
+    def kept_count_mean(tabs, idx, off, T, B, D_, pool, num_rows=None):
+        # mean over the lookups that found a row only
+        idx = np.asarray(idx, np.int64)
+        off = np.asarray(off, np.int64)
+        t_of = np.repeat(np.arange(T), np.diff(off[::B]))
+        keep = (idx >= 0) & (idx < np.asarray(num_rows)[t_of])
+        bag = np.repeat(np.arange(T * B), np.diff(off))
+        lens = np.bincount(bag[keep], minlength=T * B)
+        return O.pooled_forward(tabs, idx[keep], np.concatenate([[0], np.cumsum(lens)]), T, B, D_, pool)
+
+    def wraps_negative(tabs, idx, off, T, B, D_, pool, num_rows=None):
+        # -1 read as the table's last row (numpy's negative indexing)
+        idx = np.asarray(idx, np.int64).copy()
+        t_of = np.repeat(np.arange(T), np.diff(np.asarray(off, np.int64)[::B]))
+        m = idx == -1
+        idx[m] = np.asarray(num_rows)[t_of[m]] - 1
+        return O.pooled_forward(tabs, idx, off, T, B, D_, pool, num_rows=num_rows)
+
+    found_mean = found_wrap = False
+    for seed in range(6):
+        tables, batch, D, rows = _rowless_case(seed)
+        found_mean |= not _rowless_pin_ok(kept_count_mean, tables, batch, D, "mean", rows)
+        found_wrap |= not _rowless_pin_ok(wraps_negative, tables, batch, D, "sum", rows)
+    assert found_mean and found_wrap
+
+
+@pytest.mark.parametrize("pool", ["sum", "mean"])
+def test_reduced_grad_rowless_vs_autograd(pool):
+    # a lookup without a row has inverse -1: no gradient row of its own, and
+    # the 1/L of its bag's other lookups counts it
+    for seed in range(3):
+        tables, batch, D, rows = _rowless_case(seed + 20)
+        dY = np.random.default_rng(seed).standard_normal((batch.B, batch.T * D)).astype(np.float32)
+        ro = np.concatenate([[0], np.cumsum(rows)])
+        t_of = np.repeat(np.arange(batch.T), np.diff(batch.offsets[::batch.B].astype(np.int64)))
+        idx = batch.indices.astype(np.int64)
+        found = (idx >= 0) & (idx < np.asarray(rows)[t_of])
+        g = ro[t_of] + idx
+        u = np.unique(g[found])
+        inv = np.where(found, np.searchsorted(u, g), -1)
+        gU = O.reduced_grad(dY, batch.offsets, batch.T, batch.B, D, pool, inv, len(u))
+        ws = [torch.tensor(t.astype(np.float64), requires_grad=True) for t in tables]
+        outs = []
+        for t in range(batch.T):
+            o0, o1 = int(batch.offsets[t * batch.B]), int(batch.offsets[(t + 1) * batch.B])
+            lens = np.diff(batch.offsets[t * batch.B:(t + 1) * batch.B + 1].astype(np.int64))
+            f = found[o0:o1]
+            sc = np.repeat(1.0 / np.maximum(lens, 1), lens) if pool == "mean" else np.ones(o1 - o0)
+            off = torch.from_numpy((batch.offsets[t * batch.B:(t + 1) * batch.B] - o0).astype(np.int64))
+            outs.append(torch.nn.functional.embedding_bag(
+                torch.from_numpy(np.where(f, idx[o0:o1], 0)), ws[t], off, mode="sum",
+                per_sample_weights=torch.from_numpy(np.where(f, sc, 0.0))))
+        (torch.cat(outs, dim=1) * torch.from_numpy(dY.astype(np.float64))).sum().backward()
+        for j, key in enumerate(u.tolist()):
+            t = int(np.searchsorted(ro, key, side="right") - 1)
+            assert _f32_ulp_close(gU[j], ws[t].grad.numpy()[key - int(ro[t])].astype(np.float32), 1)
+
+
+# ---------------------------------------------------------------------------
 # Keys and dedup
 # ---------------------------------------------------------------------------
 
@@ -783,3 +930,27 @@ def test_hash_pin_catches_mistakes():
     assert ok(O.HashTables)
     assert not ok(LastSight)
     assert not ok(SharedCounter)
+
+
+@pytest.mark.parametrize("pool", ["sum", "mean"])
+def test_pooled_forward_hashed_vs_independent_lookup(pool):
+    # the fused lookup-only pooling over a map state built by insertion:
+    # rows from the independent numpy translation, pooled by torch's weighted
+    # embedding_bag (a row-less id weighs 0 and counts in L)
+    for seed in range(20):
+        T, B, rows, ids, offsets = _hash_case(seed)
+        ht = O.HashTables(rows)
+        state = ([dict() for _ in rows], [0] * T)
+        ht.translate(ids, offsets, T, B, True)
+        _translate_numpy(ids, offsets, T, B, rows, True, state)
+        ids2 = np.roll(ids, 5)
+        ids2[::4] = 1234567                      # never inserted
+        rng = np.random.default_rng(seed)
+        D = 3
+        tables = [rng.standard_normal((r, D)).astype(np.float32) for r in rows]
+        got = O.pooled_forward_hashed(tables, ht, ids2, offsets, T, B, D, pool)
+        r_np = _translate_numpy(ids2, offsets, T, B, rows, False, state)
+        lens = np.diff(offsets)
+        batch = W.Batch(r_np, offsets, lens, T, B)
+        ref = _torch_weighted_forward(tables, batch, D, pool, rows).astype(np.float32)
+        assert _f32_ulp_close(got, ref, 1), seed
