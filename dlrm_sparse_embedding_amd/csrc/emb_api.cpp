@@ -793,6 +793,40 @@ int emb_hash_translate(emb_ctx* ctx, const int64_t* ids, const void* offsets, in
   return ok();
 }
 
+int emb_hash_translate_noalloc(emb_ctx* ctx, const int64_t* ids, const void* offsets, int32_t itype, int64_t N,
+                               int32_t B, int32_t insert, void* rows_out, void* hip_stream) {
+  int rc = check_lookup_args(ctx, ids, offsets, itype, N, B);
+  if (rc) return rc;
+  if (N > 0 && !rows_out) return fail(EMB_E_INVAL, "rows_out is NULL");
+  const HashWs L = hash_ws(ctx, N);
+  if (L.total > kHashNoAllocBytes)
+    return fail(EMB_E_WORKSPACE, "%lld lookups need %zu bytes of scratch, more than the %zu the translation "
+                "without allocation holds (use emb_hash_translate with a workspace)",
+                (long long)N, L.total, kHashNoAllocBytes);
+  if (N == 0) return ok();
+  // the maps are attached, so the context's device block exists: nothing is
+  // allocated here, and the device must be the context's
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != ctx->device)
+    return fail(EMB_E_INVAL, "the context lives on device %d but device %d is current", ctx->device, dev);
+  void* scr = nullptr;
+  if ((e = hash_noalloc_scratch(dev, &scr)) != hipSuccess) return hip_fail(e, "translation scratch address");
+  char* w = static_cast<char*>(scr);
+  HashScratch hs;
+  hs.slot_of_pos = reinterpret_cast<int*>(w + L.slot_of_pos);
+  hs.pkeys = reinterpret_cast<unsigned long long*>(w + L.pkeys);
+  hs.paux = reinterpret_cast<int*>(w + L.paux);
+  hs.pval = reinterpret_cast<int*>(w + L.pval);
+  hs.blk = reinterpret_cast<uint32_t*>(w + L.blk);
+  hs.rank_base = reinterpret_cast<int*>(w + L.rank_base);
+  e = launch_hash_translate(ctx->hv, ctx->dc, ctx->g.T, reinterpret_cast<const long long*>(ids), offsets, itype,
+                            (int)N, B, insert != 0, hs, rows_out, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "hash translation");
+  return ok();
+}
+
 int emb_forward_pooled_hashed(emb_ctx* ctx, const int64_t* ids, const void* offsets, int32_t itype, int64_t N,
                               int32_t B, int32_t pool, float* out, void* hip_stream) {
   int rc = check_lookup_args(ctx, ids, offsets, itype, N, B);

@@ -55,6 +55,11 @@ constexpr int kMasterBit = 8;
 // by the update kernels (4 bytes per entry).
 constexpr int kMaxTables = 4096;
 
+// Scratch of the translation that allocates nothing: a fixed device array per
+// GPU (k_hash.hip), enough for about 1.8 M lookups.
+constexpr size_t kHashNoAllocBytes = 64ull << 20;
+constexpr int kMaxDevices = 64;
+
 // Segment chunking of the sorted lookups (see the reduce kernels): every
 // segment is cut at multiples of kChunk sorted positions (level-0 tiles);
 // partial sums of segments longer than a tile are combined per level-1 tile
@@ -206,6 +211,9 @@ hipError_t launch_combine(const Geom& g, const DevCtx& dc, int mode, int N, cons
 // hash-keyed lookup (k_hash.hip)
 hipError_t launch_hash_clear(const HashView& h, int T, hipStream_t st);
 // rows_out has the integer type `itype`
+// Device address of the fixed translation scratch (kHashNoAllocBytes) on
+// `device`, which must be current: looked up once per device, then cached.
+hipError_t hash_noalloc_scratch(int device, void** out);
 hipError_t launch_hash_translate(const HashView& h, const DevCtx& dc, int T, const long long* ids,
                                  const void* offsets, int itype, int N, int B, bool insert, const HashScratch& w,
                                  void* rows_out, hipStream_t st);

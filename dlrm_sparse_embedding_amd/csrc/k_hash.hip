@@ -27,9 +27,37 @@
 //           inserted into the table's map
 //   fill    thread per lookup: rows_out from the pending slot of a new id
 //   advance per table: next_free += its first sights (capped at rows)
+#include <mutex>
+
 #include "emb_device.h"
 
 namespace emb {
+
+// Scratch of emb_hash_translate_noalloc, for callers that cannot allocate
+// device memory: one copy per GPU, held until the process ends. Host code
+// never passes this name to a kernel (on the host it is only a stand-in for
+// the symbol); it takes the device address from hash_noalloc_scratch.
+static __device__ __align__(256) unsigned char scratch[kHashNoAllocBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t hash_noalloc_scratch(int device, void** out) {
+  *out = nullptr;
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[device] = p;
+  }
+  *out = g_scratch_ptr[device];
+  return hipSuccess;
+}
 
 constexpr int kTile = 2048;  // lookups per count / assign block (8 per thread)
 

@@ -114,6 +114,8 @@ def lib() -> ctypes.CDLL:
     L.emb_hash_workspace_bytes.restype = sz
     L.emb_hash_translate.argtypes = [vp, vp, vp, i32, i64, i32, i32, vp, sz, vp, vp]
     L.emb_hash_translate.restype = ctypes.c_int
+    L.emb_hash_translate_noalloc.argtypes = [vp, vp, vp, i32, i64, i32, i32, vp, vp]
+    L.emb_hash_translate_noalloc.restype = ctypes.c_int
     L.emb_forward_pooled_hashed.argtypes = [vp, vp, vp, i32, i64, i32, i32, vp, vp]
     L.emb_forward_pooled_hashed.restype = ctypes.c_int
     L.emb_hash_rows_used.argtypes = [vp, vp, vp]
@@ -276,6 +278,16 @@ def emb_hash_translate(ctx: int, ids, offsets, B: int, insert: bool, ws, rows_ou
     _check(lib().emb_hash_translate(ctx, _ptr(ids), _ptr(offsets), _itype(offsets), int(ids.numel()), int(B),
                                     1 if insert else 0, _ptr(ws), int(ws.numel() * ws.element_size()),
                                     _ptr(rows_out), _stream(stream)))
+
+
+def emb_hash_translate_noalloc(ctx: int, ids, offsets, B: int, insert: bool, rows_out, stream=None) -> None:
+    """emb_hash_translate without a workspace (the library's fixed scratch)."""
+    if ids.dtype != torch.int64:
+        raise ValueError("ids must be int64")
+    if rows_out.dtype != offsets.dtype:
+        raise ValueError("rows_out must have the offsets' integer type")
+    _check(lib().emb_hash_translate_noalloc(ctx, _ptr(ids), _ptr(offsets), _itype(offsets), int(ids.numel()),
+                                            int(B), 1 if insert else 0, _ptr(rows_out), _stream(stream)))
 
 
 def emb_forward_pooled_hashed(ctx: int, ids, offsets, B: int, pool: str, out, stream=None) -> None:

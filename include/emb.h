@@ -340,6 +340,21 @@ int emb_hash_translate(emb_ctx* ctx, const int64_t* ids, const void* offsets, in
                        int64_t N, int32_t B, int32_t insert, void* ws, size_t ws_bytes,
                        void* rows_out, void* hip_stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * translation as emb_hash_translate, same arguments and results, with its
+ * scratch in a fixed 64 MiB device array the library holds on every GPU it
+ * runs on (until the process ends) instead of a caller workspace. Allocates
+ * nothing and records no timing events. N is limited to what fits:
+ * emb_hash_workspace_bytes(ctx, N) <= 64 MiB (about 1.8 M lookups), else
+ * EMB_E_WORKSPACE. The array is shared by every call on one GPU and keeps the
+ * last call's contents (each call clears what it needs), so calls that
+ * overlap on one GPU -- on two streams, or from two threads -- race and give
+ * undefined results; order them. EMB_E_STATE if no map memory is attached;
+ * EMB_E_INVAL if the current device is not the context's. */
+int emb_hash_translate_noalloc(emb_ctx* ctx, const int64_t* ids, const void* offsets, int32_t itype,
+                               int64_t N, int32_t B, int32_t insert, void* rows_out, void* hip_stream);
+
 /* Fused hash lookup + pooled forward (lookup only, no insertion): as
  * emb_forward_pooled with each lookup's row found in its table's map; an id
  * without a row contributes nothing (no error) and still counts in its bag's
