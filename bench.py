@@ -81,6 +81,12 @@ def parse():
     ap.add_argument("--ceiling", action="store_true",
                     help="only time plain library kernels (copy, read-only sum, fill) over 4 GiB: the "
                          "practical HBM ceiling the path's kernels are compared with")
+    ap.add_argument("--ahead", type=int, default=1, choices=[1, 2],
+                    help="pipeline schedule: how many batches ahead the dedup runs (1: the next batch's "
+                         "dedup runs beside the current forward and update; 2: two batches ahead, with a "
+                         "third workspace)")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="skip the per-configuration block (configs 1, 2, 4, 5 after the headline)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times) and exit: the reference "
                          "point for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -92,21 +98,22 @@ def kernel_source_sha(name: str) -> str:
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, workload_tag: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None if there is none or the kernel source changed since it was taken."""
+def measured_counters(kernel: str, workload_tag: str):
+    """(HBM bytes per launch, L2 hit rate) from the committed rocprofv3
+    counter summary of the kernel on this workload; None for either if there
+    is no summary, it lacks the figure, or the kernel source changed since the
+    counters were taken."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload_tag}_counters.md")
     if not os.path.exists(path):
-        return None
+        return None, None
     txt = open(path).read()
     m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    m_h = re.search(r"l2_hit_rate:\s*([0-9.]+)", txt)
     m_s = re.search(r"source_sha256_16:\s*([0-9a-f]+)", txt)
     m_f = re.search(r"source_file:\s*(\S+)", txt)
-    if not (m_b and m_s and m_f):
-        return None
-    if kernel_source_sha(m_f.group(1)) != m_s.group(1):
-        return None
-    return float(m_b.group(1))
+    if not (m_s and m_f) or kernel_source_sha(m_f.group(1)) != m_s.group(1):
+        return None, None
+    return (float(m_b.group(1)) if m_b else None), (float(m_h.group(1)) if m_h else None)
 
 
 def main() -> int:
@@ -152,6 +159,42 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n * 4, "launches": 5}), flush=True)
         return 0
+
+    out = run_workload(args)
+    if isinstance(out, int):
+        return out
+    per_config_ok = (args.config == 3 and not args.no_per_config and not args.single_schedule and
+                     not (args.pack or args.hashed or args.unique_forward or args.master or args.uniform_keys or
+                          args.rows or args.reduce != "fused"))
+    if per_config_ok:
+        # the other workloads, each alone on the GPU after the headline (tables
+        # freed in between); fewer steps and a shorter oracle sample each
+        import gc
+        per = {}
+        for c in (1, 2, 4, 5):
+            sub = argparse.Namespace(**vars(args))
+            sub.config = c
+            sub.steps = min(args.steps, 10)
+            sub.warmup = min(args.warmup, 3)
+            sub.batches = 2 if c == 4 else min(args.batches, 4)
+            sub.cpu_seconds = min(args.cpu_seconds, 3.0)
+            sub.single_schedule = True          # the timed schedule only: no comparison or isolated pass
+            gc.collect()
+            torch.cuda.empty_cache()
+            print(f"[bench] per-config: config {c}", file=sys.stderr, flush=True)
+            per[f"cfg{c}"] = run_workload(sub, compact=True)
+        out["per_config"] = per
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def run_workload(args, compact=False):
+    """Times one workload (args.config) and returns its JSON record (the
+    headline's full record, or a compact one for the per-configuration
+    block). The tables and buffers are freed before it returns."""
+    import numpy as np
+    import torch
+    from dataclasses import replace
 
     from dlrm_sparse_embedding_amd import emb as E
     from dlrm_sparse_embedding_amd import workloads as W
@@ -222,10 +265,13 @@ def main() -> int:
         torch.cuda.synchronize()
         U_of.append(int(bufs["num_unique"].item()))
 
-    # the pipeline schedule alternates two workspaces / dedup outputs
-    bufs2 = [bufs, tabs.backward_buffers(nmax, B, with_grad=args.reduce == "atomic")]
-    ev_free2 = [torch.cuda.Event(), torch.cuda.Event()]   # buffer set j free (its update done)
-    ev_dd2 = [torch.cuda.Event(), torch.cuda.Event()]     # dedup into buffer set j done
+    # the pipeline schedule cycles ahead + 1 workspaces / dedup outputs: the
+    # dedup of batch i goes to set i % nsets
+    ahead = args.ahead if args.schedule == "pipeline" else 1
+    nsets = ahead + 1
+    bufs2 = [bufs] + [tabs.backward_buffers(nmax, B, with_grad=args.reduce == "atomic") for _ in range(nsets - 1)]
+    ev_free2 = [torch.cuda.Event() for _ in range(nsets)]   # buffer set j free (its update done)
+    ev_dd2 = [torch.cuda.Event() for _ in range(nsets)]     # dedup into buffer set j done
 
     main = torch.cuda.current_stream()
     side = torch.cuda.Stream()          # default priority
@@ -236,8 +282,8 @@ def main() -> int:
 
     def issue_dedup(i):
         """Pipeline schedule: the dedup of batch i on the side stream into
-        buffer set i % 2, once that set's previous update is done."""
-        j = i % 2
+        buffer set i % nsets, once that set's previous update is done."""
+        j = i % nsets
         idx, off, _ = dev[i % len(dev)]
         side.wait_event(ev_free2[j])
         with torch.cuda.stream(side):
@@ -247,13 +293,14 @@ def main() -> int:
     def step(i, sched, evs=None, last=False):
         """One training step; evs = three timing events (start, after forward
         [+ dedup], end) recorded on the main stream. Under the pipeline
-        schedule the step's dedup was issued ahead (by the previous step or the
-        prologue) and this step issues the next batch's unless it is the last."""
+        schedule the step's dedup was issued `ahead` steps earlier (or by the
+        prologue) and this step issues batch i + ahead's unless that is past
+        the last step."""
         idx, off, n = dev[i % len(dev)]
         if evs:
             evs[0].record(main)
         if sched == "pipeline":
-            j = i % 2
+            j = i % nsets
             tabs.forward(idx, off, B, cfg.pool, out=Y)
             if evs:
                 evs[1].record(main)
@@ -261,8 +308,8 @@ def main() -> int:
             tabs.backward(idx, off, B, cfg.pool, dy, bufs2[j])   # skips the dedup done ahead
             tabs.update(cfg.opt, cfg.lr, cfg.eps, bufs2[j], dY=dy)
             ev_free2[j].record(main)
-            if not last:
-                issue_dedup(i + 1)
+            if i + ahead < nsteps[0]:
+                issue_dedup(i + ahead)
             if evs:
                 evs[2].record(main)
             return
@@ -300,12 +347,16 @@ def main() -> int:
         if evs:
             evs[2].record(main)
 
+    nsteps = [0]
+
     def run(sched, K, ev=None):
+        nsteps[0] = K
         if sched == "pipeline":
-            # the prologue dedup starts after everything before it on main
-            ev_free2[0].record(main)
-            ev_free2[1].record(main)
-            issue_dedup(0)
+            # the prologue dedups start after everything before them on main
+            for e in ev_free2:
+                e.record(main)
+            for i in range(min(ahead, K)):
+                issue_dedup(i)
         for i in range(K):
             step(i, sched, ev[i] if ev else None, last=i == K - 1)
 
@@ -419,9 +470,10 @@ def main() -> int:
         wtag = f"cfg{args.config}" + ("_uniform" if args.uniform_keys else "")
         src = {"forward": "k_forward.hip", "reduce": "k_reduce.hip", "sort_scatter": "k_keys_sort.hip",
                "sort_hist": "k_keys_sort.hip", "keys": "k_keys_sort.hip", "atomic": "k_atomic.hip"}[dominant]
+        traffic, l2_hit = measured_counters(dominant, wtag)
         return {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": measured_traffic(dominant, wtag), "alg_bytes_per_launch": int(alg),
+                "traffic": traffic, "l2_hit_rate": l2_hit, "alg_bytes_per_launch": int(alg),
                 "avg_launch_us": round(avg_us, 2), "source": src}
 
     # live: launch durations under the timed schedule (with the pipeline the
@@ -437,7 +489,7 @@ def main() -> int:
     # CPU oracle on a bounded sample of batch 0
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, host_batches, dY_host, args.cpu_sample, args.cpu_seconds)
+        cpu = cpu_baseline(cfg, host_batches, dY_host, args.cpu_sample, args.cpu_seconds, ib, args.master)
 
     ms_step = total_ms / K
     out = {
@@ -449,7 +501,8 @@ def main() -> int:
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "ms_per_step_p10_p50_p90": [pct(10), pct(50), pct(90)],
-        "schedule": args.schedule,
+        "schedule": args.schedule + (f" (dedup {ahead} batches ahead)" if args.schedule == "pipeline" and ahead > 1
+                                     else ""),
         "reduce": args.reduce if not args.pack else f"pack to {args.pack} shards (RB)",
         f"ms_per_step_{other}": round(other_ms / K, 4) if other_ms is not None else None,
         "higher_is_better": True,
@@ -472,8 +525,8 @@ def main() -> int:
         "phases": ("fwd includes the id -> row translation; " if args.hashed else "") + (
                    "fwd = dedup, then the unique-first forward (unique rows gathered once); bwd_update = "
                    if args.unique_forward else
-                   "fwd = forward (the next batch's dedup runs on a second stream alongside the forward and "
-                   "the update); bwd_update = " if args.schedule == "pipeline" else
+                   f"fwd = forward (the dedup of the batch {ahead} step(s) ahead runs on a second stream "
+                   "alongside the forward and the update); bwd_update = " if args.schedule == "pipeline" else
                    "fwd = forward with the dedup on a second stream alongside it; bwd_update = " if args.schedule == "overlap"
                    else "fwd = forward; bwd_update = dedup + ") + (
                    f"routing to {args.pack} shards + reduce into the send slots (RB)" if args.pack
@@ -492,9 +545,12 @@ def main() -> int:
     }
     if hashed_fwd:
         out["hashed"] = hashed_fwd
-    print(json.dumps(out), flush=True)
+    if compact:
+        out = {k: out[k] for k in ("value", "unit", "ms_per_step", "ms_per_step_p10_p50_p90", "schedule", "dtype",
+                                   "config", "fwd", "bwd_update", "kernels_avg_us", "roofline", "cpu_baseline")}
     tabs.close()
-    return 0
+    del tabs, dev, bufs, bufs2, dy, Y
+    return out
 
 
 def rows_desc(cfg) -> str:
@@ -525,12 +581,15 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(cfg, batches, dY, n_samples, seconds):
+def cpu_baseline(cfg, batches, dY, n_samples, seconds, ib, master=False):
     """The oracle, as it stands, on the cycled batches of the workload (the
-    first n_samples samples of each, every table; 0 = whole batches): forward,
-    dedup, reduced gradient, optimizer step. Batches are taken in turn until
-    `seconds` of CPU time have been spent. numpy's thread pools are held to one
-    thread, so `cores` is what it used."""
+    first n_samples samples of each, every table; 0 = whole batches, or as
+    many samples as hold about 2 M lookups when a batch holds more): the
+    forward, then dedup + reduced gradient + optimizer step, each phase timed
+    on its own. Batches are taken in turn until `seconds` of CPU time have
+    been spent. numpy's thread pools are held to one thread, so `cores` is
+    what it used. Algorithmic bytes per phase use the GPU's formula on the
+    sample's own N and U."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -538,10 +597,19 @@ def cpu_baseline(cfg, batches, dY, n_samples, seconds):
     from dlrm_sparse_embedding_amd import workloads as W
 
     B = cfg.batch
-    ns = B if n_samples <= 0 else min(n_samples, B)
+    if n_samples > 0:
+        ns = min(n_samples, B)
+    else:
+        nb = batches[0].N
+        ns = B if nb <= 2_000_000 else max(1, int(B * 2_000_000 / nb))
     ro = cfg.row_offset()
+    D = cfg.dim
+    rowbytes = D * W.DTYPE_BYTES[cfg.dtype]
+    state_b = D * 4 if cfg.opt == "adagrad" else 0
+    wrow_b = 2 * D * 4 + rowbytes if master else 2 * rowbytes
     total_n = total_u = 0
-    el = 0.0
+    t_fwd = t_bwd = 0.0
+    by_fwd = by_bwd = 0
     used = 0
     with threadpool_limits(limits=1):
         for batch in batches:
@@ -558,6 +626,7 @@ def cpu_baseline(cfg, batches, dY, n_samples, seconds):
                      for t in range(cfg.T)]
             t0 = time.perf_counter()
             O.pooled_forward(otabs, sub.indices, sub.offsets, cfg.T, ns, cfg.dim, cfg.pool)
+            t1 = time.perf_counter()
             g = O.global_keys(sub.indices, sub.offsets, ro, cfg.T, ns)
             u, c, inv = O.dedup(g)
             gU = O.reduced_grad(dYs, sub.offsets, cfg.T, ns, cfg.dim, cfg.pool, inv, len(u))
@@ -565,20 +634,31 @@ def cpu_baseline(cfg, batches, dY, n_samples, seconds):
             w_old = np.concatenate([otabs[t][u[t_of == t] - ro[t]] for t in range(cfg.T)])
             G_old = np.zeros_like(w_old) if cfg.opt == "adagrad" else None
             O.update_rows(w_old, G_old, gU, cfg.opt, cfg.lr, cfg.eps, cfg.dtype)
-            el += time.perf_counter() - t0
-            total_n += sub.N
-            total_u += len(u)
+            t2 = time.perf_counter()
+            n, U = sub.N, len(u)
+            t_fwd += t1 - t0
+            t_bwd += t2 - t1
+            by_fwd += n * rowbytes + n * ib + (cfg.T * ns + 1) * ib + ns * cfg.T * D * 4
+            by_bwd += (ns * cfg.T * D * 4 + n * ib + (cfg.T * ns + 1) * ib + U * (wrow_b + 2 * state_b)
+                       + U * 8 + n * 4)
+            total_n += n
+            total_u += U
             used += 1
-            if el >= seconds:
+            if t_fwd + t_bwd >= seconds:
                 break
     try:
         avail = len(os.sched_getaffinity(0))
     except Exception:
         avail = os.cpu_count()
+    el = t_fwd + t_bwd
     return {"value": round(total_n / el, 1), "unit": "lookups/s", "cores": 1, "kind": "oracle",
+            "fwd": {"s": round(t_fwd, 3), "lookups_per_s": round(total_n / t_fwd, 1),
+                    "alg_GBps": round(by_fwd / t_fwd / 1e9, 3)},
+            "bwd_update": {"s": round(t_bwd, 3), "lookups_per_s": round(total_n / t_bwd, 1),
+                           "alg_GBps": round(by_bwd / t_bwd / 1e9, 3)},
             "sample": (f"{used} batch(es) x first {ns} samples, all {cfg.T} tables ({total_n} lookups, "
-                       f"{total_u} unique keys in total): forward + dedup + reduce + optimizer, {el:.2f} s, "
-                       f"single-threaded numpy on {cpu_model()}; {avail} host cores available")}
+                       f"{total_u} unique keys in total): forward, then dedup + reduce + optimizer, "
+                       f"{el:.2f} s, single-threaded numpy on {cpu_model()}; {avail} host cores available")}
 
 
 if __name__ == "__main__":

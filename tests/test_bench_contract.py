@@ -47,5 +47,19 @@ def test_json_line_fields():
     # roofline kernel is a main-stream one
     assert d["schedule"] == "pipeline"
     assert r["kernel"] not in ("keys", "sort_hist", "sort_scan", "sort_scatter", "rle")
+    assert "traffic" in r and "l2_hit_rate" in r
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["cores"] == 1 and c["value"] > 0 and c["unit"] == d["unit"]
+    # the oracle timed per phase, with the GPU's byte formula
+    for ph in ("fwd", "bwd_update"):
+        assert c[ph]["lookups_per_s"] > 0 and c[ph]["alg_GBps"] > 0 and c[ph]["s"] > 0
+    assert "per_config" not in d          # only the headline workload carries the other configs
+
+
+@pytest.mark.gpu
+def test_pipeline_two_ahead_runs():
+    rc, out = _run(["--config", "2", "--steps", "4", "--warmup", "2", "--ahead", "2", "--no-cpu-baseline",
+                    "--single-schedule"])
+    assert rc == 0
+    d = json.loads([l for l in out.splitlines() if l.startswith("{")][0])
+    assert d["schedule"].startswith("pipeline") and d["value"] > 0
