@@ -176,10 +176,10 @@ static int calls_on(emb_ctx* c, int has_state) {
   EXPECT(emb_set_shard_map(c, r, EMB_MAX_SHARDS + 1), EMB_E_INVAL);
   EXPECT(emb_set_shard_map(c, r, 1), EMB_E_INVAL);      /* shard 1 of 1 */
   r[2].shard = 1;
-  EXPECT(emb_set_shard_map(c, r, 4), EMB_OK);      /* row blocks take shard 0 */
+  EXPECT(emb_set_shard_map(c, r, 4), EMB_E_INVAL); /* row blocks take shard 0 */
   r[2].shard = 0;
   r[1].kind = 7;
-  EXPECT(emb_set_shard_map(c, r, 4), EMB_OK);
+  EXPECT(emb_set_shard_map(c, r, 4), EMB_E_INVAL);
   r[1].kind = EMB_SHARD_ROW_CYCLIC;
   EXPECT(emb_set_shard_map(c, r, 4), EMB_OK);
   EXPECT(emb_pack_by_shard(c, ws, NULL, uk, cnt, inv, NULL, NULL), EMB_E_STATE);
