@@ -210,7 +210,8 @@ WsLayout ws_layout(const Geom& g, long long N, int B) {
   };
   L.keys_a = take(8ull * N);
   L.keys_b = take(8ull * N);
-  L.bag_of_pos = take(4ull * N);
+  L.key_of_pos = take(4ull * N);
+  L.seg_of_key = take(4ull * ((size_t)g.total_rows + (size_t)g.T));
   L.unit_grp = take(4ull * ((TB + 63) / 64 + 1));
   L.sorted_bag = take(4ull * N);
   L.inv_len = take(4ull * (TB > 0 ? TB : 1));
@@ -290,7 +291,8 @@ int emb_create_tables(const emb_table_desc* descs, int32_t num_tables, emb_ctx**
           return fail(EMB_E_INVAL, "table %d: pointers of slice %d >= col_slices must be NULL", t, s);
       }
       sum += d.rows;
-      if (sum >= (int64_t)0xFFFFFFFFll) return fail(EMB_E_INVAL, "sum of rows must be < 2^32 - 1");
+      if (sum + num_tables >= (int64_t)0xFFFFFFFFll)
+        return fail(EMB_E_INVAL, "sum of rows plus the number of tables must be < 2^32 - 1");
     }
     emb_ctx* c = new (std::nothrow) emb_ctx();
     if (!c) return fail(EMB_E_INVAL, "out of host memory");
@@ -501,7 +503,8 @@ int run_dedup(emb_ctx* ctx, const void* indices, const void* offsets, int32_t it
     RleOut o{unique_keys, counts, inverse, num_unique};
     const long long TB = (long long)ctx->g.T * B;
     const int ngrp = N == TB ? (int)((TB + 63) / 64) : 0;
-    if ((e = launch_rle(a, (int)N, ngrp, L, w, o, st)) != hipSuccess) return hip_fail(e, "run-length encode");
+    if ((e = launch_rle(ctx->g, B, a, (int)N, ngrp, L, w, o, st)) != hipSuccess)
+      return hip_fail(e, "run-length encode");
   }
   return EMB_OK;
 }

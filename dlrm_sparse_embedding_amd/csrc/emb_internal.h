@@ -112,7 +112,8 @@ struct DevCtx {
 // Workspace carve-up for the backward / update pair.
 struct WsLayout {
   size_t keys_a, keys_b;        // uint64 [N] (key << 32 | position), ping-pong
-  size_t bag_of_pos;            // int32 [N]
+  size_t key_of_pos;            // uint32 [N] key of each lookup in input order (total_rows + t: table t's sentinel)
+  size_t seg_of_key;            // int32 [total_rows + T] segment of each key present (multi-hot inverse)
   size_t unit_grp;              // int32 [ceil(T*B/64)] 1 if each of a key-build group's 64 bags is [b, b+1)
   size_t sorted_bag;            // int32 [N] bag of each sorted lookup
   size_t inv_len;               // fp32 [T*B] 1/L per bag (mean pooling)
@@ -193,8 +194,8 @@ struct RleOut {
 };
 // ngrp: key-build groups whose one-lookup-per-bag flags decide whether the
 // bag of position p is p itself (0 when N != T*B: never).
-hipError_t launch_rle(const uint64_t* sorted, int N, int ngrp, const WsLayout& L, char* ws, const RleOut& o,
-                      hipStream_t st);
+hipError_t launch_rle(const Geom& g, int B, const uint64_t* sorted, int N, int ngrp, const WsLayout& L, char* ws,
+                      const RleOut& o, hipStream_t st);
 hipError_t launch_set_empty(const WsLayout& L, char* ws, int32_t* num_unique, hipStream_t st);
 
 // mode: 0 = write reduced gradient, 1 = fused SGD, 2 = fused Adagrad.

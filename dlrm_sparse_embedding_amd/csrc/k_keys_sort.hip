@@ -1,13 +1,13 @@
 // Backward, first half: global keys and a stable device LSD radix sort of
-// (key, position) pairs.
+// (key, bag) pairs.
 //
 // The dedup is EMBark's unique-based / reduction-based compression (RecSys'24
 // article, section on embedding clusters) applied to one GPU's share: before
 // any gradient is reduced or a row is written, the step's lookups are grouped
-// by global key g = row_offset[t] + idx. Here the grouping is a sort: each
-// lookup i becomes the 64-bit word (g << 32 | i), and an LSD radix sort
-// orders the words by key, with positions ascending inside a key because
-// every pass is stable.
+// by global key g = row_offset[t] + idx. Here the grouping is a sort: lookup
+// i of bag b becomes the 64-bit word (g << 32 | b), and an LSD radix sort
+// orders the words by key, with positions (and so bags) ascending inside a
+// key because every pass is stable.
 //
 // The sort runs over segments of positions, each sorted on its own:
 //   global     one segment [0, N), digits of the key itself (key_bits bits);
@@ -51,7 +51,7 @@ struct KeysArgs {
   const void* offsets;
   const uint32_t* row_off;
   uint64_t* keys;
-  int32_t* bag_of_pos;
+  uint32_t* key_of_pos;
   float* inv_len;  // null unless mean pooling
   int32_t* seg_start;  // [T] first position of each table's bags (clamped offsets[t*B])
   int32_t* unit_grp;   // [groups] 1 if every bag of the group is [b, b+1) (its one lookup is position b)
@@ -124,10 +124,15 @@ __global__ __launch_bounds__(256) void k_keys(KeysArgs a) {
         else
           flag |= 1;
       }
-      // non-temporal: the dedup's streams should not evict the rows of the
-      // forward / update that may run beside it on another stream
-      __builtin_nontemporal_store(((uint64_t)key << 32) | (uint32_t)p, a.keys + p);
-      __builtin_nontemporal_store((int32_t)(g0 + j), a.bag_of_pos + p);
+      // The sort word carries the bag (the sort is stable, so a key's bags
+      // stay ascending); the position's key is kept in input order for the
+      // inverse, a sentinel as total_rows + its table. Non-temporal: the
+      // dedup's streams should not evict the rows of the forward / update
+      // that may run beside it on another stream.
+      const uint32_t bg = (uint32_t)(g0 + j);
+      __builtin_nontemporal_store(((uint64_t)key << 32) | bg, a.keys + p);
+      const uint32_t kp = key < a.total_rows ? key : a.total_rows + bg / (uint32_t)a.B;
+      __builtin_nontemporal_store(kp, a.key_of_pos + p);
     }
   }
   if (flag) atomicOr(a.err, flag);
@@ -141,7 +146,7 @@ hipError_t launch_keys(const Geom& g, const DevCtx& dc, const void* indices, con
   a.offsets = offsets;
   a.row_off = dc.row_off;
   a.keys = reinterpret_cast<uint64_t*>(ws + L.keys_a);
-  a.bag_of_pos = reinterpret_cast<int32_t*>(ws + L.bag_of_pos);
+  a.key_of_pos = reinterpret_cast<uint32_t*>(ws + L.key_of_pos);
   a.inv_len = pool == EMB_POOL_MEAN ? reinterpret_cast<float*>(ws + L.inv_len) : nullptr;
   a.seg_start = reinterpret_cast<int32_t*>(ws + L.seg_start);
   a.unit_grp = reinterpret_cast<int32_t*>(ws + L.unit_grp);

@@ -1,7 +1,16 @@
 // Backward, second half of the dedup: run-length encoding of the sorted
-// (key, position) words into the unique keys, their counts, each lookup's
+// (key, bag) words into the unique keys, their counts, each lookup's
 // segment id (inverse) and the chunking of every segment used by the
 // gradient reduction.
+//
+// The inverse: on a batch of one lookup per bag at the bag's own index
+// (one-hot features) a word's bag is its input position, so the encoder
+// stores inverse[bag] = segment directly. Any other batch holds many
+// lookups per key (a multi-hot batch: 78 M lookups of 5.7 M keys in the
+// 100-table workload), so the encoder writes one entry per segment into a
+// map from key to segment, and k_inverse reads each lookup's key in input
+// order and gathers its segment: coalesced stores and mostly cached gathers
+// in place of one scattered 4-byte store per lookup.
 //
 // A segment starts where the key changes. A chunk starts at every segment
 // start and at every multiple of kChunk sorted positions, so every chunk lies
@@ -128,7 +137,9 @@ __global__ __launch_bounds__(256) void k_rle_scan(u4* __restrict__ blk, int nblk
 struct RleArgs {
   const uint64_t* sorted;
   const u4* blk;
-  const int32_t* bag_of_pos;
+  int32_t* seg_of_key;  // [total_rows + T] (batches that are not one lookup per bag)
+  uint32_t total_rows;
+  int B;
   uint32_t* unique_keys;
   int32_t* inverse;
   int32_t* seg_off;
@@ -189,32 +200,27 @@ __global__ __launch_bounds__(256) void k_rle_write(RleArgs a) {
     pc += s_wc[w];
     pm = max(pm, s_wm[w]);
   }
-  // gathers first (independent across items), stores after, so the loads
-  // of all items are in flight together
-  // one lookup per bag at the bag's own index (one-hot features): the bag of
-  // position p is p, and the random gathers of bag_of_pos are skipped
+  // one lookup per bag at the bag's own index (one-hot features): a word's
+  // bag is its input position, and the inverse is stored directly
   const bool unit = bp.w != 0u;
-  const int32_t* __restrict__ bag_of_pos = a.bag_of_pos;
   const uint64_t* __restrict__ sorted = a.sorted;
   int32_t bag[kSortIPT], cbv[kSortIPT], bag0[kSortIPT];
 #pragma unroll
   for (int k = 0; k < kSortIPT; ++k) {
     const long long i = base + k * 64 + lane;
-    const uint32_t pos = (uint32_t)item[k];
-    bag[k] = (i < a.N && pos < (uint32_t)a.N) ? (unit ? (int32_t)pos : bag_of_pos[pos]) : -1;
+    bag[k] = i < a.N ? (int32_t)(uint32_t)item[k] : -1;
     // chunk start: the later of its segment's start and its tile's start
     const int32_t seg_start = (int32_t)max(pm, im[k]) - 1;
     const int32_t tile0 = (int32_t)((i / kChunk) * kChunk);
     cbv[k] = seg_start > tile0 ? seg_start : tile0;
   }
+  // the bag of each chunk's first lookup (loads first, stores after, so the
+  // loads of all items are in flight together)
 #pragma unroll
   for (int k = 0; k < kSortIPT; ++k) {
     const long long i = base + k * 64 + lane;
     bag0[k] = bag[k];
-    if (i < a.N && (fl & (1u << (24 + k))) && cbv[k] != (int32_t)i) {
-      const uint32_t p0 = (uint32_t)sorted[cbv[k]];
-      bag0[k] = p0 < (uint32_t)a.N ? (unit ? (int32_t)p0 : bag_of_pos[p0]) : -1;
-    }
+    if (i < a.N && (fl & (1u << (24 + k))) && cbv[k] != (int32_t)i) bag0[k] = (int32_t)(uint32_t)sorted[cbv[k]];
   }
 #pragma unroll
   for (int k = 0; k < kSortIPT; ++k) {
@@ -224,11 +230,19 @@ __global__ __launch_bounds__(256) void k_rle_write(RleArgs a) {
     const int32_t chk = (int32_t)(pc + ic[k] - 1);
     const int32_t seg_start = (int32_t)max(pm, im[k]) - 1;
     const uint32_t key = key_of(item[k]);
-    const uint32_t pos = (uint32_t)item[k];
-    // the inverse index with ordinary stores: the 4-byte stores of nearby
-    // positions (a hot key's, or a tile's neighbours on one XCD) merge in L2
-    // before a line is written back
-    if (pos < (uint32_t)a.N) a.inverse[pos] = seg;
+    if (unit) {
+      // the inverse index with ordinary stores: the 4-byte stores of nearby
+      // positions (a hot key's, or a tile's neighbours on one XCD) merge in
+      // L2 before a line is written back
+      if ((uint32_t)bag[k] < (uint32_t)a.N) a.inverse[bag[k]] = seg;
+    } else if (key < a.total_rows) {
+      if (fl & (1u << k)) a.seg_of_key[key] = seg;
+    } else {
+      // lookups with out-of-range indices: each table's sentinel entry gets
+      // the segment of the run holding them (one run per table, or one run
+      // for all tables when the sort ran over the whole key)
+      a.seg_of_key[(size_t)a.total_rows + (uint32_t)bag[k] / (uint32_t)a.B] = seg;
+    }
     // the sorted bags are written whole lines at a time: non-temporal, so they
     // keep the L2 for the forward / update running beside the dedup
     __builtin_nontemporal_store(bag[k], a.sorted_bag + i);
@@ -252,6 +266,25 @@ __global__ __launch_bounds__(256) void k_rle_write(RleArgs a) {
   }
 }
 
+// inverse[i] = segment of lookup i's key, from the key -> segment map the
+// encoder wrote (batches that are not one lookup per bag; the flag is the
+// encoder's, uniform over the grid).
+__global__ __launch_bounds__(256) void k_inverse(const u4* __restrict__ blk, const uint32_t* __restrict__ key_of_pos,
+                                                 const int32_t* __restrict__ seg_of_key, uint32_t map_size, int N,
+                                                 int32_t* __restrict__ inverse) {
+  if (blk[0].w != 0u) return;  // one lookup per bag: stored by the encoder
+  const long long i0 = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
+  uint32_t k[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) k[j] = i0 + j < N ? __builtin_nontemporal_load(key_of_pos + i0 + j) : map_size;
+  int32_t v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = k[j] < map_size ? seg_of_key[k[j]] : -1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (i0 + j < N) inverse[i0 + j] = v[j];
+}
+
 __global__ void k_set_empty(int32_t* num_unique, int32_t* num_chunks) {
   if (threadIdx.x == 0) {
     *num_unique = 0;
@@ -259,8 +292,8 @@ __global__ void k_set_empty(int32_t* num_unique, int32_t* num_chunks) {
   }
 }
 
-hipError_t launch_rle(const uint64_t* sorted, int N, int ngrp, const WsLayout& L, char* ws, const RleOut& o,
-                      hipStream_t st) {
+hipError_t launch_rle(const Geom& g, int B, const uint64_t* sorted, int N, int ngrp, const WsLayout& L, char* ws,
+                      const RleOut& o, hipStream_t st) {
   u4* blk = reinterpret_cast<u4*>(ws + L.rle_blk);
   int32_t* num_chunks = reinterpret_cast<int32_t*>(ws + L.scalars);
   const int nblk = L.nblk_rle;
@@ -270,7 +303,9 @@ hipError_t launch_rle(const uint64_t* sorted, int N, int ngrp, const WsLayout& L
   RleArgs a;
   a.sorted = sorted;
   a.blk = blk;
-  a.bag_of_pos = reinterpret_cast<const int32_t*>(ws + L.bag_of_pos);
+  a.seg_of_key = reinterpret_cast<int32_t*>(ws + L.seg_of_key);
+  a.total_rows = g.total_rows;
+  a.B = B > 0 ? B : 1;
   a.unique_keys = o.unique_keys;
   a.inverse = o.inverse;
   a.seg_off = reinterpret_cast<int32_t*>(ws + L.seg_off);
@@ -282,6 +317,9 @@ hipError_t launch_rle(const uint64_t* sorted, int N, int ngrp, const WsLayout& L
   a.sorted_bag = reinterpret_cast<int32_t*>(ws + L.sorted_bag);
   a.N = N;
   hipLaunchKernelGGL(k_rle_write, dim3(nblk), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_inverse, dim3(ceil_div(N, 1024)), dim3(256), 0, st, blk,
+                     reinterpret_cast<const uint32_t*>(ws + L.key_of_pos), a.seg_of_key,
+                     g.total_rows + (uint32_t)g.T, N, o.inverse);
   return hipGetLastError();
 }
 

@@ -130,7 +130,8 @@ typedef struct emb_ctx emb_ctx;
 
 /* Register T tables (this GPU's share). Copies the descriptors; computes
  * row_offset. Fails with EMB_E_INVAL if T < 1, if the tables disagree in
- * dim/col_slices/dtype, if the sum of rows is >= 2^32 - 1, or on any layout
+ * dim/col_slices/dtype, if the sum of rows plus
+ * num_tables is >= 2^32 - 1, or on any layout
  * rule above; EMB_E_DTYPE on an unknown dtype. Touches no device state:
  * the small device descriptor block is uploaded on the first launch. */
 int emb_create_tables(const emb_table_desc* descs, int32_t num_tables, emb_ctx** out);
@@ -179,7 +180,8 @@ int emb_forward_pooled_unique(emb_ctx* ctx, const void* indices, const void* off
                               void* hip_stream);
 
 /* Bytes of workspace emb_backward_unique_reduce needs for N lookups and
- * batch B (0 on invalid arguments). */
+ * batch B (0 on invalid arguments). It grows with N and holds 4 bytes per
+ * table row besides (a key -> unique-index map for the inverse). */
 size_t emb_backward_workspace_bytes(const emb_ctx* ctx, int64_t N, int32_t B);
 
 /* Backward, dedup part (EMBark's unique/reduction-based step, locally):

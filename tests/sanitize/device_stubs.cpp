@@ -54,7 +54,8 @@ hipError_t launch_sort_scan(const SortPlan&, const SortBufs&, int, hipStream_t) 
 hipError_t launch_sort_scatter(const SortPlan&, const SortBufs&, const uint64_t*, uint64_t*, int, int, hipStream_t) {
   EMB_STUB_ABORT("launch_sort_scatter");
 }
-hipError_t launch_rle(const uint64_t*, int, int, const WsLayout&, char*, const RleOut&, hipStream_t) {
+hipError_t launch_rle(const Geom&, int, const uint64_t*, int, int, const WsLayout&, char*, const RleOut&,
+                      hipStream_t) {
   EMB_STUB_ABORT("launch_rle");
 }
 hipError_t launch_set_empty(const WsLayout&, char*, int32_t*, hipStream_t) { EMB_STUB_ABORT("launch_set_empty"); }
