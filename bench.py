@@ -81,10 +81,11 @@ def parse():
     ap.add_argument("--ceiling", action="store_true",
                     help="only time plain library kernels (copy, read-only sum, fill) over 4 GiB: the "
                          "practical HBM ceiling the path's kernels are compared with")
-    ap.add_argument("--ahead", type=int, default=1, choices=[1, 2],
+    ap.add_argument("--ahead", type=int, default=2, choices=[1, 2],
                     help="pipeline schedule: how many batches ahead the dedup runs (1: the next batch's "
-                         "dedup runs beside the current forward and update; 2: two batches ahead, with a "
-                         "third workspace)")
+                         "dedup runs beside the current forward and update; 2 (default): two batches "
+                         "ahead, with a third workspace, so a dedup slowed by the main stream's kernels "
+                         "has a second step to finish before its update needs it)")
     ap.add_argument("--no-per-config", action="store_true",
                     help="skip the per-configuration block (configs 1, 2, 4, 5 after the headline)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",

@@ -67,8 +67,10 @@ struct emb_ctx {
     const int32_t* num_unique = nullptr;
     bool valid = false;
   } last;
-  // a dedup done ahead by emb_backward_dedup, consumed by the next backward
-  struct {
+  // dedups done ahead by emb_backward_dedup, one per workspace (at most
+  // kPendingDedups at once), each consumed by the next backward on its
+  // workspace
+  struct DedupRec {
     const void* indices = nullptr;
     const void* offsets = nullptr;
     int itype = 0;
@@ -81,7 +83,10 @@ struct emb_ctx {
     const int32_t* inverse = nullptr;
     const int32_t* num_unique = nullptr;
     bool valid = false;
-  } dedup;
+    unsigned long long seq = 0;  // issue order, to replace the oldest when all are taken
+  };
+  DedupRec dedup[8];
+  unsigned long long dedup_seq = 0;
   // shard map (emb_set_shard_map): host copy, device copy uploaded on first use
   std::vector<emb_shard_rule> shard_rules;
   int num_shards = 0;
@@ -96,6 +101,15 @@ struct emb_ctx {
   std::vector<TimedLaunch> pending;
   std::vector<hipEvent_t> free_events;
 };
+
+namespace {
+// The dedup done ahead into ws, or null.
+const emb_ctx::DedupRec* find_dedup(const emb_ctx* c, const void* ws) {
+  for (const auto& d : c->dedup)
+    if (d.valid && d.ws == ws) return &d;
+  return nullptr;
+}
+}  // namespace
 
 namespace {
 
@@ -394,10 +408,11 @@ int emb_forward_pooled_unique(emb_ctx* ctx, const void* indices, const void* off
   if (B == 0) return N == 0 ? ok() : fail(EMB_E_INVAL, "B == 0 with N > 0");
   if (!offsets || !out) return fail(EMB_E_INVAL, "offsets/out is NULL");
   if (!aligned(out, 16)) return fail(EMB_E_INVAL, "out must be 16-byte aligned");
-  const auto& d = ctx->dedup;
-  if (!(d.valid && d.indices == indices && d.offsets == offsets && d.itype == itype && d.N == N && d.B == B &&
-        d.pool == pool && d.ws == ws))
+  const emb_ctx::DedupRec* dp = find_dedup(ctx, ws);
+  if (!(dp && dp->indices == indices && dp->offsets == offsets && dp->itype == itype && dp->N == N && dp->B == B &&
+        dp->pool == pool))
     return fail(EMB_E_STATE, "no dedup of these lookups was done ahead on this context (emb_backward_dedup)");
+  const emb_ctx::DedupRec& d = *dp;
   const size_t need = (size_t)N * ctx->g.D * dtype_bytes(ctx->g.dtype);
   if (N > 0 && (!rows_buf || !aligned(rows_buf, 16))) return fail(EMB_E_INVAL, "rows_buf is NULL or misaligned");
   if (rows_buf_bytes < need) return fail(EMB_E_WORKSPACE, "rows_buf of %zu bytes < %zu needed", rows_buf_bytes, need);
@@ -512,10 +527,16 @@ int run_dedup(emb_ctx* ctx, const void* indices, const void* offsets, int32_t it
 bool same_dedup(const emb_ctx* c, const void* indices, const void* offsets, int32_t itype, int64_t N, int32_t B,
                 int32_t pool, const void* ws, const uint32_t* unique_keys, const int32_t* counts,
                 const int32_t* inverse, const int32_t* num_unique) {
-  const auto& d = c->dedup;
-  return d.valid && d.indices == indices && d.offsets == offsets && d.itype == itype && d.N == N && d.B == B &&
-         d.pool == pool && d.ws == ws && d.unique_keys == unique_keys && d.counts == counts &&
-         d.inverse == inverse && d.num_unique == num_unique;
+  const emb_ctx::DedupRec* d = find_dedup(c, ws);
+  return d && d->indices == indices && d->offsets == offsets && d->itype == itype && d->N == N && d->B == B &&
+         d->pool == pool && d->unique_keys == unique_keys && d->counts == counts && d->inverse == inverse &&
+         d->num_unique == num_unique;
+}
+
+// Forgets the dedup done ahead into ws, if any.
+void drop_dedup(emb_ctx* c, const void* ws) {
+  for (auto& d : c->dedup)
+    if (d.valid && d.ws == ws) d.valid = false;
 }
 
 }  // namespace
@@ -529,13 +550,23 @@ int emb_backward_dedup(emb_ctx* ctx, const void* indices, const void* offsets, i
                             num_unique);
   if (rc) return rc;
   if ((rc = ensure_device(ctx))) return rc;
-  ctx->dedup.valid = false;
-  ctx->last.valid = false;
+  // this dedup overwrites ws: whatever an earlier call left there is gone
+  drop_dedup(ctx, ws);
+  if (ctx->last.ws == ws) ctx->last.valid = false;
   const WsLayout L = ws_layout(ctx->g, N, B);
   rc = run_dedup(ctx, indices, offsets, itype, N, B, pool, static_cast<char*>(ws), L, unique_keys, counts,
                  inverse, num_unique, static_cast<hipStream_t>(hip_stream));
   if (rc) return rc;
-  auto& d = ctx->dedup;
+  // a free record, else the oldest one
+  emb_ctx::DedupRec* slot = &ctx->dedup[0];
+  for (auto& r : ctx->dedup) {
+    if (!r.valid) {
+      slot = &r;
+      break;
+    }
+    if (r.seq < slot->seq) slot = &r;
+  }
+  auto& d = *slot;
   d.indices = indices;
   d.offsets = offsets;
   d.itype = itype;
@@ -547,6 +578,7 @@ int emb_backward_dedup(emb_ctx* ctx, const void* indices, const void* offsets, i
   d.counts = counts;
   d.inverse = inverse;
   d.num_unique = num_unique;
+  d.seq = ++ctx->dedup_seq;
   d.valid = true;
   return ok();
 }
@@ -567,7 +599,7 @@ int emb_backward_unique_reduce(emb_ctx* ctx, const void* indices, const void* of
   const WsLayout L = ws_layout(ctx->g, N, B);
   const bool done = same_dedup(ctx, indices, offsets, itype, N, B, pool, ws, unique_keys, counts, inverse,
                                num_unique);
-  ctx->dedup.valid = false;  // a dedup is consumed by one backward
+  drop_dedup(ctx, ws);  // a dedup is consumed by one backward on its workspace
   ctx->last.valid = false;
   if (!done) {
     rc = run_dedup(ctx, indices, offsets, itype, N, B, pool, w, L, unique_keys, counts, inverse, num_unique, st);

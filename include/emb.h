@@ -221,9 +221,13 @@ int emb_backward_unique_reduce(emb_ctx* ctx, const void* indices, const void* of
  * second stream concurrently with emb_forward_pooled, the way EMBark dedups
  * a batch's keys (unique-based compression) before the exchange. The next
  * emb_backward_unique_reduce on this context with the same indices, offsets,
- * itype, N, B, pool, ws and output buffers then skips its own dedup; any
- * other backward discards it. The caller orders the two calls (same stream
- * or an event) and keeps the buffers unchanged in between. */
+ * itype, N, B, pool, ws and output buffers then skips its own dedup; a
+ * backward on the same ws with other arguments discards it. Dedups into
+ * different workspaces may be pending together (up to 8; a ninth replaces
+ * the oldest), so a caller can run several batches ahead. A dedup into the
+ * ws of the last backward cancels that backward for emb_sparse_update. The
+ * caller orders the calls (same stream or an event) and keeps the buffers
+ * unchanged in between. */
 int emb_backward_dedup(emb_ctx* ctx, const void* indices, const void* offsets, int32_t itype,
                        int64_t N, int32_t B, int32_t pool, void* ws, size_t ws_bytes,
                        uint32_t* unique_keys, int32_t* counts, int32_t* inverse,

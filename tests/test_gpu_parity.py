@@ -464,47 +464,55 @@ def test_master_weights_three_steps():
                    master=True)
 
 
-@pytest.mark.parametrize("cfg_id", [2, 5])
-def test_pipelined_dedup_matches_serial(cfg_id):
-    # three steps where the next batch's dedup runs on a side stream, into a
-    # second workspace, while the current step's forward and update run --
-    # the pattern of bench.py's pipeline schedule -- against three serial steps
-    # (one-hot tables; and the multi-hot column-sliced fp16 shard)
+@pytest.mark.parametrize("cfg_id,ahead", [(2, 1), (5, 1), (2, 2), (5, 2)])
+def test_pipelined_dedup_matches_serial(cfg_id, ahead):
+    # four steps where the dedup of the batch `ahead` steps on runs on a side
+    # stream, into its own workspace (ahead + 1 of them, so up to `ahead`
+    # dedups are pending at once), while the current step's forward and
+    # update run -- the pattern of bench.py's pipeline schedule -- against
+    # four serial steps (one-hot tables; and the multi-hot column-sliced fp16
+    # shard). Every backward must find its dedup done ahead and skip its own.
     cfg = W.make_config(2, batch=4096) if cfg_id == 2 else W.make_config(5, batch=4096, rows=2_000_000)
-    batches = [W.make_batch(cfg, k=k) for k in range(3)]
-    dys = [W.make_dy(cfg, k=k) for k in range(3)]
+    K = 4
+    batches = [W.make_batch(cfg, k=k) for k in range(K)]
+    dys = [W.make_dy(cfg, k=k) for k in range(K)]
     u = np.unique(np.concatenate([P.oracle_dedup(cfg, b)[0] for b in batches]))
-    _say("pipelined dedup cfg", cfg_id)
+    _say("pipelined dedup cfg", cfg_id, "ahead", ahead)
     results = []
     for pipelined in (False, True):
         tabs = P.make_tables(cfg)
+        E.emb_set_kernel_timing(tabs.ctx, True)
+        nset = ahead + 1
         dev = [P.to_dev(b, d) for b, d in zip(batches, dys)]
-        bufs = [tabs.backward_buffers(max(b.N for b in batches), cfg.batch, with_grad=False) for _ in range(2)]
+        bufs = [tabs.backward_buffers(max(b.N for b in batches), cfg.batch, with_grad=False) for _ in range(nset)]
         main, side = torch.cuda.current_stream(), torch.cuda.Stream()
-        free = [torch.cuda.Event(), torch.cuda.Event()]
-        done = [torch.cuda.Event(), torch.cuda.Event()]
-        free[0].record(main)
-        free[1].record(main)
+        free = [torch.cuda.Event() for _ in range(nset)]
+        done = [torch.cuda.Event() for _ in range(nset)]
+        for e in free:
+            e.record(main)
 
-        def ahead(i):
-            side.wait_event(free[i % 2])
+        def dedup_ahead(i):
+            side.wait_event(free[i % nset])
             with torch.cuda.stream(side):
-                tabs.dedup(dev[i][0], dev[i][1], cfg.batch, cfg.pool, bufs[i % 2])
-            done[i % 2].record(side)
+                tabs.dedup(dev[i][0], dev[i][1], cfg.batch, cfg.pool, bufs[i % nset])
+            done[i % nset].record(side)
 
         if pipelined:
-            ahead(0)
-        for i in range(3):
+            for i in range(ahead):
+                dedup_ahead(i)
+        for i in range(K):
             idx, off, dy = dev[i]
             tabs.forward(idx, off, cfg.batch, cfg.pool)
             if pipelined:
-                main.wait_event(done[i % 2])
-            tabs.backward(idx, off, cfg.batch, cfg.pool, dy, bufs[i % 2])
-            tabs.update(cfg.opt, cfg.lr, cfg.eps, bufs[i % 2], dY=dy)
-            free[i % 2].record(main)
-            if pipelined and i < 2:
-                ahead(i + 1)
+                main.wait_event(done[i % nset])
+            tabs.backward(idx, off, cfg.batch, cfg.pool, dy, bufs[i % nset])
+            tabs.update(cfg.opt, cfg.lr, cfg.eps, bufs[i % nset], dY=dy)
+            free[i % nset].record(main)
+            if pipelined and i + ahead < K:
+                dedup_ahead(i + ahead)
         torch.cuda.synchronize()
+        # one key build per batch: no backward redid its dedup
+        assert E.emb_kernel_times(tabs.ctx)["keys"][1] == K
         results.append(P.read_rows(tabs, cfg, u))
         tabs.close()
     assert np.array_equal(results[0][0].view(np.uint32), results[1][0].view(np.uint32))
