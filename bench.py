@@ -502,8 +502,8 @@ def run_workload(args, compact=False):
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "ms_per_step_p10_p50_p90": [pct(10), pct(50), pct(90)],
-        "schedule": args.schedule + (f" (dedup {ahead} batches ahead)" if args.schedule == "pipeline" and ahead > 1
-                                     else ""),
+        "schedule": args.schedule,
+        "dedup_ahead": ahead if args.schedule == "pipeline" else None,
         "reduce": args.reduce if not args.pack else f"pack to {args.pack} shards (RB)",
         f"ms_per_step_{other}": round(other_ms / K, 4) if other_ms is not None else None,
         "higher_is_better": True,
