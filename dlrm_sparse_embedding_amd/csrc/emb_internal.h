@@ -111,7 +111,7 @@ struct DevCtx {
 
 // Workspace carve-up for the backward / update pair.
 struct WsLayout {
-  size_t keys_a, keys_b;        // uint64 [N] (key << 32 | position), ping-pong
+  size_t keys_a, keys_b;        // uint64 [N] (key << 32 | bag), ping-pong
   size_t key_of_pos;            // uint32 [N] key of each lookup in input order (total_rows + t: table t's sentinel)
   size_t seg_of_key;            // int32 [total_rows + T] segment of each key present (multi-hot inverse)
   size_t unit_grp;              // int32 [ceil(T*B/64)] 1 if each of a key-build group's 64 bags is [b, b+1)
@@ -157,7 +157,7 @@ hipError_t launch_keys(const Geom& g, const DevCtx& dc, const void* indices, con
                        int itype, long long N, int B, int pool, const WsLayout& L, char* ws,
                        hipStream_t st);
 
-// One stable LSD radix sort of N (key << 32 | position) words: passes over
+// One stable LSD radix sort of N (key << 32 | bag) words: passes over
 // shift = 0, rb, 2*rb, ... < bits, each = hist, scan, scatter.
 struct SortPlan {
   bool seg;    // table-segmented: each table's positions sorted on its row bits

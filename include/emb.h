@@ -186,7 +186,7 @@ size_t emb_backward_workspace_bytes(const emb_ctx* ctx, int64_t N, int32_t B);
 
 /* Backward, dedup part (EMBark's unique/reduction-based step, locally):
  *   global keys g_i = row_offset[t(i)] + idx_i are sorted stably (device
- *   LSD radix sort over (key, position) pairs) and run-length encoded:
+ *   LSD radix sort over (key, bag) pairs) and run-length encoded:
  *   unique_keys[u]  (capacity N) distinct keys, strictly ascending;
  *   counts[u]       (capacity N) multiplicity of unique_keys[u];
  *   inverse[i]      ([N]) index u of lookup i's key;

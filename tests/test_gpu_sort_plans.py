@@ -160,10 +160,12 @@ LENGTH_CASES = {
 
 @pytest.mark.parametrize("name", sorted(LENGTH_CASES))
 def test_bag_of_position(name):
-    # the dedup takes the bag of position p to be p only when every bag holds
-    # exactly one lookup at its own index, and gathers it otherwise (N == T*B
-    # alone must not trigger it); mean pooling weights each lookup by 1/L, so a
-    # wrong bag shows up in the reduced gradient
+    # the sort word carries each lookup's bag; the encoder stores the inverse
+    # at the bag only when every bag holds exactly one lookup at its own index,
+    # and goes through the key -> segment map otherwise (N == T*B alone must not
+    # take the direct store); mean pooling weights each lookup by 1/L, so a
+    # wrong bag shows up in the reduced gradient, and a wrong inverse in the
+    # dedup check
     rows, B, spec = LENGTH_CASES[name]
     rng = np.random.default_rng(zlib.crc32(name.encode()))
     lens = []
