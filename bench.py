@@ -79,8 +79,9 @@ def parse():
                     help="time only --schedule (no comparison schedule, no isolated-kernel pass), so a "
                          "profiler trace of the run holds that schedule's launches alone")
     ap.add_argument("--ceiling", action="store_true",
-                    help="only time plain library kernels (copy, read-only sum, fill) over 4 GiB: the "
-                         "practical HBM ceiling the path's kernels are compared with")
+                    help="only time plain library kernels (copy, read-only sum, fill) over 4 GiB, and "
+                         "random 512-byte row reads served by L2, MALL and HBM: the practical ceilings "
+                         "the path's kernels are compared with")
     ap.add_argument("--ahead", type=int, default=2, choices=[1, 2],
                     help="pipeline schedule: how many batches ahead the dedup runs (1: the next batch's "
                          "dedup runs beside the current forward and update; 2 (default): two batches "
@@ -148,7 +149,30 @@ def main() -> int:
             e1.record()
             torch.cuda.synchronize()
             res[name + "_GBps"] = round(nbytes * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
-        print(json.dumps({"ceiling": res, "bytes_per_buffer": n * 4}), flush=True)
+        del src, dst
+        # random 512-byte row reads (the library's probe kernel), the way the
+        # multi-hot reduce reads dY rows: rows 51200 bytes apart (a 100-table,
+        # 128-column fp32 dY), every XCD reading only its own eighth (an L2-
+        # resident 2 MB each), or all XCDs the whole 16 MB (MALL-resident);
+        # and rows packed over 2 GiB (HBM)
+        from dlrm_sparse_embedding_amd import emb as E
+        probe = torch.zeros(1 << 29, dtype=torch.float32, device="cuda")   # 2 GiB
+        sink = torch.empty(E.emb_probe_blocks(), dtype=torch.float32, device="cuda")
+        reads = 240
+        logical = E.emb_probe_blocks() * 8 * reads * 512
+        for name, nrows, stride, local in (("l2_xcd_local_rows", 32768, 51200, True),
+                                           ("mall_shared_rows", 32768, 51200, False),
+                                           ("hbm_random_rows", (1 << 31) // 512, 512, False)):
+            E.emb_probe_reads(probe, nrows, stride, local, reads, sink)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(10):
+                E.emb_probe_reads(probe, nrows, stride, local, reads, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            res[name + "_GBps"] = round(logical * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+        print(json.dumps({"ceiling": res, "bytes_per_buffer": n * 4, "probe_bytes_per_launch": logical}), flush=True)
         return 0
 
     if args.calibrate_copy:

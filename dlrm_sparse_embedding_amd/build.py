@@ -25,7 +25,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libemb.so")
 
 SOURCES = ["emb_api.cpp", "emb_plan.cpp", "k_init.hip", "k_forward.hip", "k_keys_sort.hip", "k_rle.hip",
-           "k_reduce.hip", "k_atomic.hip", "k_pack.hip", "k_hash.hip"]
+           "k_reduce.hip", "k_atomic.hip", "k_pack.hip", "k_hash.hip", "k_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -196,6 +196,11 @@ struct RleOut {
 // bag of position p is p itself (0 when N != T*B: never).
 hipError_t launch_rle(const Geom& g, int B, const uint64_t* sorted, int N, int ngrp, const WsLayout& L, char* ws,
                       const RleOut& o, hipStream_t st);
+// Measurement aid (k_probe.hip): probe_blocks() blocks of 8 subgroups, each
+// reading `reads` random 512-byte rows; sink gets one float per block.
+int probe_blocks();
+hipError_t launch_probe_reads(const void* buf, uint32_t nrows, uint32_t stride, int local, int reads,
+                              float* sink, hipStream_t st);
 hipError_t launch_set_empty(const WsLayout& L, char* ws, int32_t* num_unique, hipStream_t st);
 
 // mode: 0 = write reduced gradient, 1 = fused SGD, 2 = fused Adagrad.

@@ -132,6 +132,10 @@ def lib() -> ctypes.CDLL:
     L.emb_set_kernel_timing.restype = ctypes.c_int
     L.emb_kernel_times.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
     L.emb_kernel_times.restype = ctypes.c_int
+    L.emb_probe_blocks.argtypes = []
+    L.emb_probe_blocks.restype = i32
+    L.emb_probe_reads.argtypes = [vp, i64, i64, i32, i32, vp, vp]
+    L.emb_probe_reads.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -315,6 +319,16 @@ def emb_pack_by_shard(ctx: int, ws, dY, send_keys, send_offsets, slot_of_unique,
                       stream=None) -> None:
     _check(lib().emb_pack_by_shard(ctx, _ptr(ws), _ptr(dY), _ptr(send_keys), _ptr(send_offsets),
                                    _ptr(slot_of_unique), _ptr(send_grad), _stream(stream)))
+
+
+def emb_probe_blocks() -> int:
+    return int(lib().emb_probe_blocks())
+
+
+def emb_probe_reads(buf, nrows: int, stride: int, xcd_local: bool, reads: int, sink, stream=None) -> None:
+    """Measurement aid: random 512-byte row reads (see include/emb.h)."""
+    _check(lib().emb_probe_reads(_ptr(buf), int(nrows), int(stride), 1 if xcd_local else 0, int(reads),
+                                 _ptr(sink), _stream(stream)))
 
 
 def emb_kernel_times(ctx: int) -> dict:

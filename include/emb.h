@@ -414,6 +414,23 @@ int emb_set_kernel_timing(emb_ctx* ctx, int32_t enable);
  * launches[EMB_K_COUNT], and forgets them. */
 int emb_kernel_times(emb_ctx* ctx, double* ms, int64_t* launches);
 
+/* Measurement aid, not part of the method (no context): the cache and HBM
+ * read ceilings that the path's kernels are compared with. Launches
+ * emb_probe_blocks() blocks of 8 subgroups of 32 lanes on the stream; each
+ * subgroup reads `reads` rows of 512 bytes (16 bytes per lane) at
+ * pseudo-random indices in [0, nrows), row r starting at byte r*stride of
+ * buf. With xcd_local != 0, block b reads only rows of its eighth of
+ * [0, nrows): blocks are dealt round robin to the 8 XCDs, so each XCD's L2
+ * serves its own eighth. Logical bytes read: emb_probe_blocks() * 8 * reads
+ * * 512. buf (device, >= (nrows - 1) * stride + 512 bytes, 16-byte aligned)
+ * is only read; sink (device, >= emb_probe_blocks() floats) receives one
+ * value per block. EMB_E_INVAL for NULL or misaligned pointers, nrows < 8 or
+ * >= 2^32, stride < 512 or not a multiple of 16 or >= 2^32, reads not in
+ * [4, 65536] or not a multiple of 4. */
+int32_t emb_probe_blocks(void);
+int emb_probe_reads(const void* buf, int64_t nrows, int64_t stride, int32_t xcd_local, int32_t reads,
+                    float* sink, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

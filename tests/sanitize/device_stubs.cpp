@@ -59,6 +59,10 @@ hipError_t launch_rle(const Geom&, int, const uint64_t*, int, int, const WsLayou
   EMB_STUB_ABORT("launch_rle");
 }
 hipError_t launch_set_empty(const WsLayout&, char*, int32_t*, hipStream_t) { EMB_STUB_ABORT("launch_set_empty"); }
+int probe_blocks() { return 2048; }
+hipError_t launch_probe_reads(const void*, uint32_t, uint32_t, int, int, float*, hipStream_t) {
+  EMB_STUB_ABORT("launch_probe_reads");
+}
 hipError_t launch_reduce(const Geom&, const DevCtx&, int, int, int, int, const float*, const WsLayout&, const char*,
                          const uint32_t*, const int32_t*, float*, float, float, hipStream_t, const int32_t*) {
   EMB_STUB_ABORT("launch_reduce");

@@ -97,6 +97,26 @@ def test_create_null_weights():
     assert _create([d])[0] == E.EMB_E_INVAL
 
 
+def test_probe_rejects_bad_arguments_before_any_launch():
+    # the read-ceiling probe validates on the host and launches nothing on error
+    L = E.lib()
+    assert E.emb_probe_blocks() == 2048
+    good = dict(nrows=4096, stride=512, local=1, reads=60)
+    def call(buf=FAKE, sink=FAKE, **kw):
+        a = {**good, **kw}
+        return L.emb_probe_reads(buf, a["nrows"], a["stride"], a["local"], a["reads"], sink, None)
+    assert call(buf=None) == E.EMB_E_INVAL
+    assert call(sink=None) == E.EMB_E_INVAL
+    assert call(buf=FAKE + 4) == E.EMB_E_INVAL       # misaligned
+    assert call(nrows=7) == E.EMB_E_INVAL
+    assert call(nrows=1 << 32) == E.EMB_E_INVAL
+    assert call(stride=256) == E.EMB_E_INVAL
+    assert call(stride=520) == E.EMB_E_INVAL         # not a multiple of 16
+    assert call(reads=6) == E.EMB_E_INVAL
+    assert call(reads=0) == E.EMB_E_INVAL
+    assert call(reads=65540) == E.EMB_E_INVAL
+
+
 def test_valid_context_host_only_calls():
     rc, ctx = _create([_desc(rows=1000), _desc(rows=5000)])
     assert rc == E.EMB_OK and ctx
