@@ -158,6 +158,53 @@ LENGTH_CASES = {
 }
 
 
+@pytest.mark.parametrize("rows", [[1000, 700, 1023, 10, 500, 999], [50, 60, 40]], ids=["table_plan", "global_plan"])
+def test_multi_hot_out_of_range_inverse(rows):
+    # ragged multi-hot bags (not one lookup per bag, so the inverse goes
+    # through the key -> segment map) with out-of-range indices in several
+    # tables: every lookup's inverse names a segment holding its own key, the
+    # sentinel sum(rows) for the bad ones (one run per table under the
+    # per-table plan, one run for all tables under the global plan), and the
+    # counts add up
+    want_table = rows[0] == 1000
+    assert _plan(rows)[0] == want_table
+    rng = np.random.default_rng(11)
+    B = 300
+    lens = [rng.integers(0, 6, B) for _ in rows]
+    keys = [rng.integers(0, r, int(l.sum())) for l, r in zip(lens, rows)]
+    for t in (0, 1, len(rows) - 1):          # bad indices in three tables
+        k = keys[t]
+        k[rng.choice(len(k), 3, replace=False)] = [rows[t], -1, 10 * rows[t] + 7]
+    batch = W.make_batch_from_lengths(lens, keys, B, index_dtype=np.int64)
+    assert batch.N > len(rows) * B // 2
+    cfg = P.custom_cfg(rows, dim=16, B=B, pool="mean", opt="sgd")
+    P.say("multi-hot out-of-range inverse", "table plan" if want_table else "global plan", "N", batch.N)
+    tabs = P.make_tables(cfg)
+    dY = np.ones((B, len(rows) * 16), np.float32)
+    idx, off, dy = P.to_dev(batch, dY)
+    bufs = tabs.backward_buffers(batch.N, B, with_grad=False)
+    tabs.backward(idx, off, B, "mean", dy, bufs)
+    tabs.update("sgd", 0.5, 0.0, bufs, dY=dy)
+    with pytest.raises(E.EmbError) as ei:
+        tabs.check_device_error()
+    assert ei.value.code == E.EMB_E_BOUNDS
+    U = int(bufs["num_unique"].item())
+    uk = bufs["unique_keys"][:U].cpu().numpy().view(np.uint32).astype(np.int64)
+    cnt = bufs["counts"][:U].cpu().numpy().astype(np.int64)
+    inv = bufs["inverse"][:batch.N].cpu().numpy().astype(np.int64)
+    ro = cfg.row_offset()
+    g = np.concatenate([np.where((k >= 0) & (k < r), ro[t] + k, cfg.total_rows)
+                        for t, (k, r) in enumerate(zip(keys, rows))])
+    assert inv.min() >= 0 and inv.max() < U
+    assert np.array_equal(uk[inv], g)                          # every lookup's key
+    assert np.array_equal(np.bincount(inv, minlength=U), cnt)  # counts
+    in_range = uk[uk < cfg.total_rows]
+    assert np.array_equal(in_range, np.unique(g[g < cfg.total_rows]))  # distinct, ascending
+    n_sent = int((uk == cfg.total_rows).sum())
+    assert n_sent == (3 if want_table else 1)
+    tabs.close()
+
+
 @pytest.mark.parametrize("name", sorted(LENGTH_CASES))
 def test_bag_of_position(name):
     # the sort word carries each lookup's bag; the encoder stores the inverse
