@@ -24,7 +24,7 @@
 // columns take two column blocks on the grid's y axis) reduces one chunk,
 // keeping 4 to 6 dY rows in flight (as many as fit 64 VGPRs without spills).
 // On multi-hot batches a run of equal bags inside a segment loads its dY row
-// once and adds it with its multiplicity. A chunk that is a whole segment
+// once and reuses it. A chunk that is a whole segment
 // applies the optimizer right there, with the weight (and state) row
 // prefetched before the dY loop, so the reduced gradient never leaves VGPRs.
 // A segment longer than a tile leaves one partial per kChunk-tile it touches
@@ -144,7 +144,7 @@ __device__ __forceinline__ int slot_of(int so, int j, int tile) {
 }
 
 // REP: the batch may hold a key more than once in one bag (more lookups than
-// bags), so a segment can repeat a bag; see the multiplicity loop below.
+// bags), so a segment can repeat a bag; see the multi-hot loop below.
 template <int DT, int LPR, int MODE, bool MEAN, bool REP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_chunks(RedArgs a) {
   extern __shared__ uint32_t s_ro[];
@@ -154,7 +154,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
   // 8 waves/SIMD (spills cost scratch traffic in HBM: measured ~270 MB/launch);
   // Adagrad with mean pooling or a 16-bit / master row holds more live values
   constexpr int U0 = (MODE == 2 && (MEAN || (DT & 7) != EMB_F32 || (DT & kMasterBit))) ? 4 : 6;
-  constexpr int U = REP ? U0 - 1 : U0;  // the multiplicities take registers too
+  // multi-hot: the next group's bags take registers too (fp32 Adagrad rows
+  // then fit 4 in flight without spills)
+  constexpr int U = REP ? (MODE == 2 && U0 == 6 ? 4 : U0 - 1) : U0;
   constexpr int SGW = 256 / LPR;
   const int lsg = threadIdx.x & (LPR - 1);
   // blockIdx.y picks the column block: rows wider than 4*LPR columns
@@ -197,45 +199,67 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
     // loads use the uniform base + a 32-bit per-lane offset
     const uint32_t dyt = (uint32_t)(t * a.D + c0);
     const int bagt = t * a.B;
-    for (int i = cb; i < ce; i += U) {
-      int bg[U];
+    if constexpr (REP) {
+      // Multi-hot: a chunk can run to kChunk positions. The bags of the next
+      // U positions are loaded while this group's dY rows are in flight, so
+      // an iteration waits one memory round trip, not two. A segment's
+      // positions are ascending, so repeats of one bag (a key looked up
+      // several times in one bag) sit next to each other: a run's first
+      // entry loads the row and the others reuse it. Entries are added one
+      // by one in position order, so the sum does not depend on U (the fused
+      // and the materialised paths, whose U differ, agree bit for bit).
+      int bn[U];
 #pragma unroll
-      for (int k = 0; k < U; ++k) bg[k] = i + k < ce ? (i + k == cb ? bag0 : a.sorted_bag[i + k]) : -1;
-      // A segment's positions are ascending, so repeats of one bag (a key
-      // looked up several times in one multi-hot bag) sit next to each
-      // other. Only a run's first entry loads its dY row; the run adds it
-      // with its multiplicity (3 bits per entry in `mul`), a one-hot batch
-      // adds every row once, as a plain sum would.
-      uint32_t mul = 0111111u;  // one per entry: no repeats
-      if constexpr (REP) {
-        mul = 0;
-        uint32_t cnt = 0;
+      for (int k = 0; k < U; ++k) bn[k] = cb + k < ce ? (k == 0 ? bag0 : a.sorted_bag[cb + k]) : -1;
+      for (int i = cb; i < ce; i += U) {
+        int bg[U];
 #pragma unroll
-        for (int k = U - 1; k >= 0; --k) {
-          ++cnt;
-          if (!(k > 0 && bg[k] >= 0 && bg[k] == bg[k - 1])) {
-            mul |= cnt << (3 * k);
-            cnt = 0;
+        for (int k = 0; k < U; ++k) bg[k] = bn[k];
+        f4 v[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+          v[k] = f4{0.f, 0.f, 0.f, 0.f};
+          const unsigned b = (unsigned)(bg[k] - bagt);
+          if (bg[k] >= 0 && b < (unsigned)a.B && act && (k == 0 || bg[k] != bg[k - 1])) {
+            v[k] = *reinterpret_cast<const f4*>(a.dY + (b * dys + dyt));
+            if constexpr (MEAN) v[k] *= a.inv_len[bg[k]];
           }
         }
-      }
-      f4 v[U];
 #pragma unroll
-      for (int k = 0; k < U; ++k) {
-        v[k] = f4{0.f, 0.f, 0.f, 0.f};
-        const unsigned b = (unsigned)(bg[k] - bagt);
-        if (bg[k] >= 0 && b < (unsigned)a.B && act && ((mul >> (3 * k)) & 7u)) {
-          v[k] = *reinterpret_cast<const f4*>(a.dY + (b * dys + dyt));
-          if constexpr (MEAN) v[k] *= a.inv_len[bg[k]];
+        for (int k = 0; k < U; ++k) bn[k] = i + U + k < ce ? a.sorted_bag[i + U + k] : -1;
+#pragma unroll
+        for (int k = 1; k < U; ++k)
+          if (bg[k] >= 0 && bg[k] == bg[k - 1]) v[k] = v[k - 1];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+          acc[0] += v[k].x;
+          acc[1] += v[k].y;
+          acc[2] += v[k].z;
+          acc[3] += v[k].w;
         }
       }
+    } else {
+      for (int i = cb; i < ce; i += U) {
+        int bg[U];
 #pragma unroll
-      for (int k = 0; k < U; ++k) {
-        const float m = (float)((mul >> (3 * k)) & 7u);
-        acc[0] = fmaf(m, v[k].x, acc[0]);
-        acc[1] = fmaf(m, v[k].y, acc[1]);
-        acc[2] = fmaf(m, v[k].z, acc[2]);
-        acc[3] = fmaf(m, v[k].w, acc[3]);
+        for (int k = 0; k < U; ++k) bg[k] = i + k < ce ? (i + k == cb ? bag0 : a.sorted_bag[i + k]) : -1;
+        f4 v[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+          v[k] = f4{0.f, 0.f, 0.f, 0.f};
+          const unsigned b = (unsigned)(bg[k] - bagt);
+          if (bg[k] >= 0 && b < (unsigned)a.B && act) {
+            v[k] = *reinterpret_cast<const f4*>(a.dY + (b * dys + dyt));
+            if constexpr (MEAN) v[k] *= a.inv_len[bg[k]];
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+          acc[0] += v[k].x;
+          acc[1] += v[k].y;
+          acc[2] += v[k].z;
+          acc[3] += v[k].w;
+        }
       }
     }
 
