@@ -17,7 +17,8 @@
 // one-hot bags (one row per bag) still keep 4 rows per subgroup in flight.
 // The run's bag boundaries (bps+1 offsets) sit one per lane and are read by
 // lane shuffles (ds_bpermute), not by dependent global loads; so do its row
-// indices, LPR at a time, so that a row load waits on one round trip. Pooled rows
+// indices, LPR at a time and one block ahead, so that a row load waits on one
+// round trip. Pooled rows
 // are written with non-temporal stores so the L2 keeps Zipf-hot table rows.
 // The grid may be capped (grid-stride over the work) so that the dedup, run
 // on a second stream, keeps some wave slots while the forward streams.
@@ -154,37 +155,48 @@ k_forward(FwdArgs a) {
     // than U lanes read each index in every lane.)
     constexpr uint32_t kNoRow = 0xffffffffu;
     constexpr bool kLaneIdx = LPR >= U;
-    uint32_t myrow = kNoRow;
-    int blk_end = P0;  // lookups [P0, blk_end) have had their indices read
+    // row of lookup q (this lane's share of an index block), kNoRow if none
+    auto row_of = [&](int q) -> uint32_t {
+      uint32_t row = kNoRow;
+      if (q < P1) {
+        if constexpr (SRC == 2) {
+          const long long id = reinterpret_cast<const long long*>(a.indices)[q];
+          if (id != kEmpty) {  // an id without a row pools to nothing
+            const long long s0 = hm.base + (uint32_t)(mix64((uint64_t)id) & hm.mask);
+            const long long k0 = (long long)a.hkeys[s0];
+            long long r = -1;
+            if (k0 == id) {
+              r = a.hvals[s0];
+            } else if (k0 != kEmpty) {
+              const long long slot = find_slot(hm, a.hkeys, id, false);
+              if (slot >= 0) r = a.hvals[slot];
+            }
+            if (r >= 0 && r < rows_t) row = (uint32_t)r;
+          }
+        } else {
+          long long r;
+          if constexpr (SRC == 1) r = reinterpret_cast<const int32_t*>(a.indices)[q];
+          else r = ld_idx<IDX>(a.indices, q);
+          if (r >= 0 && r < rows_t) row = (uint32_t)r;
+          else bad = 1;
+        }
+      }
+      return row;
+    };
+    // The run's indices go by blocks of LPR lookups, one per lane. The next
+    // block's indices are read while the current block's first rows are in
+    // flight, so on long bags a row load never waits behind an index load
+    // (SRC 2 probes a block when it reaches it: its probe chains would not
+    // fit the registers twice).
+    uint32_t myrow = kNoRow, nxrow = kNoRow;
+    int blk_start = P0;  // first lookup of the block whose rows `myrow` holds
+    if constexpr (kLaneIdx) myrow = row_of(P0 + lsg);
     for (int p = P0; p < P1; p += U) {
       if constexpr (kLaneIdx) {
-        if (p >= blk_end) {  // uniform over the subgroup
-          const int q = p + lsg;
-          myrow = kNoRow;
-          if (q < P1) {
-            if constexpr (SRC == 2) {
-              const long long id = reinterpret_cast<const long long*>(a.indices)[q];
-              if (id != kEmpty) {  // an id without a row pools to nothing
-                const long long s0 = hm.base + (uint32_t)(mix64((uint64_t)id) & hm.mask);
-                const long long k0 = (long long)a.hkeys[s0];
-                long long r = -1;
-                if (k0 == id) {
-                  r = a.hvals[s0];
-                } else if (k0 != kEmpty) {
-                  const long long slot = find_slot(hm, a.hkeys, id, false);
-                  if (slot >= 0) r = a.hvals[slot];
-                }
-                if (r >= 0 && r < rows_t) myrow = (uint32_t)r;
-              }
-            } else {
-              long long r;
-              if constexpr (SRC == 1) r = reinterpret_cast<const int32_t*>(a.indices)[q];
-              else r = ld_idx<IDX>(a.indices, q);
-              if (r >= 0 && r < rows_t) myrow = (uint32_t)r;
-              else bad = 1;
-            }
-          }
-          blk_end = p + LPR;
+        if (p >= blk_start + LPR) {  // uniform over the subgroup
+          blk_start += LPR;
+          if constexpr (SRC == 2) myrow = row_of(blk_start + lsg);
+          else myrow = nxrow;
         }
       }
       // SRC 2: the U lookups' map probes are issued together -- ids, then the
@@ -236,10 +248,13 @@ k_forward(FwdArgs a) {
         } else {
           // lookup p + k's row sits in lane (p + k - first of its block); U
           // divides LPR, so a group never straddles two blocks
-          const uint32_t r = (uint32_t)__shfl((int)myrow, (p + k - (blk_end - LPR)) & (LPR - 1), LPR);
+          const uint32_t r = (uint32_t)__shfl((int)myrow, (p + k - blk_start) & (LPR - 1), LPR);
           if (p + k < P1 && r != kNoRow && act)
             v[k] = *reinterpret_cast<const u4*>(wbase + (size_t)r * rstride);
         }
+      }
+      if constexpr (kLaneIdx && SRC != 2) {
+        if (p == blk_start && blk_start + LPR < P1) nxrow = row_of(blk_start + LPR + lsg);
       }
 #pragma unroll
       for (int k = 0; k < U; ++k) {
