@@ -132,3 +132,48 @@ def test_fused_equals_materialized_and_reruns_bit_identical():
         assert np.array_equal(r["w_new"].view(np.uint32), res[0]["w_new"].view(np.uint32))
         assert np.array_equal(r["G_new"].view(np.uint32), res[0]["G_new"].view(np.uint32))
 
+
+
+@pytest.mark.parametrize("pool,itype", [("sum", np.int32), ("mean", np.int64)])
+def test_long_bags_out_of_range_in_later_index_blocks(pool, itype):
+    # bags of up to 150 lookups: the forward reads their row indices 16 (or
+    # 32) at a time, one block ahead; out-of-range indices sit in later
+    # blocks too. They add nothing, count in a mean's length, set the bounds
+    # flag, and every other element still matches the oracle.
+    import torch
+    from dlrm_sparse_embedding_amd import emb as E
+    rng = np.random.default_rng(31)
+    rows = [5000, 300]
+    tabs_spec = tuple(W.TableSpec(r, 64, "bf16") for r in rows)
+    B = 96
+    cfg = W.Config(97, "long-bags", tabs_spec, B, pool, "sgd", 0.05, 0.0, (1, 1), None, init_seed=97)
+    lens = [rng.integers(0, 151, B), rng.integers(15, 40, B)]
+    keys = []
+    for t, r in enumerate(rows):
+        k = rng.integers(0, r, int(lens[t].sum()))
+        bad = rng.random(len(k)) < 0.02
+        k[bad] = np.where(rng.random(int(bad.sum())) < 0.5, -1, r + 3)
+        keys.append(k)
+    batch = W.make_batch_from_lengths(lens, keys, B, index_dtype=itype)
+    _say("long bags out of range", pool, itype.__name__, "N", batch.N)
+    tabs = P.make_tables(cfg)
+    idx, off, _ = P.to_dev(batch, None)
+    Y = tabs.forward(idx, off, B, pool)
+    torch.cuda.synchronize()
+    with pytest.raises(E.EmbError) as ei:
+        tabs.check_device_error()
+    assert ei.value.code == E.EMB_E_BOUNDS
+    P.check_forward(Y.cpu().numpy(), cfg, batch, P.oracle_tables(cfg, batch), num_rows=rows)
+    tabs.close()
+
+
+def test_fused_equals_materialized_bf16_mean_sgd():
+    # the 100-table bf16 workload's arithmetic (mean pooling, SGD, 1..93
+    # lookups per bag by table) on 12 tables at a reduced batch
+    cfg = W.make_config(4, num_tables=12, batch=512)
+    batch = W.make_batch(cfg, k=1)
+    dY = W.make_dy(cfg, k=1)
+    _say("multi-hot determinism bf16 N", batch.N)
+    res = [P.run_step(cfg, batch, dY, path=p, sample_untouched=0) for p in ("fused", "materialized", "fused")]
+    for r in res[1:]:
+        assert np.array_equal(r["w_new"].view(np.uint32), res[0]["w_new"].view(np.uint32))
