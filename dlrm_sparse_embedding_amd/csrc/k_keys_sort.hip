@@ -336,6 +336,21 @@ __global__ __launch_bounds__(256) void k_sort_hist(const uint64_t* __restrict__ 
   uint32_t lo = 0, span = 0;
   if (r.lo < r.hi) seg_rows(a, r.seg, &lo, &span);
   __syncthreads();
+  // All of the tile's words are loaded before any is counted: from the
+  // tile's start (a scalar base) at clamped 32-bit offsets, so the loads need
+  // no branch and few address registers and go out back to back (one memory
+  // round trip per tile, not one per item).
+  uint64_t w[IPT];
+  const int t_lo = __builtin_amdgcn_readfirstlane(r.lo);
+  const int t_n = __builtin_amdgcn_readfirstlane(r.hi - r.lo);
+  if (t_n > 0) {
+    const uint64_t* kb = keys + t_lo;
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) w[j] = kb[min(j * 256 + (int)threadIdx.x, t_n - 1)];
+  } else {
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) w[j] = 0;
+  }
   // equal digits of a wave are counted by one LDS add from their first lane:
   // skewed keys put many lanes on one bin, which would serialise per-lane adds
   const uint64_t lt = lanemask_lt();
@@ -343,7 +358,7 @@ __global__ __launch_bounds__(256) void k_sort_hist(const uint64_t* __restrict__ 
   for (int j = 0; j < IPT; ++j) {
     const int i = r.lo + j * 256 + threadIdx.x;
     const bool valid = i < r.hi;
-    const uint32_t d = valid ? digit_of<RB>(local_of(keys[i], lo, span, a.vmax), shift) : 0u;
+    const uint32_t d = valid ? digit_of<RB>(local_of(w[j], lo, span, a.vmax), shift) : 0u;
     const uint64_t peers = digit_peers<RB>(d, valid);
     if (valid && (peers & lt) == 0) atomicAdd(&h[d], (uint32_t)__popcll(peers));
   }

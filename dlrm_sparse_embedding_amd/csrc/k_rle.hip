@@ -49,12 +49,25 @@ __global__ __launch_bounds__(256) void k_rle_count(const uint64_t* __restrict__ 
   __shared__ uint32_t lds[8];
   __shared__ uint32_t s_max[4];
   const long long base = (long long)blockIdx.x * kSortTile;
+  // every item's key and its predecessor's are loaded first, from the tile's
+  // start (a scalar base) at clamped 32-bit offsets: no branch and few
+  // address registers, so the loads go out back to back
+  uint32_t kc[kSortIPT], kp[kSortIPT];
+  const int lim = (int)min((long long)N - base, (long long)kSortTile) - 1;  // >= 0: the grid covers [0, N)
+  const uint64_t* tb = sorted + base;
+  const int pmin = base > 0 ? -1 : 0;  // the word before the tile, if there is one
+#pragma unroll
+  for (int k = 0; k < kSortIPT; ++k) {
+    const int o = min(k * 256 + (int)threadIdx.x, lim);
+    kc[k] = key_of(tb[o]);
+    kp[k] = key_of(tb[max(o - 1, pmin)]);
+  }
   uint32_t cs = 0, cc = 0, ms = 0;
 #pragma unroll
   for (int k = 0; k < kSortIPT; ++k) {
     const long long i = base + k * 256 + threadIdx.x;
     if (i < N) {
-      const bool fs = i == 0 || key_of(sorted[i]) != key_of(sorted[i - 1]);
+      const bool fs = i == 0 || kc[k] != kp[k];
       const bool fc = fs || (i % kChunk) == 0;
       cs += fs;
       cc += fc;
@@ -152,7 +165,7 @@ struct RleArgs {
   int N;
 };
 
-__global__ __launch_bounds__(256) void k_rle_write(RleArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_rle_write(RleArgs a) {
   __shared__ uint32_t s_ws[4], s_wc[4], s_wm[4];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -162,18 +175,38 @@ __global__ __launch_bounds__(256) void k_rle_write(RleArgs a) {
   uint32_t is[kSortIPT], ic[kSortIPT], im[kSortIPT];
   uint32_t fl = 0;  // bit k: segment start, 8+k: chunk start, 16+k: segment end, 24+k: chunk end
   uint32_t run_s = 0, run_c = 0, run_m = 0;
+  // The wave's 64 * kSortIPT consecutive words are loaded first, at clamped
+  // indices (no branch: the loads go out back to back), plus the word before
+  // and the word after the wave's range; every other neighbour's key comes
+  // from the lane next to it (or the previous / next item's end lane).
+  // (scalar wave base, 32-bit offsets: few address registers)
+  const long long wbase = __builtin_amdgcn_readfirstlane((int)(base - (long long)blockIdx.x * kSortTile)) +
+                          (long long)blockIdx.x * kSortTile;
+  const int wlim = (int)max(min((long long)a.N - wbase, (long long)(64 * kSortIPT)), 1ll) - 1;
+  const uint64_t* wb = a.sorted + min(wbase, (long long)a.N - 1);
+#pragma unroll
+  for (int k = 0; k < kSortIPT; ++k) item[k] = wb[min(k * 64 + lane, wlim)];
+  const uint32_t key_before = key_of(wbase > 0 ? a.sorted[min(wbase - 1, (long long)a.N - 1)] : 0ull);
+  const uint32_t key_after = key_of(a.sorted[min(wbase + 64 * kSortIPT, (long long)a.N - 1)]);
 #pragma unroll
   for (int k = 0; k < kSortIPT; ++k) {
     const long long i = base + k * 64 + lane;
+    const uint32_t key = key_of(item[k]);
+    const uint32_t up = (uint32_t)__shfl_up((int)key, 1, 64);
+    const uint32_t dn = (uint32_t)__shfl_down((int)key, 1, 64);
+    const uint32_t end_prev = (uint32_t)__builtin_amdgcn_readlane((int)key_of(item[k > 0 ? k - 1 : 0]), 63);
+    const uint32_t start_next =
+        (uint32_t)__builtin_amdgcn_readlane((int)key_of(item[k < kSortIPT - 1 ? k + 1 : k]), 0);
+    const uint32_t kprev = lane > 0 ? up : (k > 0 ? end_prev : key_before);
+    const uint32_t knext = lane < 63 ? dn : (k < kSortIPT - 1 ? start_next : key_after);
     bool fs = false, fc = false, se = false, ce = false;
-    item[k] = 0;
     if (i < a.N) {
-      item[k] = a.sorted[i];
-      const uint32_t key = key_of(item[k]);
-      fs = i == 0 || key != key_of(a.sorted[i - 1]);
+      fs = i == 0 || key != kprev;
       fc = fs || (i % kChunk) == 0;
-      se = i + 1 == a.N || key != key_of(a.sorted[i + 1]);
+      se = i + 1 == a.N || key != knext;
       ce = se || ((i + 1) % kChunk) == 0;
+    } else {
+      item[k] = 0;
     }
     const uint64_t bs = __ballot(fs);
     const uint64_t bc = __ballot(fc);
