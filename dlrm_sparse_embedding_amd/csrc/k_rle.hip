@@ -307,15 +307,32 @@ __global__ __launch_bounds__(256) void k_inverse(const u4* __restrict__ blk, con
                                                  int32_t* __restrict__ inverse) {
   if (blk[0].w != 0u) return;  // one lookup per bag: stored by the encoder
   const long long i0 = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i0 >= N) return;
+  // a whole group of 4 is one 16-byte load and (when `inverse` is 16-byte
+  // aligned) one 16-byte store: four guarded stores would each end a basic
+  // block, and each would wait for the ones before it
+  const bool whole = i0 + 4 <= N;
   uint32_t k[4];
+  if (whole) {
+    const u4 kv = __builtin_nontemporal_load(reinterpret_cast<const u4*>(key_of_pos + i0));
+    k[0] = kv.x;
+    k[1] = kv.y;
+    k[2] = kv.z;
+    k[3] = kv.w;
+  } else {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) k[j] = i0 + j < N ? __builtin_nontemporal_load(key_of_pos + i0 + j) : map_size;
+    for (int j = 0; j < 4; ++j) k[j] = i0 + j < N ? key_of_pos[i0 + j] : map_size;
+  }
   int32_t v[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) v[j] = k[j] < map_size ? seg_of_key[k[j]] : -1;
+  if (whole && (reinterpret_cast<uintptr_t>(inverse) & 15u) == 0) {
+    *reinterpret_cast<u4*>(inverse + i0) = u4{(uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]};
+  } else {
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    if (i0 + j < N) inverse[i0 + j] = v[j];
+    for (int j = 0; j < 4; ++j)
+      if (i0 + j < N) inverse[i0 + j] = v[j];
+  }
 }
 
 __global__ void k_set_empty(int32_t* num_unique, int32_t* num_chunks) {
