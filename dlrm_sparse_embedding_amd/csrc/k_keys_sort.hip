@@ -104,8 +104,14 @@ __global__ __launch_bounds__(256) void k_keys(KeysArgs a) {
   }
   const int lo = g0 == 0 ? 0 : __shfl(s, 0);
   const int hi = g0 + 64 < nbags ? __shfl(nxt, 63) : N;
+  // Each pass reads the next pass's row indices (at clamped positions, so
+  // the load needs no branch) while it finds bags and stores keys: a long
+  // group waits on one index round trip, not one per 64 positions.
+  long long rnext = lo < hi ? ld_idx<IDX>(a.indices, min(lo + lane, hi - 1)) : 0;
   for (int p0 = lo; p0 < hi; p0 += 64) {  // trip count uniform: every lane joins the cross-lane reads
     const int p = p0 + lane;
+    const long long r = rnext;
+    rnext = ld_idx<IDX>(a.indices, min(p + 64, hi - 1));
     int j = 0;
 #pragma unroll
     for (int st = 32; st >= 1; st >>= 1) {
@@ -118,7 +124,6 @@ __global__ __launch_bounds__(256) void k_keys(KeysArgs a) {
       if (p < sj || p >= ej) {
         flag |= 2;
       } else {
-        const long long r = ld_idx<IDX>(a.indices, p);
         if (r >= 0 && r < (long long)rowsj)
           key = roj + (uint32_t)r;
         else
@@ -441,6 +446,20 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const uint64_t* __restrict
   seg_rows(a, r.seg, &lo, &span);
   const int sb = a.seg_start ? m.sb[r.seg] : 0;
 
+  // The tile's words and the digit bases are all loaded before anything is
+  // computed: the words from the tile's start (a scalar base) at clamped
+  // 32-bit offsets, so the loads go out back to back and their latency
+  // overlaps the bases' scan.
+  const int base = r.lo + wave * (64 * IPT);
+  uint64_t item[IPT];
+  uint32_t rank[IPT];
+  {
+    const int t_lo = __builtin_amdgcn_readfirstlane(r.lo);
+    const int t_n = __builtin_amdgcn_readfirstlane(r.hi - r.lo);
+    const uint64_t* tb = in + t_lo;
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) item[j] = tb[min(wave * (64 * IPT) + j * 64 + lane, t_n - 1)];
+  }
   {
     // digit d's run of this tile starts at: segment start + items of the
     // segment with smaller digits + items of digit d in the segment's tiles
@@ -448,29 +467,23 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const uint64_t* __restrict
     const uint32_t* b0 = a.segbase + (size_t)r.seg * R;
     const uint32_t* b1 = b0 + R;
     const uint32_t* gh = a.ghist + k;
-    uint32_t in_[PER], pre[PER];
-#pragma unroll
-    for (int j = 0; j < PER; ++j) in_[j] = b1[tid * PER + j] - b0[tid * PER + j];
-    block_excl_scan_digits<PER>(in_, pre, s_scan);
+    uint32_t in_[PER], pre[PER], g_[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int dd = tid * PER + j;
-      s_gbase[dd] = (uint32_t)sb + pre[j] + gh[(size_t)dd * a.nblk] - b0[dd];
+      const uint32_t lo0 = b0[dd];
+      in_[j] = b1[dd] - lo0;
+      g_[j] = gh[(size_t)dd * a.nblk] - lo0;
     }
+    block_excl_scan_digits<PER>(in_, pre, s_scan);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) s_gbase[tid * PER + j] = (uint32_t)sb + pre[j] + g_[j];
   }
 #pragma unroll
   for (int w = 0; w < 4; ++w)
     for (int dd = tid; dd < R; dd += 256) s_wcnt[w][dd] = 0;
   __syncthreads();
 
-  const int base = r.lo + wave * (64 * IPT);
-  uint64_t item[IPT];
-  uint32_t rank[IPT];
-#pragma unroll
-  for (int j = 0; j < IPT; ++j) {
-    const int i = base + j * 64 + lane;
-    item[j] = i < r.hi ? in[i] : 0ull;
-  }
   const uint64_t lt = lanemask_lt();
 #pragma unroll
   for (int j = 0; j < IPT; ++j) {
