@@ -387,34 +387,51 @@ __global__ __launch_bounds__(256) void k_sort_scan(SortKArgs a) {
     m.tf[1] = a.nblk;
   }
   __syncthreads();
+  // The row is scanned 1024 tiles at a time; the next window's counts are
+  // loaded (at clamped indices, without a branch) while this one is scanned,
+  // so a window costs a block scan, not a memory round trip. Each window's
+  // exclusive prefixes are kept in LDS, where the segments whose first tile
+  // falls in the window read their base.
+  constexpr int W = 256 * 4;
+  __shared__ uint32_t s_ex[W];
+  const int last = a.nblk - 1;
   uint32_t running = 0;
-  for (int base = 0; base < a.nblk; base += 256 * 4) {
+  // raw loads; counts past the row's end are masked where they are used, so
+  // that nothing waits on the prefetch before the next window
+  uint32_t xn[4] = {0u, 0u, 0u, 0u};
+  if (last >= 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xn[j] = row[min((int)threadIdx.x * 4 + j, last)];
+  }
+  for (int base = 0; base < a.nblk; base += W) {
     uint32_t v[4];
     uint32_t sum = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int i = base + threadIdx.x * 4 + j;
-      v[j] = i < a.nblk ? row[i] : 0u;
+      v[j] = base + (int)threadIdx.x * 4 + j <= last ? xn[j] : 0u;
       sum += v[j];
+    }
+    if (base + W <= last) {  // uniform over the block
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xn[j] = row[min(base + W + (int)threadIdx.x * 4 + j, last)];
     }
     uint32_t tot;
     uint32_t run = running + block_excl_scan_256(sum, lds, &tot);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int i = base + threadIdx.x * 4 + j;
-      if (i < a.nblk) {
-        row[i] = run;
-        // segments whose first tile is i (several when segments are empty)
-        int lo = 0, hi = a.S + 1;  // first t with tf[t] >= i
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if (m.tf[mid] < i) lo = mid + 1;
-          else hi = mid;
-        }
-        for (int t = lo; t <= a.S && m.tf[t] == i; ++t) s_base[t] = run;
-      }
+      if (i < a.nblk) row[i] = run;
+      s_ex[threadIdx.x * 4 + j] = run;
       run += v[j];
     }
+    __syncthreads();
+    // segments whose first tile lies in this window (several share a tile
+    // when segments are empty)
+    for (int t = threadIdx.x; t <= a.S; t += 256) {
+      const int f = m.tf[t];
+      if (f >= base && f < base + W && f < a.nblk) s_base[t] = s_ex[f - base];
+    }
+    __syncthreads();
     running += tot;
   }
   for (int t = threadIdx.x; t <= a.S; t += 256)
