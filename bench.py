@@ -80,7 +80,8 @@ def parse():
                          "profiler trace of the run holds that schedule's launches alone")
     ap.add_argument("--ceiling", action="store_true",
                     help="only time plain library kernels (copy, read-only sum, fill) over 4 GiB, and "
-                         "random 512-byte row reads served by L2, MALL and HBM: the practical ceilings "
+                         "random 512-byte row reads served by L2, MALL and HBM, and the fused update's "
+                         "random row read/write mix: the practical ceilings "
                          "the path's kernels are compared with")
     ap.add_argument("--ahead", type=int, default=2, choices=[1, 2],
                     help="pipeline schedule: how many batches ahead the dedup runs (1: the next batch's "
@@ -172,7 +173,30 @@ def main() -> int:
             e1.record()
             torch.cuda.synchronize()
             res[name + "_GBps"] = round(logical * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
-        print(json.dumps({"ceiling": res, "bytes_per_buffer": n * 4, "probe_bytes_per_launch": logical}), flush=True)
+        del probe
+        # the fused Adagrad update's mix at the 26 x 4M x 128 fp32 workload's
+        # sizes: per item 2-3 random rows of a 65536 x 26-row dY, then one
+        # random weight row and state row read and written (two 53 GB arrays),
+        # 636 k items (the workload's unique rows per step)
+        nsrc, nrows, items = 65536 * 26, 26 * 4_000_000, 636_000
+        usrc = torch.zeros(nsrc * 128, dtype=torch.float32, device="cuda")
+        ua = torch.zeros(nrows * 128, dtype=torch.float32, device="cuda")
+        ub = torch.zeros(nrows * 128, dtype=torch.float32, device="cuda")
+        E.emb_probe_update(usrc, nsrc, ua, ub, nrows, items)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            E.emb_probe_update(usrc, nsrc, ua, ub, nrows, items)
+        e1.record()
+        torch.cuda.synchronize()
+        ub_ms = e0.elapsed_time(e1) / 20
+        ubytes = E.emb_probe_update_bytes(items)
+        res["update_rows_GBps"] = round(ubytes / (ub_ms * 1e-3) / 1e9, 1)
+        res["update_rows_us"] = round(ub_ms * 1e3, 1)
+        del usrc, ua, ub
+        print(json.dumps({"ceiling": res, "bytes_per_buffer": n * 4, "probe_bytes_per_launch": logical,
+                          "update_probe_bytes_per_launch": ubytes}), flush=True)
         return 0
 
     if args.calibrate_copy:

@@ -1028,6 +1028,19 @@ int emb_probe_reads(const void* buf, int64_t nrows, int64_t stride, int32_t xcd_
   return ok();
 }
 
+int emb_probe_update(const float* src, int64_t nsrc, float* a, float* b, int64_t nrows, int32_t items,
+                     void* hip_stream) {
+  if (!src || !a || !b) return fail(EMB_E_INVAL, "src/a/b is NULL");
+  if (!aligned(src, 16) || !aligned(a, 16) || !aligned(b, 16)) return fail(EMB_E_INVAL, "src/a/b must be 16-byte aligned");
+  if (nsrc < 1 || nsrc >= (1ll << 32)) return fail(EMB_E_INVAL, "nsrc %lld not in [1, 2^32)", (long long)nsrc);
+  if (nrows < 1 || nrows >= (1ll << 32)) return fail(EMB_E_INVAL, "nrows %lld not in [1, 2^32)", (long long)nrows);
+  if (items < 1) return fail(EMB_E_INVAL, "items %d < 1", items);
+  hipError_t e = emb::launch_probe_update(src, (uint32_t)nsrc, a, b, (uint32_t)nrows, items,
+                                          static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "update probe kernel");
+  return ok();
+}
+
 int emb_kernel_times(emb_ctx* ctx, double* ms, int64_t* launches) {
   if (!ctx || !ms || !launches) return fail(EMB_E_INVAL, "NULL argument");
   for (int k = 0; k < EMB_K_COUNT; ++k) {

@@ -136,6 +136,8 @@ def lib() -> ctypes.CDLL:
     L.emb_probe_blocks.restype = i32
     L.emb_probe_reads.argtypes = [vp, i64, i64, i32, i32, vp, vp]
     L.emb_probe_reads.restype = ctypes.c_int
+    L.emb_probe_update.argtypes = [vp, i64, vp, vp, i64, i32, vp]
+    L.emb_probe_update.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -329,6 +331,17 @@ def emb_probe_reads(buf, nrows: int, stride: int, xcd_local: bool, reads: int, s
     """Measurement aid: random 512-byte row reads (see include/emb.h)."""
     _check(lib().emb_probe_reads(_ptr(buf), int(nrows), int(stride), 1 if xcd_local else 0, int(reads),
                                  _ptr(sink), _stream(stream)))
+
+
+def emb_probe_update(src, nsrc: int, a, b, nrows: int, items: int, stream=None) -> None:
+    """Measurement aid: the fused update's random row read/write mix (see include/emb.h)."""
+    _check(lib().emb_probe_update(_ptr(src), int(nsrc), _ptr(a), _ptr(b), int(nrows), int(items), _stream(stream)))
+
+
+def emb_probe_update_bytes(items: int) -> int:
+    """Bytes one emb_probe_update launch moves (include/emb.h)."""
+    n3 = 34 * (items // 50) + min(items % 50, 34)
+    return 512 * (3 * n3 + 2 * (items - n3) + 4 * items)
 
 
 def emb_kernel_times(ctx: int) -> dict:

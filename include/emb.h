@@ -431,6 +431,23 @@ int32_t emb_probe_blocks(void);
 int emb_probe_reads(const void* buf, int64_t nrows, int64_t stride, int32_t xcd_local, int32_t reads,
                     float* sink, void* hip_stream);
 
+/* Measurement aid, not part of the method (no context): the ceiling of the
+ * fused Adagrad update's access mix, random 512-byte rows read and written.
+ * Launches emb_probe_blocks() blocks of 8 subgroups of 32 lanes, grid-strided
+ * over items i < items. Item i reads 3 rows of src (2 when i mod 50 >= 34)
+ * at pseudo-random indices in [0, nsrc) and the row r of a and of b at one
+ * pseudo-random r in [0, nrows), then writes both rows back (a step of the
+ * summed src rows). Row k of a buffer is the 128 floats at element k*128.
+ * Bytes per launch: 512 * (n_src_rows + 4 * items), n_src_rows = 3 * n3 +
+ * 2 * (items - n3), n3 = 34 * (items / 50) + min(items mod 50, 34). Items
+ * may draw the same r; their writes race, and a and b hold meaningless
+ * values afterwards (src is only read). src (device, >= nsrc * 512 bytes),
+ * a and b (device, >= nrows * 512 bytes each), all 16-byte aligned.
+ * EMB_E_INVAL for NULL or misaligned pointers, nsrc or nrows not in
+ * [1, 2^32), items < 1. */
+int emb_probe_update(const float* src, int64_t nsrc, float* a, float* b, int64_t nrows, int32_t items,
+                     void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

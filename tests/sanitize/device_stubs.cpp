@@ -63,6 +63,9 @@ int probe_blocks() { return 2048; }
 hipError_t launch_probe_reads(const void*, uint32_t, uint32_t, int, int, float*, hipStream_t) {
   EMB_STUB_ABORT("launch_probe_reads");
 }
+hipError_t launch_probe_update(const float*, uint32_t, float*, float*, uint32_t, int, hipStream_t) {
+  EMB_STUB_ABORT("launch_probe_update");
+}
 hipError_t launch_reduce(const Geom&, const DevCtx&, int, int, int, int, const float*, const WsLayout&, const char*,
                          const uint32_t*, const int32_t*, float*, float, float, hipStream_t, const int32_t*) {
   EMB_STUB_ABORT("launch_reduce");

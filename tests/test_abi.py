@@ -117,6 +117,22 @@ def test_probe_rejects_bad_arguments_before_any_launch():
     assert call(reads=65540) == E.EMB_E_INVAL
 
 
+def test_update_probe_rejects_bad_arguments_before_any_launch():
+    L = E.lib()
+    good = dict(nsrc=1000, nrows=5000, items=100)
+    def call(src=FAKE, a=FAKE, b=FAKE, **kw):
+        k = {**good, **kw}
+        return L.emb_probe_update(src, k["nsrc"], a, b, k["nrows"], k["items"], None)
+    assert call(src=None) == E.EMB_E_INVAL
+    assert call(a=None) == E.EMB_E_INVAL
+    assert call(b=None) == E.EMB_E_INVAL
+    assert call(b=FAKE + 8) == E.EMB_E_INVAL        # misaligned
+    assert call(nsrc=0) == E.EMB_E_INVAL
+    assert call(nrows=1 << 32) == E.EMB_E_INVAL
+    assert call(items=0) == E.EMB_E_INVAL
+    assert E.emb_probe_update_bytes(100) == 512 * (3 * 68 + 2 * 32 + 400)
+
+
 def test_valid_context_host_only_calls():
     rc, ctx = _create([_desc(rows=1000), _desc(rows=5000)])
     assert rc == E.EMB_OK and ctx
