@@ -60,6 +60,7 @@ struct RedArgs {
   int N;
   int ntiles, ntiles1;
   float lr, eps;
+  int ptr_lds;  // k_chunks: the tables' row pointers (one slice each) are staged in LDS
 };
 
 // DT below is the update type code: storage type, | kMasterBit with a master.
@@ -147,8 +148,23 @@ __device__ __forceinline__ int slot_of(int so, int j, int tile) {
 // bags), so a segment can repeat a bag; see the multi-hot loop below.
 template <int DT, int LPR, int MODE, bool MEAN, bool REP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_chunks(RedArgs a) {
-  extern __shared__ uint32_t s_ro[];
+  // With ptr_lds (multi-hot batches of unsliced tables, few of them) the tables' weight, state and
+  // master pointers sit in LDS ahead of the row offsets, so a chunk's row
+  // address needs no global load of its table's descriptor: the weight and
+  // state loads go out with the dY loads.
+  extern __shared__ uint64_t s_dyn[];
+  const bool ptr_lds = REP && a.ptr_lds;  // set only for multi-hot batches
+  const int nptr = ptr_lds ? 3 * a.T : 0;
+  char** s_w = reinterpret_cast<char**>(s_dyn);
+  float** s_g = reinterpret_cast<float**>(s_dyn + a.T);
+  float** s_m = reinterpret_cast<float**>(s_dyn + 2 * a.T);
+  uint32_t* s_ro = reinterpret_cast<uint32_t*>(s_dyn + nptr);
   for (int i = threadIdx.x; i <= a.T; i += 256) s_ro[i] = a.row_off[i];
+  for (int i = threadIdx.x; i < (ptr_lds ? a.T : 0); i += 256) {
+    s_w[i] = reinterpret_cast<char*>(a.tables[i].w[0]);
+    s_g[i] = a.tables[i].g[0];
+    s_m[i] = a.tables[i].m[0];
+  }
   __syncthreads();
   // dY rows in flight: the largest count that fits 64 VGPRs without spills at
   // 8 waves/SIMD (spills cost scratch traffic in HBM: measured ~270 MB/launch);
@@ -188,7 +204,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
     float wv[4] = {0.f, 0.f, 0.f, 0.f}, Gv[4] = {0.f, 0.f, 0.f, 0.f};
     if constexpr (MODE != 0) {
       if (whole && act) {  // prefetch the row so its latency overlaps the dY loads
-        row_ptrs<DT>(a, t, key - s_ro[t], c0, &wp, &gp, &mp);
+        if (ptr_lds) {
+          const size_t e = (size_t)(key - s_ro[t]) * a.D + c0;
+          wp = s_w[t] + e * Stor<(DT & 7)>::kBytes;
+          gp = s_g[t] ? s_g[t] + e : nullptr;
+          if constexpr ((DT & kMasterBit) != 0) mp = s_m[t] + e;
+        } else {
+          row_ptrs<DT>(a, t, key - s_ro[t], c0, &wp, &gp, &mp);
+        }
         load_weight<DT>(wp, mp, wv);
         if constexpr (MODE == 2) load4<EMB_F32>(gp, Gv);
       }
@@ -452,6 +475,7 @@ static RedArgs make_args(const Geom& g, const DevCtx& dc, int N, const WsLayout&
   a.ntiles1 = L.ntiles1;
   a.lr = lr;
   a.eps = eps;
+  a.ptr_lds = 0;
   return a;
 }
 
@@ -553,10 +577,14 @@ hipError_t launch_reduce(const Geom& g, const DevCtx& dc, int mode, int N, int B
   const long long upper = (long long)N + L.ntiles;
   const long long want = (upper + sgw - 1) / sgw;
   const int grid = (int)(want < 16384 ? (want > 0 ? want : 1) : 16384);
-  const size_t smem = (size_t)(g.T + 1) * 4;
   // with no more lookups than bags a repeat is rare (it needs an empty bag
   // elsewhere); the plain loop is then the faster one, and both are exact
   const bool rep = (long long)N > (long long)g.T * B;
+  // row pointers from LDS: measured faster on multi-hot batches (the
+  // 100-table bf16 workload: 4.71 -> 4.64 ms) and slower on one-hot ones
+  // (26 x 4M x 128: 397-407 -> 410-438 us), so only there
+  a.ptr_lds = rep && g.T <= 256 && g.Dsl == g.D ? 1 : 0;
+  const size_t smem = (size_t)(a.ptr_lds ? 3 * g.T : 0) * 8 + (size_t)(g.T + 1) * 4;
   DISPATCH_DT_MODE(launch_chunks_pool, mean, rep, lpr, grid, smem, st, a)
   return hipGetLastError();
 }
