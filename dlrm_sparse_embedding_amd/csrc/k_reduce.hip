@@ -576,7 +576,15 @@ hipError_t launch_reduce(const Geom& g, const DevCtx& dc, int mode, int N, int B
   // chunks <= N + ntiles; the loop is grid-strided over the device count
   const long long upper = (long long)N + L.ntiles;
   const long long want = (upper + sgw - 1) / sgw;
-  const int grid = (int)(want < 16384 ? (want > 0 ? want : 1) : 16384);
+  // The grid is capped at one block per 32 bags, between 16384 and 32768
+  // blocks: the chunk count grows with the bag count, and a longer chunk list
+  // runs faster on the larger grid (26 x 4M x 128, 1.7 M bags: 437 -> 429 us;
+  // 100 x 1M x 128 bf16, 3.3 M bags: 5.40 -> 5.16 ms beside the next dedup)
+  // while a short one leaves its extra blocks idle (one 200M-row table, 65 k
+  // bags: 90 -> 94 us).
+  const long long bags = (long long)g.T * B;
+  const long long cap = bags / 32 < 16384 ? 16384 : (bags / 32 > 32768 ? 32768 : bags / 32);
+  const int grid = (int)(want < cap ? (want > 0 ? want : 1) : cap);
   // with no more lookups than bags a repeat is rare (it needs an empty bag
   // elsewhere); the plain loop is then the faster one, and both are exact
   const bool rep = (long long)N > (long long)g.T * B;
