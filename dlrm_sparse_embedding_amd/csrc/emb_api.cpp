@@ -230,7 +230,7 @@ WsLayout ws_layout(const Geom& g, long long N, int B) {
   L.sorted_bag = take(4ull * N);
   L.inv_len = take(4ull * (TB > 0 ? TB : 1));
   L.seg_off = take(4ull * (N + 1));
-  L.desc = take(16ull * (N + L.ntiles + 1));
+  L.desc = take(16ull * (N + L.ntiles + 4));  // + 3 entries read past the end by a wave's scalar prefetch
   L.chunk_seg = take(4ull * (N + L.ntiles + 1));
   L.tile_first_seg = take(4ull * (L.ntiles > 0 ? L.ntiles : 1));
   L.tile_last_seg = take(4ull * (L.ntiles > 0 ? L.ntiles : 1));

@@ -118,7 +118,7 @@ struct WsLayout {
   size_t sorted_bag;            // int32 [N] bag of each sorted lookup
   size_t inv_len;               // fp32 [T*B] 1/L per bag (mean pooling)
   size_t seg_off;               // int32 [N+1]
-  size_t desc;                  // int32x4 [N + ntiles] chunk descriptors
+  size_t desc;                  // int32x4 [N + ntiles + 4] chunk descriptors (3 of slack for a scalar prefetch)
   size_t chunk_seg;             // int32 [N + ntiles] segment of each chunk
   size_t tile_first_seg;        // int32 [ntiles] segment of a tile's first position
   size_t tile_last_seg;         // int32 [ntiles] segment of a tile's last position

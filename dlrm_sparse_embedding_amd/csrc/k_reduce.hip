@@ -183,10 +183,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
   const int nsg = gridDim.x * SGW;
   const int nch = min(*a.num_chunks, a.N + a.ntiles);
   int q = blockIdx.x * SGW + threadIdx.x / LPR;
-  // the next descriptor is loaded while the current chunk is processed
+  // The next descriptor is loaded while the current chunk is processed. The
+  // subgroups of a wave take consecutive chunks, so with at most 2 per wave
+  // (LPR >= 32) the wave reads its next 2 descriptors with scalar loads from a
+  // uniform base: those are counted apart from the vector loads, so the waits
+  // for dY and row loads never wait for them. The base is clamped so that
+  // [qb, qb + W) stays inside the buffer (N + ntiles + 4 entries); a subgroup
+  // past the list's end picks a duplicate it never uses. The pick happens
+  // where the loop moves on, and the loads are issued after the chunk's last
+  // LDS read (LDS and scalar loads share a wait counter). Narrower subgroups
+  // load their next descriptor with a vector load at the loop's head.
+  constexpr int W = 64 / LPR;
+  constexpr bool kScalarDesc = W <= 2;
+  typedef const __attribute__((address_space(4))) int* cdesc_t;
+  const int sub_in_wave = (int)(threadIdx.x & 63) / LPR;
+  int4 vn0 = {0, 0, -1, -1}, vn1 = {0, 0, -1, -1};
+  int qbn = 0;
+  auto prefetch = [&](int qn) {
+    if constexpr (kScalarDesc) {
+      int qb = __builtin_amdgcn_readfirstlane(qn - sub_in_wave);
+      qb = max(min(qb, nch - W), 0);
+      const cdesc_t p = (cdesc_t)(a.desc) + 4 * qb;
+      vn0 = int4{p[0], p[1], p[2], p[3]};
+      if constexpr (W == 2) vn1 = int4{p[4], p[5], p[6], p[7]};
+      qbn = qb;
+    }
+  };
   int4 d = q < nch ? a.desc[q] : int4{0, 0, -1, -1};
-  for (; q < nch; q += nsg) {
-    const int4 dn = q + nsg < nch ? a.desc[q + nsg] : int4{0, 0, -1, -1};
+  for (; q < nch; q += nsg, d = (kScalarDesc && q - qbn == 1) ? vn1 : vn0) {
+    if constexpr (!kScalarDesc) vn0 = a.desc[min(q + nsg, nch - 1)];
     // every index below is clamped into its buffer: a wrong count or offset
     // can give a wrong result, never an access outside the workspace
     const int cb = max(d.x, 0);
@@ -194,8 +219,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
     const bool whole = d.y < 0;
     const uint32_t key = (uint32_t)d.z;
     const int bag0 = d.w;
-    d = dn;
-    if (key >= a.total_rows) continue;  // lookups with out-of-range indices
+    if (key >= a.total_rows) {  // lookups with out-of-range indices
+      prefetch(q + nsg);
+      continue;
+    }
     const int t = table_of(s_ro, a.T, key);
 
     char* wp = nullptr;
@@ -216,6 +243,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
         if constexpr (MODE == 2) load4<EMB_F32>(gp, Gv);
       }
     }
+    // the chunk's last LDS read is behind: issue the next descriptor now
+    prefetch(q + nsg);
 
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     // dY element offsets fit in 32 bits (fewer than 2^32 elements), so the
