@@ -1,8 +1,8 @@
 """Multi-hot batches (more lookups than bags): segment lengths around the
 chunk (128), level-1 tile (4096) and 256-position marks, a key repeated inside
 one bag, batches of fewer bags than the reduce has XCDs, integer gradients
-(exact sums, bit-exact rows) and fused == materialised bit for bit. Every
-element is checked against the oracle."""
+(exact sums, bit-exact rows), fused == materialised bit for bit, and chunk
+lists of one to a few chunks. Every element is checked against the oracle."""
 from __future__ import annotations
 
 import numpy as np
@@ -177,3 +177,34 @@ def test_fused_equals_materialized_bf16_mean_sgd():
     res = [P.run_step(cfg, batch, dY, path=p, sample_untouched=0) for p in ("fused", "materialized", "fused")]
     for r in res[1:]:
         assert np.array_equal(r["w_new"].view(np.uint32), res[0]["w_new"].view(np.uint32))
+
+
+@pytest.mark.parametrize("dim,dtype,opt,case", [(128, "f32", "adagrad", "one"), (128, "f32", "adagrad", "two"),
+                                                (128, "f32", "sgd", "three"), (256, "bf16", "sgd", "odd"),
+                                                (128, "f32", "adagrad", "repeat")])
+def test_short_chunk_lists(dim, dtype, opt, case):
+    # a handful of chunks: the reduce's waves read their next descriptors in
+    # pairs from a clamped base, so lists of 1, 2, 3 and an odd number of
+    # chunks (and a wave whose second chunk lies past the end) must still
+    # give every key its own sum
+    rng = np.random.default_rng(41)
+    rows = 50
+    if case == "one":
+        lens, keys = [np.array([1])], [np.array([7])]
+    elif case == "two":
+        lens, keys = [np.array([1, 1])], [np.array([7, 9])]
+    elif case == "three":
+        lens, keys = [np.array([2, 1, 0])], [np.array([3, 7, 7])]
+    elif case == "odd":
+        lens = [rng.integers(0, 4, 9)]
+        keys = [rng.integers(0, rows, int(lens[0].sum()))]
+    else:  # one key in every bag, several times: one segment split into chunks only at tile edges
+        lens = [np.full(5, 3)]
+        keys = [np.full(15, 11)]
+    B = len(lens[0])
+    batch = W.make_batch_from_lengths(lens, keys, B)
+    cfg = _cfg(rows, dim, dtype, B, "sum", opt)
+    dY = rng.standard_normal((B, dim)).astype(np.float32)
+    _say("short chunk list", case, dim, dtype, opt, "N", batch.N)
+    for path in ("materialized", "fused"):
+        P.run_step(cfg, batch, dY, path=path)
