@@ -618,8 +618,8 @@ hipError_t launch_reduce(const Geom& g, const DevCtx& dc, int mode, int N, int B
   // elsewhere); the plain loop is then the faster one, and both are exact
   const bool rep = (long long)N > (long long)g.T * B;
   // row pointers from LDS: measured faster on multi-hot batches (the
-  // 100-table bf16 workload: 4.71 -> 4.64 ms) and slower on one-hot ones
-  // (26 x 4M x 128: 397-407 -> 410-438 us), so only there
+  // 100-table bf16 workload: 4.71 -> 4.64 ms) and no faster on one-hot ones
+  // (26 x 4M x 128: 429.6 vs 430.8 us), so only there
   a.ptr_lds = rep && g.T <= 256 && g.Dsl == g.D ? 1 : 0;
   const size_t smem = (size_t)(a.ptr_lds ? 3 * g.T : 0) * 8 + (size_t)(g.T + 1) * 4;
   DISPATCH_DT_MODE(launch_chunks_pool, mean, rep, lpr, grid, smem, st, a)
