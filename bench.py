@@ -161,15 +161,20 @@ def main() -> int:
         sink = torch.empty(E.emb_probe_blocks(), dtype=torch.float32, device="cuda")
         reads = 240
         logical = E.emb_probe_blocks() * 8 * reads * 512
-        for name, nrows, stride, local in (("l2_xcd_local_rows", 32768, 51200, True),
-                                           ("mall_shared_rows", 32768, 51200, False),
-                                           ("hbm_random_rows", (1 << 31) // 512, 512, False)):
-            E.emb_probe_reads(probe, nrows, stride, local, reads, sink)
+        # and the same with 256-byte rows (a 128-column bf16 row, as the
+        # 100-table forward reads them): 65536 packed rows (2 MB per eighth)
+        for name, nrows, stride, local, rb in (("l2_xcd_local_rows", 32768, 51200, True, 512),
+                                               ("mall_shared_rows", 32768, 51200, False, 512),
+                                               ("hbm_random_rows", (1 << 31) // 512, 512, False, 512),
+                                               ("l2_xcd_local_rows256", 65536, 256, True, 256),
+                                               ("mall_shared_rows256", 65536, 256, False, 256),
+                                               ("hbm_random_rows256", (1 << 31) // 256, 256, False, 256)):
+            E.emb_probe_reads(probe, nrows, stride, local, reads, sink, row_bytes=rb)
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             for _ in range(10):
-                E.emb_probe_reads(probe, nrows, stride, local, reads, sink)
+                E.emb_probe_reads(probe, nrows, stride, local, reads, sink, row_bytes=rb)
             e1.record()
             torch.cuda.synchronize()
             res[name + "_GBps"] = round(logical * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)

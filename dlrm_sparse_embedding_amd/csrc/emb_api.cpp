@@ -1015,15 +1015,16 @@ int emb_set_kernel_timing(emb_ctx* ctx, int32_t enable) {
 int32_t emb_probe_blocks(void) { return emb::probe_blocks(); }
 
 int emb_probe_reads(const void* buf, int64_t nrows, int64_t stride, int32_t xcd_local, int32_t reads,
-                    float* sink, void* hip_stream) {
+                    int32_t row_bytes, float* sink, void* hip_stream) {
   if (!buf || !sink) return fail(EMB_E_INVAL, "buf/sink is NULL");
   if (!aligned(buf, 16) || !aligned(sink, 4)) return fail(EMB_E_INVAL, "buf must be 16-byte and sink 4-byte aligned");
+  if (row_bytes != 256 && row_bytes != 512) return fail(EMB_E_INVAL, "row_bytes %d is not 256 or 512", row_bytes);
   if (nrows < 8 || nrows >= (1ll << 32)) return fail(EMB_E_INVAL, "nrows %lld not in [8, 2^32)", (long long)nrows);
-  if (stride < 512 || stride % 16 != 0 || stride >= (1ll << 32))
-    return fail(EMB_E_INVAL, "stride %lld: need >= 512, a multiple of 16, < 2^32", (long long)stride);
+  if (stride < row_bytes || stride % 16 != 0 || stride >= (1ll << 32))
+    return fail(EMB_E_INVAL, "stride %lld: need >= row_bytes, a multiple of 16, < 2^32", (long long)stride);
   if (reads < 4 || reads > 65536 || reads % 4 != 0) return fail(EMB_E_INVAL, "reads %d not in [4, 65536] / 4", reads);
-  hipError_t e = emb::launch_probe_reads(buf, (uint32_t)nrows, (uint32_t)stride, xcd_local ? 1 : 0, reads, sink,
-                                         static_cast<hipStream_t>(hip_stream));
+  hipError_t e = emb::launch_probe_reads(buf, (uint32_t)nrows, (uint32_t)stride, xcd_local ? 1 : 0, reads, row_bytes,
+                                         sink, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "probe kernel");
   return ok();
 }

@@ -200,7 +200,7 @@ hipError_t launch_rle(const Geom& g, int B, const uint64_t* sorted, int N, int n
 // reading `reads` random 512-byte rows; sink gets one float per block.
 int probe_blocks();
 hipError_t launch_probe_reads(const void* buf, uint32_t nrows, uint32_t stride, int local, int reads,
-                              float* sink, hipStream_t st);
+                              int row_bytes, float* sink, hipStream_t st);
 hipError_t launch_probe_update(const float* src, uint32_t nsrc, float* a, float* b, uint32_t nrows, int items,
                                hipStream_t st);
 hipError_t launch_set_empty(const WsLayout& L, char* ws, int32_t* num_unique, hipStream_t st);

@@ -24,11 +24,13 @@ __device__ __forceinline__ uint32_t mix32(uint32_t x) {
 
 constexpr int kProbeBlocks = 2048;
 
+// LPR lanes per row: 32 for 512-byte rows, 16 for 256-byte rows.
+template <int LPR>
 __global__ __launch_bounds__(256) void k_probe_reads(const char* __restrict__ buf, uint32_t nrows,
                                                      uint32_t stride, int local, int reads,
                                                      float* __restrict__ sink) {
-  const int lane = threadIdx.x & 31;
-  const uint32_t sg = blockIdx.x * 8 + (threadIdx.x >> 5);
+  const int lane = threadIdx.x & (LPR - 1);
+  const uint32_t sg = blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
   uint32_t lo = 0, span = nrows;
   if (local) {
     span = nrows / 8;
@@ -94,9 +96,13 @@ hipError_t launch_probe_update(const float* src, uint32_t nsrc, float* a, float*
 }
 
 hipError_t launch_probe_reads(const void* buf, uint32_t nrows, uint32_t stride, int local, int reads,
-                              float* sink, hipStream_t st) {
-  hipLaunchKernelGGL(k_probe_reads, dim3(kProbeBlocks), dim3(256), 0, st, static_cast<const char*>(buf), nrows,
-                     stride, local, reads, sink);
+                              int row_bytes, float* sink, hipStream_t st) {
+  if (row_bytes == 256)
+    hipLaunchKernelGGL(k_probe_reads<16>, dim3(kProbeBlocks), dim3(256), 0, st, static_cast<const char*>(buf),
+                       nrows, stride, local, reads, sink);
+  else
+    hipLaunchKernelGGL(k_probe_reads<32>, dim3(kProbeBlocks), dim3(256), 0, st, static_cast<const char*>(buf),
+                       nrows, stride, local, reads, sink);
   return hipGetLastError();
 }
 

@@ -134,7 +134,7 @@ def lib() -> ctypes.CDLL:
     L.emb_kernel_times.restype = ctypes.c_int
     L.emb_probe_blocks.argtypes = []
     L.emb_probe_blocks.restype = i32
-    L.emb_probe_reads.argtypes = [vp, i64, i64, i32, i32, vp, vp]
+    L.emb_probe_reads.argtypes = [vp, i64, i64, i32, i32, i32, vp, vp]
     L.emb_probe_reads.restype = ctypes.c_int
     L.emb_probe_update.argtypes = [vp, i64, vp, vp, i64, i32, vp]
     L.emb_probe_update.restype = ctypes.c_int
@@ -327,10 +327,11 @@ def emb_probe_blocks() -> int:
     return int(lib().emb_probe_blocks())
 
 
-def emb_probe_reads(buf, nrows: int, stride: int, xcd_local: bool, reads: int, sink, stream=None) -> None:
-    """Measurement aid: random 512-byte row reads (see include/emb.h)."""
+def emb_probe_reads(buf, nrows: int, stride: int, xcd_local: bool, reads: int, sink, stream=None,
+                    row_bytes: int = 512) -> None:
+    """Measurement aid: random 256- or 512-byte row reads (see include/emb.h)."""
     _check(lib().emb_probe_reads(_ptr(buf), int(nrows), int(stride), 1 if xcd_local else 0, int(reads),
-                                 _ptr(sink), _stream(stream)))
+                                 int(row_bytes), _ptr(sink), _stream(stream)))
 
 
 def emb_probe_update(src, nsrc: int, a, b, nrows: int, items: int, stream=None) -> None:

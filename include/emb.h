@@ -416,20 +416,21 @@ int emb_kernel_times(emb_ctx* ctx, double* ms, int64_t* launches);
 
 /* Measurement aid, not part of the method (no context): the cache and HBM
  * read ceilings that the path's kernels are compared with. Launches
- * emb_probe_blocks() blocks of 8 subgroups of 32 lanes on the stream; each
- * subgroup reads `reads` rows of 512 bytes (16 bytes per lane) at
- * pseudo-random indices in [0, nrows), row r starting at byte r*stride of
- * buf. With xcd_local != 0, block b reads only rows of its eighth of
- * [0, nrows): blocks are dealt round robin to the 8 XCDs, so each XCD's L2
- * serves its own eighth. Logical bytes read: emb_probe_blocks() * 8 * reads
- * * 512. buf (device, >= (nrows - 1) * stride + 512 bytes, 16-byte aligned)
- * is only read; sink (device, >= emb_probe_blocks() floats) receives one
- * value per block. EMB_E_INVAL for NULL or misaligned pointers, nrows < 8 or
- * >= 2^32, stride < 512 or not a multiple of 16 or >= 2^32, reads not in
- * [4, 65536] or not a multiple of 4. */
+ * emb_probe_blocks() blocks of 256 lanes on the stream, in subgroups of
+ * row_bytes / 16 lanes (256 or 512 bytes per row: 16 bytes per lane); each
+ * subgroup reads `reads` rows at pseudo-random indices in [0, nrows), row r
+ * starting at byte r*stride of buf. With xcd_local != 0, block b reads only
+ * rows of its eighth of [0, nrows): blocks are dealt round robin to the 8
+ * XCDs, so each XCD's L2 serves its own eighth. Logical bytes read:
+ * emb_probe_blocks() * 256 * reads * 16 (whatever the row size). buf
+ * (device, >= (nrows - 1) * stride + row_bytes bytes, 16-byte aligned) is
+ * only read; sink (device, >= emb_probe_blocks() floats) receives one value
+ * per block. EMB_E_INVAL for NULL or misaligned pointers, row_bytes other
+ * than 256 or 512, nrows < 8 or >= 2^32, stride < row_bytes or not a
+ * multiple of 16 or >= 2^32, reads not in [4, 65536] or not a multiple of 4. */
 int32_t emb_probe_blocks(void);
 int emb_probe_reads(const void* buf, int64_t nrows, int64_t stride, int32_t xcd_local, int32_t reads,
-                    float* sink, void* hip_stream);
+                    int32_t row_bytes, float* sink, void* hip_stream);
 
 /* Measurement aid, not part of the method (no context): the ceiling of the
  * fused Adagrad update's access mix, random 512-byte rows read and written.

@@ -60,7 +60,7 @@ hipError_t launch_rle(const Geom&, int, const uint64_t*, int, int, const WsLayou
 }
 hipError_t launch_set_empty(const WsLayout&, char*, int32_t*, hipStream_t) { EMB_STUB_ABORT("launch_set_empty"); }
 int probe_blocks() { return 2048; }
-hipError_t launch_probe_reads(const void*, uint32_t, uint32_t, int, int, float*, hipStream_t) {
+hipError_t launch_probe_reads(const void*, uint32_t, uint32_t, int, int, int, float*, hipStream_t) {
   EMB_STUB_ABORT("launch_probe_reads");
 }
 hipError_t launch_probe_update(const float*, uint32_t, float*, float*, uint32_t, int, hipStream_t) {

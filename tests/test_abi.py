@@ -101,10 +101,10 @@ def test_probe_rejects_bad_arguments_before_any_launch():
     # the read-ceiling probe validates on the host and launches nothing on error
     L = E.lib()
     assert E.emb_probe_blocks() == 2048
-    good = dict(nrows=4096, stride=512, local=1, reads=60)
+    good = dict(nrows=4096, stride=512, local=1, reads=60, row_bytes=512)
     def call(buf=FAKE, sink=FAKE, **kw):
         a = {**good, **kw}
-        return L.emb_probe_reads(buf, a["nrows"], a["stride"], a["local"], a["reads"], sink, None)
+        return L.emb_probe_reads(buf, a["nrows"], a["stride"], a["local"], a["reads"], a["row_bytes"], sink, None)
     assert call(buf=None) == E.EMB_E_INVAL
     assert call(sink=None) == E.EMB_E_INVAL
     assert call(buf=FAKE + 4) == E.EMB_E_INVAL       # misaligned
@@ -115,6 +115,8 @@ def test_probe_rejects_bad_arguments_before_any_launch():
     assert call(reads=6) == E.EMB_E_INVAL
     assert call(reads=0) == E.EMB_E_INVAL
     assert call(reads=65540) == E.EMB_E_INVAL
+    assert call(row_bytes=128) == E.EMB_E_INVAL
+    assert call(row_bytes=256, stride=128) == E.EMB_E_INVAL   # stride shorter than a row
 
 
 def test_update_probe_rejects_bad_arguments_before_any_launch():

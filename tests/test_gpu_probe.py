@@ -12,14 +12,15 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("local", [False, True])
-@pytest.mark.parametrize("nrows,stride", [(64, 512), (1024, 51200)])
-def test_probe_reads_inside_buffer(local, nrows, stride):
-    print(f"[gpu] probe nrows={nrows} stride={stride} local={local}", flush=True)
-    nbytes = (nrows - 1) * stride + 512
+@pytest.mark.parametrize("nrows,stride,row_bytes", [(64, 512, 512), (1024, 51200, 512), (64, 256, 256),
+                                                    (1024, 25600, 256)])
+def test_probe_reads_inside_buffer(local, nrows, stride, row_bytes):
+    print(f"[gpu] probe nrows={nrows} stride={stride} row={row_bytes} local={local}", flush=True)
+    nbytes = (nrows - 1) * stride + row_bytes
     buf = torch.ones((nbytes + 3) // 4, dtype=torch.float32, device="cuda")
     sink = torch.full((E.emb_probe_blocks(),), -1.0, dtype=torch.float32, device="cuda")
     reads = 16
-    E.emb_probe_reads(buf, nrows, stride, local, reads, sink)
+    E.emb_probe_reads(buf, nrows, stride, local, reads, sink, row_bytes=row_bytes)
     torch.cuda.synchronize()
     assert torch.all(sink == 4.0 * reads)
 
