@@ -314,19 +314,22 @@ def test_segments_on_chunk_boundaries():
         P.run_step(cfg, batch, dY, path=path)
 
 
-def test_out_of_range_index_flagged_not_applied():
-    cfg = _custom_cfg([50, 60], B=4, opt="sgd")
+@pytest.mark.parametrize("dim", [16, 128])
+def test_out_of_range_index_flagged_not_applied(dim):
+    # 128 columns: the reduce's waves read their chunk descriptors in pairs,
+    # and the sentinel segment's chunk takes its own path through that loop
+    cfg = _custom_cfg([50, 60], dim=dim, B=4, opt="sgd")
     keys = [np.array([1, 2, 50, 3]), np.array([-1, 5, 59, 60])]   # 50, -1, 60 out of range
     batch = W.make_batch_from_lengths([np.ones(4, int)] * 2, keys, 4, index_dtype=np.int64)
-    _say("out-of-range")
+    _say("out-of-range", dim)
     tabs = P.make_tables(cfg)
-    idx, off, dy = P.to_dev(batch, np.ones((4, 32), np.float32))
+    idx, off, dy = P.to_dev(batch, np.ones((4, 2 * dim), np.float32))
     Y = tabs.forward(idx, off, 4, "sum")
     with pytest.raises(E.EmbError) as ei:
         tabs.check_device_error()
     assert ei.value.code == E.EMB_E_BOUNDS
     y = Y.cpu().numpy()
-    assert np.all(y[2, :16] == 0) and np.all(y[0, 16:] == 0) and np.all(y[3, 16:] == 0)
+    assert np.all(y[2, :dim] == 0) and np.all(y[0, dim:] == 0) and np.all(y[3, dim:] == 0)
     bufs = tabs.backward_buffers(8, 4, with_grad=False)
     tabs.backward(idx, off, 4, "sum", dy, bufs)
     tabs.update("sgd", 0.5, 0.0, bufs, dY=dy)
